@@ -1,0 +1,284 @@
+#!/usr/bin/env python3
+"""Benchmark of the grouped / depthwise conv forward HIP library on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the hot path over one batch of the workload: the
+default workload is the MobileNetV2-style depthwise fp16 case (N=32, C=144,
+56x56, 3x3, pad 1, bias) in its stride-1 form and its stride-2 form, i.e. two
+gconv_fwd calls per step (each one kernel launch).  Inputs are seeded
+synthetic tensors already resident in HBM.  To keep the 256 MB Infinity Cache
+from serving repeated reads, every call takes the next of R rotating input /
+output buffer sets, R chosen so the sets span >= 512 MB.
+
+Prints ONE JSON line: whole-step algorithmic HBM throughput (GB/s) as
+`value`, TFLOP/s and fractions of the MI355X peaks per call, a `roofline`
+object for the dominant kernel (its average duration from HIP events recorded
+on the launch stream around each of its launches inside the timed region),
+and a `cpu_baseline` object (the CPU oracle, timed on this host's cores on
+the same workload).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from depthwise_convolution_grouped_amd import inputs, metrics  # noqa: E402
+
+WORKLOAD_SETS = {
+    # name -> (workload names run once each per step, dominant one)
+    "depthwise2d_f16": (["depthwise2d_f16", "depthwise2d_s2_f16"], "depthwise2d_f16"),
+}
+for _n in inputs.WORKLOADS:
+    WORKLOAD_SETS.setdefault(_n, ([_n], _n))
+
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+ROTATE_BYTES = 512 << 20
+
+
+def kernel_source_hash() -> str:
+    """Hash of the kernel sources; the stored counter-based traffic is only valid for it."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "depthwise_convolution_grouped_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counters, if taken on these sources."""
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            db = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = db.get(workload)
+    if not e or e.get("source_hash") != kernel_source_hash():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(names, max_seconds: float):
+    """Time the CPU oracle on the workload (whole batches, repeated) on this host's cores."""
+    import numpy as np  # noqa: F401
+    import oracle
+    total_bytes = 0
+    elapsed = 0.0
+    runs = 0
+    per = []
+    data = []
+    for n in names:
+        wl = inputs.WORKLOADS[n]
+        p = wl.problem
+        t = inputs.workload_tensors(wl)
+        x = inputs.storage_to_f64(t.x, p.dtype)
+        w = inputs.storage_to_f64(t.w, p.dtype)
+        b = inputs.storage_to_f64(t.bias, p.dtype) if t.bias is not None else None
+        data.append((p, x, w, b))
+    # bound the sample: shrink the batch if one pass would exceed the budget
+    t0 = time.perf_counter()
+    p, x, w, b = data[0]
+    st, pd, dl = p.spatial_args()
+    oracle.conv_fwd(x[:1], w, b, p.G, st, pd, dl)
+    one_image = time.perf_counter() - t0
+    nimg = max(1, min(data[0][0].N, int(max_seconds / 3 / max(one_image * len(data), 1e-9))))
+    while runs < 1 or (elapsed < max_seconds / 2 and runs < 200):
+        for p, x, w, b in data:
+            st, pd, dl = p.spatial_args()
+            t0 = time.perf_counter()
+            oracle.conv_fwd(x[:nimg], w, b, p.G, st, pd, dl)
+            dt = time.perf_counter() - t0
+            per.append(dt)
+            elapsed += dt
+            sub = inputs.Problem(p.ndim, p.dtype, nimg, p.G, p.C, p.K, p.spatial, p.filt,
+                                 p.stride, p.pad, p.dil, p.bias)
+            total_bytes += metrics.total_bytes(sub)
+        runs += 1
+    return {
+        "value": total_bytes / elapsed / 1e9,
+        "unit": "GB/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": "%s, first %d of %d images, %d pass(es), fp64 direct conv, %.1f s"
+                  % ("+".join(names), nimg, data[0][0].N, runs, elapsed),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="depthwise2d_f16", choices=sorted(WORKLOAD_SETS))
+    ap.add_argument("--path", default="auto", help="force a kernel path (auto|generic|depthwise|smallg_mfma|igemm_mfma)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="rough bound on the CPU oracle's timing sample")
+    ap.add_argument("--hot", action="store_true", help="no buffer rotation (cache-hot; labelled)")
+    a = ap.parse_args()
+
+    if a.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % a.gpus, file=sys.stderr)
+        return 2
+
+    import torch
+    from depthwise_convolution_grouped_amd import gconv as G
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 2
+    G.lib()  # fail loudly if the HIP library is missing
+
+    names, dominant = WORKLOAD_SETS[a.workload]
+    path = G.GCONV_PATH_AUTO if a.path == "auto" else G.PATHS[a.path]
+    dev = torch.device("cuda", 0)
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+    def to_dev(arr, dtype):
+        import numpy as np
+        if dtype == "bf16":
+            t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+        else:
+            t = torch.from_numpy(np.ascontiguousarray(arr))
+        return t.to(dev)
+
+    calls = []
+    for n in names:
+        wl = inputs.WORKLOADS[n]
+        p = wl.problem
+        t = inputs.workload_tensors(wl)
+        d = G.desc_from_problem(p)
+        o = G.gconv_out_dims(d)
+        oshape = (p.N,) + (o if p.ndim == 3 else o[1:]) + (p.K,)
+        per_set = metrics.io_bytes(p)["x"] + metrics.io_bytes(p)["y"]
+        R = 1 if a.hot else max(2, -(-ROTATE_BYTES // per_set))
+        x0 = to_dev(t.x, p.dtype)
+        xs = [x0] + [x0.clone() for _ in range(R - 1)]
+        ys = [torch.empty(oshape, dtype=tdt[p.dtype], device=dev) for _ in range(R)]
+        w = to_dev(t.w, p.dtype)
+        b = to_dev(t.bias, p.dtype) if t.bias is not None else None
+        sel = G.gconv_select_path(d) if path == G.GCONV_PATH_AUTO else path
+        calls.append(dict(name=n, p=p, d=d, xs=xs, ys=ys, w=w, b=b, R=R, path=sel,
+                          plan=G.gconv_get_plan(d, sel)))
+
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+    counter = [0]
+
+    def launch(c):
+        i = counter[0] % c["R"]
+        rc = G.gconv_fwd_path(c["d"], c["path"], c["xs"][i].data_ptr(), c["w"].data_ptr(),
+                              c["b"].data_ptr() if c["b"] is not None else None,
+                              c["ys"][i].data_ptr(), sptr)
+        if rc != 0:
+            raise G.GconvError(rc, "gconv_fwd(%s)" % c["name"])
+
+    def step(events=None):
+        for c in calls:
+            if events is not None and c["name"] in events:
+                ev0 = torch.cuda.Event(enable_timing=True)
+                ev1 = torch.cuda.Event(enable_timing=True)
+                ev0.record(stream)
+                launch(c)
+                ev1.record(stream)
+                events[c["name"]].append((ev0, ev1))
+            else:
+                launch(c)
+        counter[0] += 1
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: K steps back to back, events around every launch.
+    events = {c["name"]: [] for c in calls}
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for _ in range(a.steps):
+        step(events)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / a.steps
+
+    per_config = {}
+    step_bytes = 0
+    step_flops = 0
+    for c in calls:
+        ds = sorted(e0.elapsed_time(e1) for e0, e1 in events[c["name"]])
+        avg_ms = sum(ds) / len(ds)
+        med_ms = ds[len(ds) // 2]
+        p = c["p"]
+        r = metrics.rates(p, avg_ms * 1e-3)
+        per_config[c["name"]] = {
+            "path": G.gconv_path_name(c["path"]),
+            "us_avg": avg_ms * 1e3, "us_median": med_ms * 1e3, "us_min": ds[0] * 1e3,
+            "tflops": r["tflops"], "gbs": r["gbs"], "frac_hbm": r["frac_hbm"],
+            "frac_compute": r["frac_compute"], "flop": metrics.flops(p),
+            "bytes": metrics.total_bytes(p), "rotating_sets": c["R"],
+            "grid": list(c["plan"]["grid"]), "block": c["plan"]["block"],
+        }
+        step_bytes += metrics.total_bytes(p)
+        step_flops += metrics.flops(p)
+
+    dom = next(c for c in calls if c["name"] == dominant)
+    dp = dom["p"]
+    dom_cfg = per_config[dominant]
+    ai = metrics.flops(dp) / metrics.total_bytes(dp)
+    peak_tf = metrics.PEAK_TFLOPS["f32_vector"] if dp.dtype == "f32" else metrics.PEAK_TFLOPS[dp.dtype]
+    ridge = peak_tf * 1e12 / (metrics.PEAK_HBM_GBS * 1e9)
+    if ai < ridge:
+        roof = {"bound": "hbm", "achieved": dom_cfg["gbs"], "peak": metrics.PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": dom_cfg["gbs"] / metrics.PEAK_HBM_GBS}
+    else:
+        roof = {"bound": "mfma", "achieved": dom_cfg["tflops"], "peak": peak_tf,
+                "unit": "TFLOP/s", "frac": dom_cfg["tflops"] / peak_tf}
+    roof["traffic"] = stored_traffic(dominant)
+    roof["kernel"] = dom_cfg["path"]
+    roof["workload"] = dominant
+    roof["algorithmic_bytes"] = metrics.total_bytes(dp)
+    roof["algorithmic_flop"] = metrics.flops(dp)
+    roof["us_per_launch"] = dom_cfg["us_avg"]
+
+    out = {
+        "metric": "grouped conv fwd TFLOP/s + HBM GB/s (% of MI355X peak) per config, 1 GPU",
+        "value": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dp.dtype,
+        "data": "synthetic (seeded; x~N(0,1), w~N(0,1/fan_in), bias~U[-1,1]); inputs resident in HBM",
+        "config": {"workload": " + ".join(inputs.WORKLOADS[n].about for n in names),
+                   "names": names, "layout": "NHWGC/GKYXC -> NHWGK",
+                   "cache": "hot (no rotation)" if a.hot else "rotating buffer sets >= 512 MB"},
+        "tflops": step_flops / (ms_per_step * 1e-3) / 1e12,
+        "frac_hbm_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / metrics.PEAK_HBM_GBS,
+        "per_config": per_config,
+        "roofline": roof,
+        "cpu_baseline": None,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(names, a.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

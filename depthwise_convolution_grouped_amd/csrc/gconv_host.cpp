@@ -1,0 +1,260 @@
+// Host side of the C ABI declared in include/gconv.h: descriptor validation,
+// output extents, path selection, launch shapes and the single launch per
+// call.  Validation, extents, selection and plans make no HIP call, so they
+// run (and are tested) on machines without a GPU.
+//
+// Validation follows rocm-libraries PR 10064 (Technical Details: the
+// dispatcher checks C % G == 0 and K % G == 0 and accepts bf16 besides fp16
+// and fp32) and the TileOPs PR 1568 review (summary: the forward ops route
+// grouped problems to grouped kernels and check the expected weight shape;
+// here the weight shape is implied by the descriptor).
+#include <limits.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "gconv_internal.h"
+
+#define GCONV_API extern "C" __attribute__((visibility("default")))
+
+namespace gconv {
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)INT32_MAX;  // tensors must have < 2^31 elements
+
+// out = floor((in + 2 pad - dil (k - 1) - 1) / stride) + 1, or 0 if no window fits.
+int64_t out_extent(int64_t in, int64_t k, int64_t s, int64_t p, int64_t d)
+{
+    int64_t room = in + 2 * p - d * (k - 1) - 1;
+    return room < 0 ? 0 : room / s + 1;
+}
+
+// Product with saturation at INT64_MAX/2 so absurd descriptors cannot overflow.
+int64_t sat_mul(int64_t a, int64_t b)
+{
+    const int64_t cap = INT64_MAX / 2;
+    if (a <= 0 || b <= 0) return a * b;
+    if (a > cap / b) return cap;
+    return a * b;
+}
+
+int check_desc(const gconv_desc *d, int64_t out[3])
+{
+    if (!d) return GCONV_ERR_NULL_PTR;
+    if (d->ndim != 2 && d->ndim != 3) return GCONV_ERR_BAD_DESC;
+    if (d->dtype != GCONV_F32 && d->dtype != GCONV_F16 && d->dtype != GCONV_BF16)
+        return GCONV_ERR_BAD_DESC;
+    if (d->N <= 0 || d->G <= 0 || d->C <= 0 || d->K <= 0) return GCONV_ERR_BAD_DESC;
+    if (d->C % d->G != 0 || d->K % d->G != 0) return GCONV_ERR_BAD_DESC;
+    for (int a = 0; a < 3; ++a) {
+        if (d->in[a] <= 0 || d->filt[a] <= 0 || d->stride[a] <= 0 || d->dil[a] <= 0 ||
+            d->pad[a] < 0)
+            return GCONV_ERR_BAD_DESC;
+        // keep every per-axis quantity far from int32 overflow
+        if (d->in[a] > kMaxElems || d->filt[a] > kMaxElems || d->stride[a] > kMaxElems ||
+            d->dil[a] > kMaxElems || d->pad[a] > kMaxElems)
+            return GCONV_ERR_TOO_LARGE;
+    }
+    if (d->ndim == 2 && (d->in[0] != 1 || d->filt[0] != 1 || d->stride[0] != 1 ||
+                         d->dil[0] != 1 || d->pad[0] != 0))
+        return GCONV_ERR_BAD_DESC;
+    for (int a = 0; a < 3; ++a) {
+        out[a] = out_extent(d->in[a], d->filt[a], d->stride[a], d->pad[a], d->dil[a]);
+        if (out[a] <= 0) return GCONV_ERR_BAD_OUT_DIMS;
+    }
+    const int64_t Cpg = d->C / d->G, Kpg = d->K / d->G;
+    int64_t x_el = sat_mul(sat_mul(sat_mul(sat_mul(d->N, d->in[0]), d->in[1]), d->in[2]), d->C);
+    int64_t y_el = sat_mul(sat_mul(sat_mul(sat_mul(d->N, out[0]), out[1]), out[2]), d->K);
+    int64_t w_el = sat_mul(sat_mul(sat_mul(sat_mul(d->K, d->filt[0]), d->filt[1]), d->filt[2]), Cpg);
+    int64_t span = 0;
+    for (int a = 0; a < 3; ++a)  // padded extent must also stay in int32
+        span = span > d->in[a] + 2 * d->pad[a] ? span : d->in[a] + 2 * d->pad[a];
+    if (x_el >= kMaxElems || y_el >= kMaxElems || w_el >= kMaxElems || span >= kMaxElems ||
+        d->K >= kMaxElems || d->C >= kMaxElems || Kpg >= kMaxElems)
+        return GCONV_ERR_TOO_LARGE;
+    return GCONV_OK;
+}
+
+Problem to_problem(const gconv_desc *d, const int64_t out[3])
+{
+    Problem p;
+    p.ndim = d->ndim;
+    p.dtype = d->dtype;
+    p.N = (int)d->N;
+    p.G = (int)d->G;
+    p.Cpg = (int)(d->C / d->G);
+    p.Kpg = (int)(d->K / d->G);
+    p.D = (int)d->in[0];  p.H = (int)d->in[1];  p.W = (int)d->in[2];
+    p.Z = (int)d->filt[0]; p.Y = (int)d->filt[1]; p.X = (int)d->filt[2];
+    p.Do = (int)out[0];   p.Ho = (int)out[1];   p.Wo = (int)out[2];
+    p.sd = (int)d->stride[0]; p.sh = (int)d->stride[1]; p.sw = (int)d->stride[2];
+    p.pd = (int)d->pad[0];    p.ph = (int)d->pad[1];    p.pw = (int)d->pad[2];
+    p.dd = (int)d->dil[0];    p.dh = (int)d->dil[1];    p.dw = (int)d->dil[2];
+    return p;
+}
+
+bool path_ok(const Problem &p, int path)
+{
+    switch (path) {
+    case GCONV_PATH_GENERIC: return generic::supported(p);
+    case GCONV_PATH_DEPTHWISE: return depthwise::supported(p);
+    case GCONV_PATH_SMALLG: return smallg::supported(p);
+    case GCONV_PATH_IGEMM: return igemm::supported(p);
+    default: return false;
+    }
+}
+
+// Channels-per-group dispatcher.  Depthwise (Cpg = Kpg = 1) goes to the VALU
+// direct kernel; large per-group contractions (Cpg, Kpg >= 32, half types)
+// are a real GEMM per group and go to the implicit-GEMM MFMA kernel; small
+// groups in half types merge several groups into one block-diagonal MFMA
+// tile; everything else takes the generic kernel.
+int select(const Problem &p)
+{
+    if (depthwise::supported(p)) return GCONV_PATH_DEPTHWISE;
+    if (p.dtype != GCONV_F32 && p.Cpg >= 32 && p.Kpg >= 32 && igemm::supported(p))
+        return GCONV_PATH_IGEMM;
+    if (smallg::supported(p)) return GCONV_PATH_SMALLG;
+    if (igemm::supported(p)) return GCONV_PATH_IGEMM;
+    return GCONV_PATH_GENERIC;
+}
+
+gconv_plan plan_of(const Problem &p, int path)
+{
+    switch (path) {
+    case GCONV_PATH_DEPTHWISE: return depthwise::plan(p);
+    case GCONV_PATH_SMALLG: return smallg::plan(p);
+    case GCONV_PATH_IGEMM: return igemm::plan(p);
+    default: return generic::plan(p);
+    }
+}
+
+bool aligned(const void *ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
+
+int run(const gconv_desc *d, int path, const void *x, const void *w, const void *bias,
+        void *y, void *stream)
+{
+    int64_t out[3];
+    int rc = check_desc(d, out);
+    if (rc != GCONV_OK) return rc;
+    if (!x || !w || !y) return GCONV_ERR_NULL_PTR;
+    Problem p = to_problem(d, out);
+    const uintptr_t es = (uintptr_t)elem_size(p.dtype);
+    if (!aligned(x, es) || !aligned(w, es) || !aligned(y, es) || (bias && !aligned(bias, es)))
+        return GCONV_ERR_MISALIGNED;
+    // The vector paths load and store 16-byte channel vectors; automatic
+    // dispatch falls back to the generic kernel for other pointers.
+    const bool vec_ok = aligned(x, 16) && aligned(w, 16) && aligned(y, 16);
+    if (path == GCONV_PATH_AUTO) {
+        path = select(p);
+        if (!vec_ok) path = GCONV_PATH_GENERIC;
+    } else {
+        if (path < 0 || path >= GCONV_NUM_PATHS) return GCONV_ERR_BAD_PATH;
+        if (!path_ok(p, path)) return GCONV_ERR_PATH_UNSUPPORTED;
+        if (path != GCONV_PATH_GENERIC && !vec_ok) return GCONV_ERR_MISALIGNED;
+    }
+    Args a{x, w, bias, y};
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    switch (path) {
+    case GCONV_PATH_DEPTHWISE: e = depthwise::launch(p, a, s); break;
+    case GCONV_PATH_SMALLG: e = smallg::launch(p, a, s); break;
+    case GCONV_PATH_IGEMM: e = igemm::launch(p, a, s); break;
+    default: e = generic::launch(p, a, s); break;
+    }
+    if (e != hipSuccess) return GCONV_ERR_LAUNCH;
+    return GCONV_OK;
+}
+
+}  // namespace
+}  // namespace gconv
+
+using namespace gconv;
+
+GCONV_API int gconv_validate(const gconv_desc *d)
+{
+    int64_t out[3];
+    return check_desc(d, out);
+}
+
+GCONV_API int gconv_out_dims(const gconv_desc *d, int64_t out[3])
+{
+    if (!out) return GCONV_ERR_NULL_PTR;
+    int64_t o[3];
+    int rc = check_desc(d, o);
+    if (rc != GCONV_OK) return rc;
+    memcpy(out, o, sizeof(o));
+    return GCONV_OK;
+}
+
+GCONV_API int gconv_select_path(const gconv_desc *d)
+{
+    int64_t out[3];
+    int rc = check_desc(d, out);
+    if (rc != GCONV_OK) return rc;
+    return select(to_problem(d, out));
+}
+
+GCONV_API int gconv_path_supported(const gconv_desc *d, int path)
+{
+    int64_t out[3];
+    int rc = check_desc(d, out);
+    if (rc != GCONV_OK) return rc;
+    if (path < 0 || path >= GCONV_NUM_PATHS) return GCONV_ERR_BAD_PATH;
+    return path_ok(to_problem(d, out), path) ? 1 : 0;
+}
+
+GCONV_API int gconv_get_plan(const gconv_desc *d, int path, gconv_plan *plan)
+{
+    if (!plan) return GCONV_ERR_NULL_PTR;
+    int64_t out[3];
+    int rc = check_desc(d, out);
+    if (rc != GCONV_OK) return rc;
+    Problem p = to_problem(d, out);
+    if (path == GCONV_PATH_AUTO) path = select(p);
+    else if (path < 0 || path >= GCONV_NUM_PATHS) return GCONV_ERR_BAD_PATH;
+    else if (!path_ok(p, path)) return GCONV_ERR_PATH_UNSUPPORTED;
+    *plan = plan_of(p, path);
+    return GCONV_OK;
+}
+
+GCONV_API int gconv_fwd(const gconv_desc *d, const void *x, const void *w, const void *bias,
+                        void *y, void *stream)
+{
+    return run(d, GCONV_PATH_AUTO, x, w, bias, y, stream);
+}
+
+GCONV_API int gconv_fwd_path(const gconv_desc *d, int path, const void *x, const void *w,
+                             const void *bias, void *y, void *stream)
+{
+    return run(d, path, x, w, bias, y, stream);
+}
+
+GCONV_API const char *gconv_status_str(int status)
+{
+    switch (status) {
+    case GCONV_OK: return "ok";
+    case GCONV_ERR_BAD_DESC: return "bad descriptor";
+    case GCONV_ERR_BAD_OUT_DIMS: return "empty output (an output extent is <= 0)";
+    case GCONV_ERR_NULL_PTR: return "null pointer";
+    case GCONV_ERR_TOO_LARGE: return "tensor too large (>= 2^31 elements)";
+    case GCONV_ERR_MISALIGNED: return "misaligned pointer";
+    case GCONV_ERR_BAD_PATH: return "unknown path";
+    case GCONV_ERR_PATH_UNSUPPORTED: return "path cannot run this problem";
+    case GCONV_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+GCONV_API const char *gconv_path_name(int path)
+{
+    switch (path) {
+    case GCONV_PATH_AUTO: return "auto";
+    case GCONV_PATH_GENERIC: return "generic";
+    case GCONV_PATH_DEPTHWISE: return "depthwise";
+    case GCONV_PATH_SMALLG: return "smallg_mfma";
+    case GCONV_PATH_IGEMM: return "igemm_mfma";
+    default: return "unknown";
+    }
+}
+
+GCONV_API int gconv_abi_version(void) { return GCONV_ABI_VERSION; }

@@ -1,0 +1,62 @@
+// Internal interface between the host library (gconv_host.cpp) and the
+// kernel translation units.  Not installed; the public ABI is include/gconv.h.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "gconv.h"
+
+namespace gconv {
+
+// A validated problem.  Every tensor has < 2^31 elements, so all sizes and
+// flat offsets fit in int32.
+struct Problem {
+    int ndim, dtype;
+    int N, G, Cpg, Kpg;
+    int D, H, W;        // input extents
+    int Z, Y, X;        // filter extents
+    int Do, Ho, Wo;     // output extents
+    int sd, sh, sw;     // strides
+    int pd, ph, pw;     // paddings
+    int dd, dh, dw;     // dilations
+    int C() const { return G * Cpg; }
+    int K() const { return G * Kpg; }
+    int taps() const { return Z * Y * X; }
+    long long y_elems() const { return (long long)N * Do * Ho * Wo * G * Kpg; }
+};
+
+struct Args {
+    const void *x;
+    const void *w;
+    const void *bias;   // may be null
+    void *y;
+};
+
+// Per-path hooks.  `supported` and `plan` are pure host functions (no HIP
+// call); `launch` enqueues exactly one kernel on `stream`.
+namespace generic {
+bool supported(const Problem &p);
+gconv_plan plan(const Problem &p);
+hipError_t launch(const Problem &p, const Args &a, hipStream_t s);
+}
+namespace depthwise {
+bool supported(const Problem &p);
+gconv_plan plan(const Problem &p);
+hipError_t launch(const Problem &p, const Args &a, hipStream_t s);
+}
+namespace smallg {
+bool supported(const Problem &p);
+gconv_plan plan(const Problem &p);
+hipError_t launch(const Problem &p, const Args &a, hipStream_t s);
+}
+namespace igemm {
+bool supported(const Problem &p);
+gconv_plan plan(const Problem &p);
+hipError_t launch(const Problem &p, const Args &a, hipStream_t s);
+}
+
+inline int elem_size(int dtype) { return dtype == GCONV_F32 ? 4 : 2; }
+
+}  // namespace gconv

@@ -1,0 +1,157 @@
+/*
+ * gconv.h -- grouped / depthwise convolution forward on AMD Instinct MI355X
+ * (gfx950).  C ABI: plain pointers and sizes, no framework types.
+ *
+ * The operation (all entry points below compute or describe it):
+ *
+ *   y[n, o, g*Kpg + k] = bias[g*Kpg + k]
+ *       + sum over taps t of the filter window and c < Cpg of
+ *           x[n, o*stride - pad + t*dil, g*Cpg + c] * w[g*Kpg + k, t, c]
+ *
+ * for every image n, output position o (2D or 3D), group g < G and output
+ * channel k < Kpg, with Cpg = C/G and Kpg = K/G.  Channel mapping as in
+ * rocm-libraries PR 10064 (grouped forward conv in the implicit-GEMM conv),
+ * Technical Details: the input channel is (group, channel-in-group) embedded
+ * as g*Cpg + c, the output channel is g*Kpg + k.  Grouped and depthwise
+ * (G == C) forward conv with and without bias, stride, padding and dilation,
+ * 2D and 3D, as the TileOPs PR 1568 review (summary) describes its
+ * GroupConv2d/GroupConv3d kernels.  The filter is not flipped
+ * (cross-correlation).  Taps outside the input read zero; padding is
+ * symmetric, one value per spatial axis (CK grouped_conv tile-engine README,
+ * Problem Registry field list).  Output extent per axis:
+ *   out = floor((in + 2*pad - dil*(filt-1) - 1) / stride) + 1.
+ *
+ * Memory layouts (packed, last index fastest; the forward NHWGC / GKYXC pair
+ * of the CK grouped-conv Python examples README, Examples table, with a depth
+ * axis for 3D):
+ *   x     [N][D][H][W][G][Cpg]       (2D: D = 1)      NDHWGC
+ *   w     [G][Kpg][Z][Y][X][Cpg]     (2D: Z = 1)      GKZYXC
+ *   bias  [G*Kpg]  or NULL
+ *   y     [N][Do][Ho][Wo][G][Kpg]                     NDHWGK
+ * x, w, bias and y share one element type; products are accumulated in fp32
+ * and the result is rounded once (to nearest even) to the element type.
+ *
+ * Ownership: the caller allocates, owns and frees every buffer (device memory
+ * for x, w, bias, y).  The library never allocates, frees or keeps a pointer
+ * after a call returns, needs no workspace and holds no mutable global state;
+ * calls from several host threads are safe.  y must not overlap x, w or bias.
+ *
+ * Errors: every function returns GCONV_OK (0) or a negative gconv_status.
+ * Validation errors are detected on the host before anything is launched.
+ */
+#ifndef GCONV_H
+#define GCONV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GCONV_ABI_VERSION 1
+
+/* Element type of x, w, bias and y. */
+typedef enum gconv_dtype {
+    GCONV_F32 = 0,
+    GCONV_F16 = 1,
+    GCONV_BF16 = 2
+} gconv_dtype;
+
+typedef enum gconv_status {
+    GCONV_OK = 0,
+    GCONV_ERR_BAD_DESC = -1,        /* ndim/dtype out of range, C%G or K%G != 0,
+                                       non-positive size/stride/dilation,
+                                       negative pad, 2D with depth entries set */
+    GCONV_ERR_BAD_OUT_DIMS = -2,    /* an output extent would be <= 0 */
+    GCONV_ERR_NULL_PTR = -3,        /* desc, x, w or y is NULL */
+    GCONV_ERR_TOO_LARGE = -4,       /* a tensor has >= 2^31 elements */
+    GCONV_ERR_MISALIGNED = -5,      /* a pointer is not aligned as the path needs */
+    GCONV_ERR_BAD_PATH = -6,        /* unknown path id */
+    GCONV_ERR_PATH_UNSUPPORTED = -7,/* forced path cannot run this problem */
+    GCONV_ERR_LAUNCH = -8           /* the HIP launch reported an error */
+} gconv_status;
+
+/* Kernel paths.  gconv_fwd picks one from the descriptor. */
+typedef enum gconv_path {
+    GCONV_PATH_AUTO = -1,
+    GCONV_PATH_GENERIC = 0,     /* one thread per output, any shape */
+    GCONV_PATH_DEPTHWISE = 1,   /* Cpg = Kpg = 1: LDS halo tile, channel vectors, VALU */
+    GCONV_PATH_SMALLG = 2,      /* small groups: LDS halo tile, block-diagonal MFMA */
+    GCONV_PATH_IGEMM = 3,       /* large groups: implicit GEMM, group on grid z, MFMA */
+    GCONV_NUM_PATHS = 4
+} gconv_path;
+
+/* Problem descriptor.  Spatial arrays are (depth, height, width); a 2D
+ * problem sets in[0] = filt[0] = stride[0] = dil[0] = 1 and pad[0] = 0.
+ * Fields mirror the CK grouped_conv problem dataclass (tile-engine README,
+ * Problem Registry): N, C, K, G, input and filter extents, stride, pad,
+ * dilation. */
+typedef struct gconv_desc {
+    int32_t ndim;       /* 2 or 3 */
+    int32_t dtype;      /* gconv_dtype */
+    int64_t N, G, C, K; /* batch, groups, total input / output channels */
+    int64_t in[3];      /* D, H, W */
+    int64_t filt[3];    /* Z, Y, X */
+    int64_t stride[3];
+    int64_t pad[3];
+    int64_t dil[3];
+} gconv_desc;
+
+/* Launch shape a path would use (for tests and profiling). */
+typedef struct gconv_plan {
+    int32_t path;
+    uint32_t grid[3];
+    uint32_t block;
+    uint32_t lds_bytes;
+    uint32_t groups_per_tile; /* groups merged into one tile (1 if none) */
+} gconv_plan;
+
+/* Checks the descriptor alone (no pointers, no HIP call).  Returns GCONV_OK,
+ * GCONV_ERR_BAD_DESC, GCONV_ERR_BAD_OUT_DIMS or GCONV_ERR_TOO_LARGE. */
+int gconv_validate(const gconv_desc *d);
+
+/* Writes (Do, Ho, Wo) to out[0..2] (Do = 1 in 2D) after validating d. */
+int gconv_out_dims(const gconv_desc *d, int64_t out[3]);
+
+/* Path gconv_fwd would take for d (a gconv_path >= 0), or a negative status.
+ * The choice depends on channels per group and dtype only, after the group
+ * dispatch of the TileOPs PR 1568 review (summary: grouped problems are
+ * routed to dedicated grouped kernels) and the group merging of the CK
+ * Python examples README (Config-options harness, num_groups_to_merge). */
+int gconv_select_path(const gconv_desc *d);
+
+/* 1 if `path` can run d, 0 if not, or a negative status. */
+int gconv_path_supported(const gconv_desc *d, int path);
+
+/* Fills *plan with the launch shape of `path` (GCONV_PATH_AUTO: the selected
+ * one) for d. */
+int gconv_get_plan(const gconv_desc *d, int path, gconv_plan *plan);
+
+/* Forward convolution, asynchronous on `stream` (a hipStream_t; NULL = the
+ * null stream).  x, w, bias (NULL = no bias) and y are device pointers in the
+ * layouts above, aligned to the element size.  Exactly one kernel is
+ * launched; the caller synchronises the stream before reading y.  Results
+ * are bitwise deterministic from run to run (no atomics). */
+int gconv_fwd(const gconv_desc *d, const void *x, const void *w,
+              const void *bias, void *y, void *stream);
+
+/* As gconv_fwd, but on a caller-chosen path (GCONV_PATH_AUTO = select).
+ * Returns GCONV_ERR_PATH_UNSUPPORTED when that path cannot take d, and
+ * GCONV_ERR_MISALIGNED when its vector loads need 16-byte aligned pointers
+ * and one is not.  Used by the tests to run every path on shapes several can
+ * take. */
+int gconv_fwd_path(const gconv_desc *d, int path, const void *x, const void *w,
+                   const void *bias, void *y, void *stream);
+
+/* Static strings; never NULL. */
+const char *gconv_status_str(int status);
+const char *gconv_path_name(int path);
+
+/* GCONV_ABI_VERSION of the built library. */
+int gconv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GCONV_H */

@@ -1,0 +1,183 @@
+"""GPU parity of the HIP library (called through its C ABI) against the oracle.
+
+* every workload at full size: element by element where the oracle finishes
+  in seconds, else at sampled outputs (random positions plus every corner);
+* reduced-batch versions of the large workloads element by element;
+* every kernel path forced on shapes it can take, including random small
+  2D/3D problems with odd channel counts, strides, paddings and dilations;
+* output poisoned with NaN before the call (every element must be written),
+  canary elements after y (nothing written past the end), bitwise run-to-run
+  determinism, and a non-default stream.
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from depthwise_convolution_grouped_amd import gconv as G
+from depthwise_convolution_grouped_amd import inputs, metrics
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    G.lib()   # fail loudly if the library is missing
+
+
+def poisoned_out(p):
+    shape = (p.N,) + (metrics.out_spatial(p) if p.ndim == 3 else metrics.out_spatial(p)[1:]) + (p.K,)
+    return torch.full(shape, float("nan"), dtype=U.TORCH_DTYPE[p.dtype], device="cuda")
+
+
+def run_and_fetch(p, t, path=G.GCONV_PATH_AUTO):
+    x, w, b = U.device_tensors(p, t)
+    y = U.run(p, x, w, b, path=path, out=poisoned_out(p))
+    torch.cuda.synchronize()
+    return U.to_f64(y)
+
+
+def reduced(p: inputs.Problem, N: int) -> inputs.Problem:
+    return inputs.Problem(p.ndim, p.dtype, N, p.G, p.C, p.K, p.spatial, p.filt, p.stride,
+                          p.pad, p.dil, p.bias)
+
+
+FULL = ["grouped2d_small_f32", "depthwise2d_f16", "depthwise2d_s2_f16",
+        "grouped3d_f16_n1", "grouped3d_f16_n8"]
+SAMPLED = ["grouped2d_resnext_bf16", "grouped2d_large_bf16", "grouped2d_large_dil2_bf16"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_workload_full_elementwise(name):
+    wl = inputs.WORKLOADS[name]
+    p, t = wl.problem, inputs.workload_tensors(wl)
+    y = run_and_fetch(p, t)
+    st, pd, dl = p.spatial_args()
+    ref, scale = oracle.conv_fwd(*U.oracle_inputs(p, t), p.G, st, pd, dl)
+    r = U.check(y, ref, scale, p.dtype, name)
+    print("%s path=%s max err/tol=%.3f" % (name, G.gconv_path_name(G.gconv_select_path(G.desc_from_problem(p))), r))
+
+
+def corner_indices(p):
+    Do, Ho, Wo = metrics.out_spatial(p)
+    dims = (p.N, Do, Ho, Wo, p.K)
+    idx = []
+    for n, od, oh, ow, k in itertools.product({0, p.N - 1}, {0, Do - 1}, {0, Ho - 1}, {0, Wo - 1},
+                                             {0, p.Kpg - 1, p.K - p.Kpg, p.K - 1}):
+        idx.append(np.ravel_multi_index((n, od, oh, ow, k), dims))
+    return np.array(sorted(set(idx)), dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", SAMPLED)
+def test_workload_full_sampled(name):
+    wl = inputs.WORKLOADS[name]
+    p, t = wl.problem, inputs.workload_tensors(wl)
+    y = run_and_fetch(p, t)
+    assert np.isfinite(y).all(), "some outputs were not written"
+    total = y.size
+    rng = np.random.default_rng(wl.seed + 5)
+    idx = np.unique(np.concatenate([rng.integers(0, total, 6000), corner_indices(p)]))
+    st, pd, dl = p.spatial_args()
+    ref, scale = oracle.conv_fwd_points(*U.oracle_inputs(p, t), p.G, st, pd, dl, idx)
+    r = U.check(y.reshape(-1)[idx], ref, scale, p.dtype, name)
+    print("%s sampled %d max err/tol=%.3f" % (name, idx.size, r))
+
+
+REDUCED = [("grouped2d_resnext_bf16", 2), ("grouped2d_large_bf16", 2),
+           ("grouped2d_large_dil2_bf16", 1), ("depthwise2d_f16", 3), ("depthwise2d_s2_f16", 3),
+           ("grouped3d_f16_n8", 2), ("grouped2d_small_f32", 1)]
+
+
+@pytest.mark.parametrize("name,N", REDUCED)
+@pytest.mark.parametrize("path", list(G.PATHS))
+def test_reduced_workload_every_path(name, N, path):
+    wl = inputs.WORKLOADS[name]
+    p = reduced(wl.problem, N)
+    d = G.desc_from_problem(p)
+    pid = G.PATHS[path]
+    if G.gconv_path_supported(d, pid) != 1:
+        pytest.skip("%s cannot run %s" % (path, name))
+    t = inputs.make_tensors(p, wl.seed + 7, wl.x_dist, wl.w_dist, wl.b_dist)
+    y = run_and_fetch(p, t, pid)
+    st, pd, dl = p.spatial_args()
+    ref, scale = oracle.conv_fwd(*U.oracle_inputs(p, t), p.G, st, pd, dl)
+    r = U.check(y, ref, scale, p.dtype, "%s N=%d path=%s" % (name, N, path))
+    print("%s N=%d path=%s max err/tol=%.3f" % (name, N, path, r))
+
+
+def sweep_cases():
+    cases = []
+    for dtype, ndim in itertools.product(["f32", "f16", "bf16"], [2, 3]):
+        rng = np.random.default_rng({"f32": 1, "f16": 2, "bf16": 3}[dtype] * 10 + ndim)
+        for i in range(12):
+            cases.append((dtype, ndim, i, inputs.random_problem(rng, dtype, ndim)))
+    return cases
+
+
+SWEEP = sweep_cases()
+
+
+@pytest.mark.parametrize("case", range(len(SWEEP)),
+                         ids=["%s-%dd-%d" % c[:3] for c in SWEEP])
+def test_random_small_every_path(case):
+    dtype, ndim, i, p = SWEEP[case]
+    t = inputs.make_tensors(p, 90000 + case)
+    st, pd, dl = p.spatial_args()
+    ref, scale = oracle.conv_fwd(*U.oracle_inputs(p, t), p.G, st, pd, dl)
+    d = G.desc_from_problem(p)
+    ran = []
+    for path, pid in G.PATHS.items():
+        if G.gconv_path_supported(d, pid) != 1:
+            continue
+        y = run_and_fetch(p, t, pid)
+        U.check(y, ref, scale, p.dtype, "%s path=%s" % (p, path))
+        ran.append(path)
+    assert "generic" in ran
+
+
+@pytest.mark.parametrize("name", ["depthwise2d_f16", "grouped2d_resnext_bf16", "grouped3d_f16_n1",
+                                  "grouped2d_large_bf16", "grouped2d_small_f32"])
+def test_deterministic_and_no_overrun(name):
+    wl = inputs.WORKLOADS[name]
+    p = wl.problem if name != "grouped2d_resnext_bf16" else reduced(wl.problem, 4)
+    t = inputs.workload_tensors(wl) if p is wl.problem else inputs.make_tensors(p, wl.seed, wl.x_dist, wl.w_dist)
+    x, w, b = U.device_tensors(p, t)
+    shape = tuple(poisoned_out(p).shape)
+    n = int(np.prod(shape))
+    canary = 4096
+    buf = torch.full((n + canary,), 7.0, dtype=U.TORCH_DTYPE[p.dtype], device="cuda")
+    y1 = U.run(p, x, w, b, out=buf[:n].view(shape))
+    torch.cuda.synchronize()
+    first = y1.clone()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        y2 = U.run(p, x, w, b, out=buf[:n].view(shape), stream=side.cuda_stream)
+    side.synchronize()
+    assert torch.equal(first.view(torch.int16 if p.dtype != "f32" else torch.int32),
+                       y2.view(torch.int16 if p.dtype != "f32" else torch.int32)), "not bitwise deterministic"
+    assert torch.all(buf[n:] == 7.0).item(), "kernel wrote past the end of y"
+
+
+def test_misaligned_falls_back_or_errors():
+    p = reduced(inputs.WORKLOADS["depthwise2d_f16"].problem, 1)
+    t = inputs.make_tensors(p, 123)
+    x, w, b = U.device_tensors(p, t)
+    # x shifted by one element: 2-byte aligned, not 16-byte aligned
+    xs = torch.empty(x.numel() + 1, dtype=x.dtype, device="cuda")
+    xs[1:].copy_(x.view(-1))
+    xv = xs[1:].view(x.shape)
+    y = U.run(p, xv, w, b, out=poisoned_out(p))       # auto: falls back to a path that accepts it
+    torch.cuda.synchronize()
+    st, pd, dl = p.spatial_args()
+    ref, scale = oracle.conv_fwd(*U.oracle_inputs(p, t), p.G, st, pd, dl)
+    U.check(U.to_f64(y), ref, scale, p.dtype, "misaligned x")
+    d = G.desc_from_problem(p)
+    sel = G.gconv_select_path(d)
+    if sel != G.GCONV_PATH_GENERIC:
+        rc = G.gconv_fwd_path(d, sel, xv.data_ptr(), w.data_ptr(), b.data_ptr(), y.data_ptr(), 0)
+        assert rc == G.GCONV_ERR_MISALIGNED

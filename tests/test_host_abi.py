@@ -1,0 +1,206 @@
+"""Host side of the C ABI, without a GPU: exports, validation, extents,
+path selection and launch plans.  Nothing here launches a kernel: every call
+either is a pure host function or fails validation before a launch."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from depthwise_convolution_grouped_amd import gconv as G
+from depthwise_convolution_grouped_amd import inputs, metrics
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gconv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gconv_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) >= 10, names
+    L = G.lib()
+    for n in names:
+        assert hasattr(L, n), "libgconv.so does not export %s" % n
+    assert set(names) == set(G.EXPORTS)
+
+
+def test_exports_nothing_else():
+    import subprocess
+    r = subprocess.run(["nm", "-D", "--defined-only", G.LIB_PATH], capture_output=True, text=True)
+    if r.returncode != 0:
+        pytest.skip("nm unavailable")
+    syms = {line.split()[-1] for line in r.stdout.splitlines() if line.strip()}
+    ours = {s for s in syms if s.startswith("gconv")}
+    assert ours == set(declared_functions())
+    assert not any(s.startswith("_ZN5gconv") for s in syms), "internal C++ symbols leak"
+
+
+def test_abi_version():
+    assert G.gconv_abi_version() == 1
+
+
+def base_desc(**kw):
+    a = dict(ndim=2, dtype="f16", N=2, G=4, C=8, K=12, spatial=(9, 10), filt=(3, 3),
+             stride=(1, 1), pad=(1, 1), dil=(1, 1))
+    a.update(kw)
+    return G.make_desc(**a)
+
+
+def test_valid_descriptor():
+    assert G.gconv_validate(base_desc()) == G.GCONV_OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ndim=4), G.GCONV_ERR_BAD_DESC),
+    (dict(ndim=1), G.GCONV_ERR_BAD_DESC),
+    (dict(dtype=7), G.GCONV_ERR_BAD_DESC),
+    (dict(C=9), G.GCONV_ERR_BAD_DESC),            # C % G != 0
+    (dict(K=10), G.GCONV_ERR_BAD_DESC),           # K % G != 0
+    (dict(N=0), G.GCONV_ERR_BAD_DESC),
+    (dict(G=0), G.GCONV_ERR_BAD_DESC),
+    (dict(stride=(0, 1)), G.GCONV_ERR_BAD_DESC),
+    (dict(dil=(1, 0)), G.GCONV_ERR_BAD_DESC),
+    (dict(pad=(-1, 0)), G.GCONV_ERR_BAD_DESC),
+    (dict(spatial=(0, 4)), G.GCONV_ERR_BAD_DESC),
+    (dict(filt=(3, 0)), G.GCONV_ERR_BAD_DESC),
+    (dict(spatial=(2, 2), pad=(0, 0)), G.GCONV_ERR_BAD_OUT_DIMS),
+    (dict(spatial=(5, 5), pad=(0, 0), dil=(3, 3)), G.GCONV_ERR_BAD_OUT_DIMS),
+    (dict(N=1 << 20, spatial=(1024, 1024)), G.GCONV_ERR_TOO_LARGE),
+    (dict(N=1 << 40), G.GCONV_ERR_TOO_LARGE),
+])
+def test_validation_errors(kw, status):
+    assert G.gconv_validate(base_desc(**kw)) == status
+
+
+def test_2d_with_depth_entries_is_rejected():
+    d = base_desc()
+    d.in_[0] = 2
+    assert G.gconv_validate(d) == G.GCONV_ERR_BAD_DESC
+    d = base_desc()
+    d.pad[0] = 1
+    assert G.gconv_validate(d) == G.GCONV_ERR_BAD_DESC
+
+
+def test_null_descriptor():
+    L = G.lib()
+    assert L.gconv_validate(None) == G.GCONV_ERR_NULL_PTR
+    assert L.gconv_select_path(None) == G.GCONV_ERR_NULL_PTR
+
+
+def test_out_dims_match_metrics_random():
+    rng = np.random.default_rng(5)
+    for i in range(300):
+        p = inputs.random_problem(rng, ["f32", "f16", "bf16"][i % 3], 2 + i % 2)
+        d = G.desc_from_problem(p)
+        assert G.gconv_validate(d) == G.GCONV_OK
+        assert G.gconv_out_dims(d) == metrics.out_spatial(p)
+
+
+def test_out_dims_match_oracle_on_workloads():
+    import oracle
+    for name, wl in inputs.WORKLOADS.items():
+        p = wl.problem
+        o = G.gconv_out_dims(G.desc_from_problem(p))
+        for a in range(3):
+            assert o[a] == oracle.out_extent(p.spatial[a], p.filt[a], p.stride[a], p.pad[a], p.dil[a]), name
+
+
+# Paths the dispatcher must pick for the workloads (channels per group decide).
+EXPECTED_PATH = {
+    "grouped2d_small_f32": "generic",
+    "depthwise2d_f16": "depthwise",
+    "depthwise2d_s2_f16": "depthwise",
+    "grouped2d_resnext_bf16": "smallg_mfma",
+    "grouped3d_f16_n1": "smallg_mfma",
+    "grouped3d_f16_n8": "smallg_mfma",
+    "grouped2d_large_bf16": "igemm_mfma",
+    "grouped2d_large_dil2_bf16": "igemm_mfma",
+}
+
+
+def _built_paths():
+    d = G.desc_from_problem(inputs.WORKLOADS["depthwise2d_f16"].problem)
+    out = {"generic"}
+    for name, pid in G.PATHS.items():
+        probe = {"depthwise": "depthwise2d_f16", "smallg_mfma": "grouped2d_resnext_bf16",
+                 "igemm_mfma": "grouped2d_large_bf16", "generic": "depthwise2d_f16"}[name]
+        d = G.desc_from_problem(inputs.WORKLOADS[probe].problem)
+        if G.gconv_path_supported(d, pid) == 1:
+            out.add(name)
+    return out
+
+
+@pytest.mark.parametrize("name", sorted(EXPECTED_PATH))
+def test_dispatch_per_workload(name):
+    want = EXPECTED_PATH[name]
+    if want not in _built_paths():
+        pytest.skip("path %s not built" % want)
+    d = G.desc_from_problem(inputs.WORKLOADS[name].problem)
+    assert G.gconv_path_name(G.gconv_select_path(d)) == want
+
+
+def test_generic_supports_everything_and_plans():
+    rng = np.random.default_rng(9)
+    for i in range(100):
+        p = inputs.random_problem(rng, "f16", 2 + i % 2)
+        d = G.desc_from_problem(p)
+        assert G.gconv_path_supported(d, G.GCONV_PATH_GENERIC) == 1
+        pl = G.gconv_get_plan(d, G.GCONV_PATH_GENERIC)
+        assert pl["grid"][0] * pl["block"] >= metrics.outputs(p)
+        sel = G.gconv_select_path(d)
+        assert 0 <= sel < G.GCONV_NUM_PATHS
+        assert G.gconv_path_supported(d, sel) == 1
+        assert G.gconv_get_plan(d)["path"] == sel
+
+
+def test_bad_path_ids():
+    d = base_desc()
+    assert G.gconv_path_supported(d, 17) == G.GCONV_ERR_BAD_PATH
+    with pytest.raises(G.GconvError):
+        G.gconv_get_plan(d, 17)
+
+
+def test_errors_return_before_launch():
+    d = base_desc()
+    # null x / w / y
+    assert G.gconv_fwd(d, 0, 256, None, 512) == G.GCONV_ERR_NULL_PTR
+    assert G.gconv_fwd(d, 256, 0, None, 512) == G.GCONV_ERR_NULL_PTR
+    assert G.gconv_fwd(d, 256, 256, None, 0) == G.GCONV_ERR_NULL_PTR
+    # element misalignment (fp16 needs 2-byte alignment)
+    assert G.gconv_fwd(d, 257, 256, None, 512) == G.GCONV_ERR_MISALIGNED
+    assert G.gconv_fwd(d, 256, 256, 259, 512) == G.GCONV_ERR_MISALIGNED
+    # bad descriptor wins over pointers
+    assert G.gconv_fwd(base_desc(C=9), 256, 256, None, 512) == G.GCONV_ERR_BAD_DESC
+    # unknown path id
+    assert G.gconv_fwd_path(d, 9, 256, 256, None, 512) == G.GCONV_ERR_BAD_PATH
+
+
+def test_forced_vector_path_needs_16_byte_alignment():
+    for name, pid in G.PATHS.items():
+        if name == "generic" or name not in _built_paths():
+            continue
+        probe = {"depthwise": "depthwise2d_f16", "smallg_mfma": "grouped2d_resnext_bf16",
+                 "igemm_mfma": "grouped2d_large_bf16"}[name]
+        d = G.desc_from_problem(inputs.WORKLOADS[probe].problem)
+        assert G.gconv_fwd_path(d, pid, 256 + 2, 256, None, 512) == G.GCONV_ERR_MISALIGNED
+
+
+def test_forced_unsupported_path():
+    # fp32 grouped problem with 3 channels per group: no MFMA path takes it
+    d = G.make_desc(2, "f32", 1, 2, 6, 6, (8, 8), (3, 3), (1, 1), (1, 1), (1, 1))
+    for pid in (G.GCONV_PATH_DEPTHWISE, G.GCONV_PATH_SMALLG, G.GCONV_PATH_IGEMM):
+        assert G.gconv_path_supported(d, pid) == 0
+        assert G.gconv_fwd_path(d, pid, 256, 256, None, 512) == G.GCONV_ERR_PATH_UNSUPPORTED
+
+
+def test_status_strings():
+    for s in range(-9, 1):
+        assert isinstance(G.gconv_status_str(s), str) and G.gconv_status_str(s)
+    assert G.gconv_path_name(G.GCONV_PATH_AUTO) == "auto"
+    assert [G.gconv_path_name(i) for i in range(4)] == list(G.PATHS)
