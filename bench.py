@@ -124,6 +124,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="rough bound on the CPU oracle's timing sample")
     ap.add_argument("--hot", action="store_true", help="no buffer rotation (cache-hot; labelled)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="first run 3 plain device copies of MIB MiB (a reference kernel of "
+                         "known size for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     a = ap.parse_args()
 
     if a.gpus != 1:
@@ -137,6 +140,15 @@ def main():
         print("no GPU visible", file=sys.stderr)
         return 2
     G.lib()  # fail loudly if the HIP library is missing
+
+    if a.calibrate_copy:
+        nb = a.calibrate_copy << 20
+        src = torch.ones(nb // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     names, dominant = WORKLOAD_SETS[a.workload]
     path = G.GCONV_PATH_AUTO if a.path == "auto" else G.PATHS[a.path]

@@ -181,3 +181,32 @@ def test_misaligned_falls_back_or_errors():
     if sel != G.GCONV_PATH_GENERIC:
         rc = G.gconv_fwd_path(d, sel, xv.data_ptr(), w.data_ptr(), b.data_ptr(), y.data_ptr(), 0)
         assert rc == G.GCONV_ERR_MISALIGNED
+
+
+DW_CASES = [
+    # dtype, N, C, H, W, stride, pad, dil
+    ("f16", 1, 8, 5, 7, 1, 1, 1),
+    ("f16", 2, 24, 17, 13, 2, 1, 1),
+    ("bf16", 1, 40, 9, 31, 1, 2, 2),
+    ("bf16", 3, 144, 11, 57, 2, 1, 2),
+    ("f32", 2, 12, 19, 23, 1, 0, 1),
+    ("f32", 1, 100, 6, 6, 2, 2, 1),
+    ("f16", 1, 520, 7, 9, 1, 1, 1),     # more channel vectors than one slab holds
+    ("bf16", 2, 264, 30, 3, 1, 1, 2),
+    ("f16", 1, 16, 64, 1, 1, 1, 1),     # one column
+    ("f16", 1, 16, 1, 64, 2, 1, 1),     # one row
+]
+
+
+@pytest.mark.parametrize("case", range(len(DW_CASES)))
+def test_depthwise_shapes(case):
+    dtype, N, C, H, W, s, pd, dl = DW_CASES[case]
+    p = inputs.conv2d(dtype, N=N, G=C, C=C, K=C, H=H, W=W, Y=3, X=3, stride=s, pad=pd, dil=dl,
+                      bias=case % 2 == 0)
+    d = G.desc_from_problem(p)
+    assert G.gconv_path_supported(d, G.GCONV_PATH_DEPTHWISE) == 1, "depthwise path should take %r" % (p,)
+    t = inputs.make_tensors(p, 5000 + case)
+    st, pad, dil = p.spatial_args()
+    ref, scale = oracle.conv_fwd(*U.oracle_inputs(p, t), p.G, st, pad, dil)
+    y = run_and_fetch(p, t, G.GCONV_PATH_DEPTHWISE)
+    U.check(y, ref, scale, p.dtype, "depthwise %r" % (DW_CASES[case],))
