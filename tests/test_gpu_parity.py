@@ -210,3 +210,38 @@ def test_depthwise_shapes(case):
     ref, scale = oracle.conv_fwd(*U.oracle_inputs(p, t), p.G, st, pad, dil)
     y = run_and_fetch(p, t, G.GCONV_PATH_DEPTHWISE)
     U.check(y, ref, scale, p.dtype, "depthwise %r" % (DW_CASES[case],))
+
+
+SMALLG_CASES = [
+    # ndim, dtype, N, G, Cpg, Kpg, spatial (D,H,W), filt (Z,Y,X), stride, pad, dil, bias
+    (2, "bf16", 2, 32, 8, 8, (1, 13, 17), (1, 3, 3), 1, 1, 1, False),   # ResNeXt-like, ragged tiles
+    (2, "f16", 1, 8, 8, 8, (1, 9, 30), (1, 3, 3), 2, 1, 1, True),
+    (2, "bf16", 1, 16, 4, 4, (1, 11, 11), (1, 3, 3), 1, 2, 2, True),     # dilation 2
+    (2, "f16", 2, 4, 16, 16, (1, 7, 9), (1, 3, 3), 1, 1, 1, True),      # one group per tile
+    (2, "bf16", 1, 16, 4, 8, (1, 6, 40), (1, 5, 5), 1, 2, 1, True),     # 5x5
+    (2, "f16", 1, 64, 1, 2, (1, 10, 10), (1, 3, 3), 1, 1, 1, False),    # 8 groups per tile
+    (3, "f16", 1, 32, 2, 4, (8, 28, 28), (3, 3, 3), 1, 1, 1, True),     # the 3D workload at N=1
+    (3, "bf16", 2, 8, 2, 4, (5, 7, 9), (3, 3, 3), 1, 1, 1, True),
+    (3, "f16", 1, 16, 4, 4, (6, 5, 7), (3, 3, 3), 2, 1, 1, True),       # 14 MFMAs per tile
+    (3, "bf16", 1, 8, 8, 8, (4, 6, 6), (3, 1, 3), 1, (1, 0, 1), 1, False),
+    (3, "f16", 1, 4, 4, 4, (7, 7, 7), (3, 3, 3), 1, 2, 2, True),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SMALLG_CASES)))
+def test_smallg_shapes(case):
+    nd, dt, N, Gr, Cpg, Kpg, sp, fl, s, pd, dl, bias = SMALLG_CASES[case]
+    pad = pd if isinstance(pd, tuple) else (pd, pd, pd)
+    if nd == 2:
+        pad = (0, pad[1], pad[2])
+    p = inputs.Problem(nd, dt, N, Gr, Gr * Cpg, Gr * Kpg, sp, fl,
+                       (1, s, s) if nd == 2 else (s, s, s), pad,
+                       (1, dl, dl) if nd == 2 else (dl, dl, dl), bias)
+    d = G.desc_from_problem(p)
+    assert G.gconv_path_supported(d, G.GCONV_PATH_SMALLG) == 1, "small-group path should take %r" % (p,)
+    t = inputs.make_tensors(p, 6000 + case)
+    st, pa, di = p.spatial_args()
+    ref, scale = oracle.conv_fwd(*U.oracle_inputs(p, t), p.G, st, pa, di)
+    y = run_and_fetch(p, t, G.GCONV_PATH_SMALLG)
+    r = U.check(y, ref, scale, p.dtype, "smallg %r" % (SMALLG_CASES[case],))
+    print("smallg case %d max err/tol %.3f plan %s" % (case, r, G.gconv_get_plan(d, G.GCONV_PATH_SMALLG)))
