@@ -1,10 +1,359 @@
-// Placeholder: path not built yet (supported() is false, so it is never chosen).
+// Implicit-GEMM grouped convolution on the matrix cores (fp16 / bf16, 2D and
+// 3D), for groups with many channels (Cpg % 32 == 0, Kpg % 64 == 0).
+//
+// Per group g the convolution is a GEMM: M = output pixels (N * Do * Ho *
+// Wo), N = Kpg output channels, K = taps * Cpg.  The group is the grid's z
+// coordinate and the grid is (M tiles, N tiles, G), after the grid-per-group
+// scheme of rocm-libraries PR 10064 (Technical Details: the launch grid is
+// (gn, gm, groups)).  K is decoded into (tap, channel in group) with the
+// channel fastest, as that page's A descriptor does, so the im2col operand is
+// never materialised: for one K stage (one tap, KT consecutive channels) each
+// output pixel needs KT contiguous input channels of one input pixel, or
+// zeros when the tap falls into the padding.  The weight operand of a stage
+// is KT contiguous values of each output channel's GKZYXC row (the B
+// descriptor's channel extent is Cpg).
+//
+// A workgroup (4 waves, 2 x 2) computes a BM x BN output tile.  Every K stage
+// of both operands is staged in LDS by direct-to-LDS buffer loads (zero fill
+// from the buffer range check), double-buffered: the loads of stage s+1 are
+// in flight while stage s is multiplied (v_mfma_f32_16x16x32, fp32
+// accumulators).  Rows are padded by one 16-byte slot so the 16 rows read by
+// one MFMA operand fall in different LDS banks.  The weights are the first
+// MFMA operand, so each lane ends with four adjacent output channels of one
+// pixel: the fused epilogue adds the bias, rounds and stores 8 bytes.
+#include "device_common.h"
 #include "gconv_internal.h"
 
 namespace gconv {
 namespace igemm {
-bool supported(const Problem &) { return false; }
-gconv_plan plan(const Problem &) { return gconv_plan{}; }
-hipError_t launch(const Problem &, const Args &, hipStream_t) { return hipErrorInvalidValue; }
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kWaves = 4;
+constexpr int BM = 128;
+constexpr unsigned kOob = 0x80000000u;
+
+typedef int rsrc_t __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+struct Params {
+    int N, G, Cpg, Kpg, C, K;
+    int D, H, W, Do, Ho, Wo, Z, Y, X;
+    int sd, sh, sw, pd, ph, pw, dd, dh, dw;
+    int M;                 // N * Do * Ho * Wo
+    int mtiles, ntiles;    // grid x, y
+    int stages;            // taps * Cpg / KT
+    unsigned x_bytes, w_bytes;
+};
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, unsigned bytes)
+{
+    const unsigned long long a = (unsigned long long)base;
+    rsrc_t r;
+    r.x = (int)(unsigned)(a & 0xffffffffull);
+    r.y = (int)(unsigned)((a >> 32) & 0xffffull);
+    r.z = (int)bytes;
+    r.w = 0x00020000;
+    return r;
+}
+
+__device__ __forceinline__ void dma16(unsigned voffset, unsigned lds_byte, rsrc_t r)
+{
+    asm volatile("s_mov_b32 m0, %1\n\t"
+                 "s_nop 0\n\t"
+                 "buffer_load_dwordx4 %0, %2, 0 offen lds"
+                 :
+                 : "v"(voffset), "s"(lds_byte), "s"(r)
+                 : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(n) for a wave-uniform n (other counters not waited on).
+__device__ __forceinline__ void vm_wait(int n)
+{
+#define GCONV_VMW(k) \
+    case k: __builtin_amdgcn_s_waitcnt(((k) & 15) | (7 << 4) | (15 << 8) | (((k) >> 4) << 14)); break;
+    switch (__builtin_amdgcn_readfirstlane(n)) {
+        GCONV_VMW(1) GCONV_VMW(2) GCONV_VMW(3) GCONV_VMW(4) GCONV_VMW(5) GCONV_VMW(6)
+        GCONV_VMW(7) GCONV_VMW(8) GCONV_VMW(9) GCONV_VMW(10) GCONV_VMW(11) GCONV_VMW(12)
+        GCONV_VMW(13) GCONV_VMW(14) GCONV_VMW(15) GCONV_VMW(16) GCONV_VMW(17) GCONV_VMW(18)
+        GCONV_VMW(19) GCONV_VMW(20) GCONV_VMW(21) GCONV_VMW(22) GCONV_VMW(23) GCONV_VMW(24)
+    default: __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); break;   // vmcnt(0)
+    }
+#undef GCONV_VMW
+}
+
+template <typename T> struct Mfma;
+template <> struct Mfma<_Float16> {
+    typedef f16x8 V;
+    static __device__ __forceinline__ f32x4 run(V a, V b, f32x4 c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct Mfma<__bf16> {
+    typedef bf16x8 V;
+    static __device__ __forceinline__ f32x4 run(V a, V b, f32x4 c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+// BN: output channels per tile (64 or 128); KT: K per stage (32 or 64).
+template <typename T, int BN, int KT>
+__global__ __launch_bounds__(kBlock) void kernel(Params q, const T *__restrict__ x,
+                                                 const T *__restrict__ w,
+                                                 const T *__restrict__ bias, T *__restrict__ y)
+{
+    typedef typename Mfma<T>::V V;
+    constexpr int RS = KT / 8 + 1;              // 16-byte slots per staged row (one pad)
+    constexpr int A_SLOTS = BM * RS, B_SLOTS = BN * RS;
+    constexpr int A_INSTR = (A_SLOTS + 63) / 64, B_INSTR = (B_SLOTS + 63) / 64;
+    constexpr int INSTR = A_INSTR + B_INSTR;    // load instructions per stage (all waves)
+    constexpr int LPW = (INSTR + kWaves - 1) / kWaves;
+    constexpr int STAGE_BYTES = (A_SLOTS + B_SLOTS) * 16;
+    constexpr int WM = BM / 2, WN = BN / 2;     // wave tile
+    constexpr int TM = WM / 16, TN = WN / 16;   // MFMA tiles per wave
+    constexpr int KS = KT / 32;                 // MFMA K steps per stage
+    extern __shared__ uint4 lds[];
+
+    const int t = threadIdx.x;
+    const int wave = t >> 6, lane = t & 63;
+    const int g = blockIdx.z;
+    const int nb = blockIdx.y;
+    const int mb = (int)blockIdx.x;
+    const int m0 = mb * BM, n0 = nb * BN;
+    const int taps = q.Z * q.Y * q.X;
+    const unsigned es = (unsigned)sizeof(T);
+    const rsrc_t rx = make_rsrc(x, q.x_bytes);
+    const rsrc_t rw = make_rsrc(w, q.w_bytes);
+    const unsigned lds_b = (unsigned)(size_t)lds;
+
+    // ---- this lane's share of a stage's loads: instruction k = wave + 4 i.
+    // Instructions [0, A_INSTR) fill the input tile (row = output pixel),
+    // the rest the weight tile (row = output channel).  Slot j of a row is
+    // channel vector j of the stage; slot RS-1 is the zero pad.
+    int ld_kind[LPW];           // 0 none, 1 input, 2 weight
+    int ld_slot[LPW];           // slot within its row
+    int ld_pix_n[LPW], ld_pix_d[LPW], ld_pix_h[LPW], ld_pix_w[LPW];   // input row: pixel origin
+    int ld_wrow[LPW];           // weight row: output channel index g*Kpg + n
+    unsigned ld_m0[LPW];        // LDS byte offset inside a stage buffer
+    int nld = 0;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+        const int k = wave + kWaves * i;
+        ld_kind[i] = 0; ld_slot[i] = RS - 1; ld_pix_n[i] = -1; ld_pix_d[i] = 0; ld_pix_h[i] = 0;
+        ld_pix_w[i] = 0; ld_wrow[i] = -1; ld_m0[i] = 0;
+        if (k < A_INSTR) {
+            const int L = k * 64 + lane;
+            nld = i + 1;
+            ld_kind[i] = L < A_SLOTS ? 1 : 0;
+            ld_m0[i] = (unsigned)(k * 64) * 16u;
+            const int row = L / RS;
+            ld_slot[i] = L - row * RS;
+            const int m = m0 + row;
+            if (L < A_SLOTS && m < q.M) {
+                int r = m;
+                const int ow = r % q.Wo; r /= q.Wo;
+                const int oh = r % q.Ho; r /= q.Ho;
+                const int od = r % q.Do;
+                ld_pix_n[i] = r / q.Do;
+                ld_pix_d[i] = od * q.sd - q.pd;
+                ld_pix_h[i] = oh * q.sh - q.ph;
+                ld_pix_w[i] = ow * q.sw - q.pw;
+            }
+        } else if (k < INSTR) {
+            const int L = (k - A_INSTR) * 64 + lane;
+            nld = i + 1;
+            ld_kind[i] = L < B_SLOTS ? 2 : 0;
+            ld_m0[i] = (unsigned)(A_SLOTS * 16) + (unsigned)((k - A_INSTR) * 64) * 16u;
+            const int row = L / RS;
+            ld_slot[i] = L - row * RS;
+            if (L < B_SLOTS && n0 + row < q.Kpg) ld_wrow[i] = g * q.Kpg + n0 + row;
+        }
+    }
+    // issue stage st (tap st / (Cpg/KT), channels c0 .. c0+KT-1) into buffer b
+    const int cstages = q.Cpg / KT;
+    auto issue = [&](int st, int b) {
+        const int tap = st / cstages;
+        const int c0 = (st - tap * cstages) * KT;
+        const int xx = tap % q.X, yy = (tap / q.X) % q.Y, zz = tap / (q.X * q.Y);
+        const unsigned base = lds_b + (unsigned)(b * STAGE_BYTES);
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) {
+            if (i < nld) {
+                unsigned vo = kOob;
+                if (ld_kind[i] == 1 && ld_slot[i] < RS - 1 && ld_pix_n[i] >= 0) {
+                    const int id = ld_pix_d[i] + zz * q.dd, ih = ld_pix_h[i] + yy * q.dh,
+                              iw = ld_pix_w[i] + xx * q.dw;
+                    if (id >= 0 && id < q.D && ih >= 0 && ih < q.H && iw >= 0 && iw < q.W)
+                        vo = ((unsigned)(((ld_pix_n[i] * q.D + id) * q.H + ih) * q.W + iw) * (unsigned)q.C +
+                              (unsigned)(g * q.Cpg + c0 + ld_slot[i] * 8)) * es;
+                } else if (ld_kind[i] == 2 && ld_slot[i] < RS - 1 && ld_wrow[i] >= 0) {
+                    vo = ((unsigned)(ld_wrow[i] * taps + tap) * (unsigned)q.Cpg +
+                          (unsigned)(c0 + ld_slot[i] * 8)) * es;
+                }
+                if (ld_kind[i] != 0) {
+                    // input instructions read through the x buffer, weight ones through w
+                    const int k = wave + kWaves * i;
+                    if (k < A_INSTR) dma16(vo, __builtin_amdgcn_readfirstlane(base + ld_m0[i]), rx);
+                    else dma16(vo, __builtin_amdgcn_readfirstlane(base + ld_m0[i]), rw);
+                }
+            }
+        }
+    };
+
+    // ---- fragments: lane (l16 = lane % 16, kq = lane / 16)
+    const int l16 = lane & 15, kq = lane >> 4;
+    const int wm = (wave & 1) * WM, wn = (wave >> 1) * WN;
+    f32x4 acc[TM][TN];
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nst = q.stages;
+    issue(0, 0);
+    for (int st = 0; st < nst; ++st) {
+        const int b = st & 1;
+        // this wave's loads of stage st are in when none issued later remain
+        vm_wait(0);
+        __syncthreads();
+        if (st + 1 < nst) issue(st + 1, b ^ 1);   // buffer b^1 was last read before the barrier
+        const char *sb = reinterpret_cast<const char *>(lds) + b * STAGE_BYTES;
+        const char *sa = sb;                                  // input tile rows (pixels)
+        const char *sw_ = sb + A_SLOTS * 16;                  // weight tile rows (channels)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            V wf[TN], xf[TM];
+#pragma unroll
+            for (int nt = 0; nt < TN; ++nt) {
+                const uint4 raw = *reinterpret_cast<const uint4 *>(sw_ + ((wn + nt * 16 + l16) * RS + ks * 4 + kq) * 16);
+                wf[nt] = *reinterpret_cast<const V *>(&raw);
+            }
+#pragma unroll
+            for (int mt = 0; mt < TM; ++mt) {
+                const uint4 raw = *reinterpret_cast<const uint4 *>(sa + ((wm + mt * 16 + l16) * RS + ks * 4 + kq) * 16);
+                xf[mt] = *reinterpret_cast<const V *>(&raw);
+            }
+#pragma unroll
+            for (int mt = 0; mt < TM; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < TN; ++nt) acc[mt][nt] = Mfma<T>::run(wf[nt], xf[mt], acc[mt][nt]);
+        }
+    }
+
+    // ---- epilogue: acc[mt][nt][i] = channel n0 + wn + nt*16 + 4 kq + i of pixel m0 + wm + mt*16 + l16
+#pragma unroll
+    for (int nt = 0; nt < TN; ++nt) {
+        const int ch = n0 + wn + nt * 16 + 4 * kq;            // channel within the group
+        float bv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (bias && ch < q.Kpg) {
+            const uint2 braw = *reinterpret_cast<const uint2 *>(bias + g * q.Kpg + ch);
+            const T *bel = reinterpret_cast<const T *>(&braw);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) bv[i] = to_f32(bel[i]);
+        }
+#pragma unroll
+        for (int mt = 0; mt < TM; ++mt) {
+            const int m = m0 + wm + mt * 16 + l16;
+            if (m < q.M && ch < q.Kpg) {
+                T o[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[i] = from_f32<T>(acc[mt][nt][i] + bv[i]);
+                *reinterpret_cast<uint2 *>(y + (size_t)m * q.K + g * q.Kpg + ch) = *reinterpret_cast<const uint2 *>(o);
+            }
+        }
+    }
+}
+
+// ----------------------------------------------------------------- host side
+
+struct Config {
+    int BN, KT, mtiles, ntiles, stages, lds;
+};
+
+bool configure(const Problem &p, Config &c)
+{
+    if (p.dtype != GCONV_F16 && p.dtype != GCONV_BF16) return false;
+    if (p.Cpg % 32 != 0 || p.Kpg % 64 != 0) return false;
+    const long long xb = (long long)p.N * p.D * p.H * p.W * p.C() * 2;
+    const long long wb = (long long)p.K() * p.taps() * p.Cpg * 2;
+    if (xb >= (1LL << 31) || wb >= (1LL << 31)) return false;
+    const long long M = (long long)p.N * p.Do * p.Ho * p.Wo;
+    if (M >= (1LL << 31)) return false;
+    c.BN = p.Kpg % 128 == 0 ? 128 : 64;
+    c.KT = p.Cpg % 64 == 0 ? 64 : 32;
+    c.mtiles = (int)((M + BM - 1) / BM);
+    c.ntiles = p.Kpg / c.BN;
+    c.stages = p.taps() * p.Cpg / c.KT;
+    const int RS = c.KT / 8 + 1;
+    c.lds = 2 * (BM + c.BN) * RS * 16;
+    return c.mtiles < (1 << 30) && c.ntiles < 65536 && p.G < 65536;
+}
+
+template <typename T, int BN, int KT>
+hipError_t go3(const Problem &p, const Config &c, const Args &a, hipStream_t s)
+{
+    Params q;
+    q.N = p.N; q.G = p.G; q.Cpg = p.Cpg; q.Kpg = p.Kpg; q.C = p.C(); q.K = p.K();
+    q.D = p.D; q.H = p.H; q.W = p.W; q.Do = p.Do; q.Ho = p.Ho; q.Wo = p.Wo;
+    q.Z = p.Z; q.Y = p.Y; q.X = p.X;
+    q.sd = p.sd; q.sh = p.sh; q.sw = p.sw; q.pd = p.pd; q.ph = p.ph; q.pw = p.pw;
+    q.dd = p.dd; q.dh = p.dh; q.dw = p.dw;
+    q.M = p.N * p.Do * p.Ho * p.Wo;
+    q.mtiles = c.mtiles; q.ntiles = c.ntiles; q.stages = c.stages;
+    q.x_bytes = (unsigned)((long long)p.N * p.D * p.H * p.W * p.C() * 2);
+    q.w_bytes = (unsigned)((long long)p.K() * p.taps() * p.Cpg * 2);
+    auto k = kernel<T, BN, KT>;
+    static bool lds_set = false;
+    if (c.lds > 64 * 1024 && !lds_set) {
+        hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        lds_set = true;
+    }
+    hipLaunchKernelGGL(k, dim3(c.mtiles, c.ntiles, p.G), dim3(kBlock), c.lds, s, q,
+                       (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t go(const Problem &p, const Config &c, const Args &a, hipStream_t s)
+{
+    if (c.BN == 128) return c.KT == 64 ? go3<T, 128, 64>(p, c, a, s) : go3<T, 128, 32>(p, c, a, s);
+    return c.KT == 64 ? go3<T, 64, 64>(p, c, a, s) : go3<T, 64, 32>(p, c, a, s);
+}
+
+}  // namespace
+
+bool supported(const Problem &p)
+{
+    Config c;
+    return configure(p, c);
+}
+
+gconv_plan plan(const Problem &p)
+{
+    Config c;
+    configure(p, c);
+    gconv_plan pl{};
+    pl.path = GCONV_PATH_IGEMM;
+    pl.grid[0] = (uint32_t)c.mtiles;
+    pl.grid[1] = (uint32_t)c.ntiles;
+    pl.grid[2] = (uint32_t)p.G;
+    pl.block = kBlock;
+    pl.lds_bytes = (uint32_t)c.lds;
+    pl.groups_per_tile = 1;
+    return pl;
+}
+
+hipError_t launch(const Problem &p, const Args &a, hipStream_t s)
+{
+    Config c;
+    if (!configure(p, c)) return hipErrorInvalidValue;
+    if (p.dtype == GCONV_F16) return go<_Float16>(p, c, a, s);
+    return go<__bf16>(p, c, a, s);
+}
+
 }  // namespace igemm
 }  // namespace gconv

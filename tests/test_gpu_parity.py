@@ -245,3 +245,33 @@ def test_smallg_shapes(case):
     y = run_and_fetch(p, t, G.GCONV_PATH_SMALLG)
     r = U.check(y, ref, scale, p.dtype, "smallg %r" % (SMALLG_CASES[case],))
     print("smallg case %d max err/tol %.3f plan %s" % (case, r, G.gconv_get_plan(d, G.GCONV_PATH_SMALLG)))
+
+
+IGEMM_CASES = [
+    # ndim, dtype, N, G, Cpg, Kpg, spatial (D,H,W), filt (Z,Y,X), stride, pad, dil, bias
+    (2, "bf16", 1, 2, 128, 128, (1, 14, 14), (1, 3, 3), 1, 1, 1, True),     # the large-group case, small batch
+    (2, "bf16", 1, 2, 128, 128, (1, 14, 14), (1, 3, 3), 1, 2, 2, True),     # its dilation-2 variant
+    (2, "f16", 2, 3, 64, 64, (1, 9, 11), (1, 3, 3), 2, 1, 1, False),        # stride 2, ragged M
+    (2, "bf16", 1, 1, 32, 192, (1, 7, 13), (1, 1, 1), 1, 0, 1, True),       # 1x1, KT=32, BN=64 tiles
+    (2, "f16", 1, 4, 96, 64, (1, 10, 10), (1, 5, 3), 1, (0, 2, 1), 1, True),  # 5x3 filter, Cpg=96
+    (3, "bf16", 1, 2, 64, 128, (4, 6, 7), (3, 3, 3), 1, 1, 1, True),
+    (3, "f16", 2, 2, 32, 64, (5, 5, 5), (3, 1, 3), (2, 1, 1), 1, (1, 2, 1), False),
+]
+
+
+@pytest.mark.parametrize("case", range(len(IGEMM_CASES)))
+def test_igemm_shapes(case):
+    nd, dt, N, Gr, Cpg, Kpg, sp, fl, s, pd, dl, bias = IGEMM_CASES[case]
+    tr = lambda v, fill: (v if isinstance(v, tuple) else (v, v, v))
+    st, pad, dil = tr(s, 1), tr(pd, 0), tr(dl, 1)
+    if nd == 2:
+        st, pad, dil = (1, st[1], st[2]), (0, pad[1], pad[2]), (1, dil[1], dil[2])
+    p = inputs.Problem(nd, dt, N, Gr, Gr * Cpg, Gr * Kpg, sp, fl, st, pad, dil, bias)
+    d = G.desc_from_problem(p)
+    assert G.gconv_path_supported(d, G.GCONV_PATH_IGEMM) == 1, "implicit-GEMM path should take %r" % (p,)
+    t = inputs.make_tensors(p, 7000 + case)
+    sa, pa, da = p.spatial_args()
+    ref, scale = oracle.conv_fwd(*U.oracle_inputs(p, t), p.G, sa, pa, da)
+    y = run_and_fetch(p, t, G.GCONV_PATH_IGEMM)
+    r = U.check(y, ref, scale, p.dtype, "igemm %r" % (IGEMM_CASES[case],))
+    print("igemm case %d max err/tol %.3f plan %s" % (case, r, G.gconv_get_plan(d, G.GCONV_PATH_IGEMM)))
