@@ -43,26 +43,16 @@ PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 ROTATE_BYTES = 512 << 20
 
 
-def kernel_source_hash() -> str:
-    """Hash of the kernel sources; the stored counter-based traffic is only valid for it."""
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "depthwise_convolution_grouped_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(f.encode() + b"\0" + fh.read())
-    return h.hexdigest()[:16]
-
-
-def stored_traffic(workload: str):
+def stored_traffic(workload: str, path_name: str):
     """HBM bytes per launch from committed rocprofv3 counters, if taken on these sources."""
+    from depthwise_convolution_grouped_amd.profile_summary import source_hash
     try:
         with open(PROFILE_TRAFFIC) as f:
             db = json.load(f)
     except (OSError, ValueError):
         return None
     e = db.get(workload)
-    if not e or e.get("source_hash") != kernel_source_hash():
+    if not e or e.get("kernel") != path_name or e.get("source_hash") != source_hash(path_name):
         return None
     return e.get("hbm_bytes_per_launch")
 
@@ -172,7 +162,9 @@ def main():
         o = G.gconv_out_dims(d)
         oshape = (p.N,) + (o if p.ndim == 3 else o[1:]) + (p.K,)
         per_set = metrics.io_bytes(p)["x"] + metrics.io_bytes(p)["y"]
-        R = 1 if a.hot else max(2, -(-ROTATE_BYTES // per_set))
+        # enough sets to span 512 MB (twice the 256 MB Infinity Cache), at most
+        # 64: a workload that small is launch-bound and gains nothing from more
+        R = 1 if a.hot else min(64, max(2, -(-ROTATE_BYTES // per_set)))
         x0 = to_dev(t.x, p.dtype)
         xs = [x0] + [x0.clone() for _ in range(R - 1)]
         ys = [torch.empty(oshape, dtype=tdt[p.dtype], device=dev) for _ in range(R)]
@@ -256,7 +248,7 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": dom_cfg["tflops"], "peak": peak_tf,
                 "unit": "TFLOP/s", "frac": dom_cfg["tflops"] / peak_tf}
-    roof["traffic"] = stored_traffic(dominant)
+    roof["traffic"] = stored_traffic(dominant, dom_cfg["path"])
     roof["kernel"] = dom_cfg["path"]
     roof["workload"] = dominant
     roof["algorithmic_bytes"] = metrics.total_bytes(dp)
@@ -284,7 +276,6 @@ def main():
         "per_config": per_config,
         "roofline": roof,
         "cpu_baseline": None,
-        "kernel_source_hash": kernel_source_hash(),
     }
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(names, a.cpu_seconds)
