@@ -99,6 +99,7 @@ bool path_ok(const Problem &p, int path)
     case GCONV_PATH_DEPTHWISE: return depthwise::supported(p);
     case GCONV_PATH_SMALLG: return smallg::supported(p);
     case GCONV_PATH_IGEMM: return igemm::supported(p);
+    case GCONV_PATH_IGHALO: return ighalo::supported(p);
     default: return false;
     }
 }
@@ -111,9 +112,12 @@ bool path_ok(const Problem &p, int path)
 int select(const Problem &p)
 {
     if (depthwise::supported(p)) return GCONV_PATH_DEPTHWISE;
-    if (p.dtype != GCONV_F32 && p.Cpg >= 32 && p.Kpg >= 32 && igemm::supported(p))
-        return GCONV_PATH_IGEMM;
+    if (p.dtype != GCONV_F32 && p.Cpg >= 32 && p.Kpg >= 32) {
+        if (ighalo::supported(p)) return GCONV_PATH_IGHALO;
+        if (igemm::supported(p)) return GCONV_PATH_IGEMM;
+    }
     if (smallg::supported(p)) return GCONV_PATH_SMALLG;
+    if (ighalo::supported(p)) return GCONV_PATH_IGHALO;
     if (igemm::supported(p)) return GCONV_PATH_IGEMM;
     return GCONV_PATH_GENERIC;
 }
@@ -124,6 +128,7 @@ gconv_plan plan_of(const Problem &p, int path)
     case GCONV_PATH_DEPTHWISE: return depthwise::plan(p);
     case GCONV_PATH_SMALLG: return smallg::plan(p);
     case GCONV_PATH_IGEMM: return igemm::plan(p);
+    case GCONV_PATH_IGHALO: return ighalo::plan(p);
     default: return generic::plan(p);
     }
 }
@@ -131,7 +136,7 @@ gconv_plan plan_of(const Problem &p, int path)
 bool aligned(const void *ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
 
 int run(const gconv_desc *d, int path, const void *x, const void *w, const void *bias,
-        void *y, void *stream)
+        void *y, void *stream, void *ev_start = nullptr, void *ev_stop = nullptr)
 {
     int64_t out[3];
     int rc = check_desc(d, out);
@@ -143,7 +148,8 @@ int run(const gconv_desc *d, int path, const void *x, const void *w, const void 
         return GCONV_ERR_MISALIGNED;
     // The vector paths load and store 16-byte channel vectors; automatic
     // dispatch falls back to the generic kernel for other pointers.
-    const bool vec_ok = aligned(x, 16) && aligned(w, 16) && aligned(y, 16);
+    const bool vec_ok = aligned(x, 16) && aligned(w, 16) && aligned(y, 16) &&
+                        (!bias || aligned(bias, 16));
     if (path == GCONV_PATH_AUTO) {
         path = select(p);
         if (!vec_ok) path = GCONV_PATH_GENERIC;
@@ -152,13 +158,14 @@ int run(const gconv_desc *d, int path, const void *x, const void *w, const void 
         if (!path_ok(p, path)) return GCONV_ERR_PATH_UNSUPPORTED;
         if (path != GCONV_PATH_GENERIC && !vec_ok) return GCONV_ERR_MISALIGNED;
     }
-    Args a{x, w, bias, y};
+    Args a{x, w, bias, y, (hipEvent_t)ev_start, (hipEvent_t)ev_stop};
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
     switch (path) {
     case GCONV_PATH_DEPTHWISE: e = depthwise::launch(p, a, s); break;
     case GCONV_PATH_SMALLG: e = smallg::launch(p, a, s); break;
     case GCONV_PATH_IGEMM: e = igemm::launch(p, a, s); break;
+    case GCONV_PATH_IGHALO: e = ighalo::launch(p, a, s); break;
     default: e = generic::launch(p, a, s); break;
     }
     if (e != hipSuccess) return GCONV_ERR_LAUNCH;
@@ -229,6 +236,13 @@ GCONV_API int gconv_fwd_path(const gconv_desc *d, int path, const void *x, const
     return run(d, path, x, w, bias, y, stream);
 }
 
+GCONV_API int gconv_fwd_timed(const gconv_desc *d, int path, const void *x, const void *w,
+                              const void *bias, void *y, void *stream, void *ev_start,
+                              void *ev_stop)
+{
+    return run(d, path, x, w, bias, y, stream, ev_start, ev_stop);
+}
+
 GCONV_API const char *gconv_status_str(int status)
 {
     switch (status) {
@@ -253,6 +267,7 @@ GCONV_API const char *gconv_path_name(int path)
     case GCONV_PATH_DEPTHWISE: return "depthwise";
     case GCONV_PATH_SMALLG: return "smallg_mfma";
     case GCONV_PATH_IGEMM: return "igemm_mfma";
+    case GCONV_PATH_IGHALO: return "ighalo_mfma";
     default: return "unknown";
     }
 }

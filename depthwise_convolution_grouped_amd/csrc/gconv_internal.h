@@ -4,6 +4,7 @@
 
 #include <stdint.h>
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "gconv.h"
@@ -32,7 +33,23 @@ struct Args {
     const void *w;
     const void *bias;   // may be null
     void *y;
+    hipEvent_t ev_start = nullptr;   // optional, bound to the kernel dispatch
+    hipEvent_t ev_stop = nullptr;
 };
+
+template <class T> struct exactly { using type = T; };
+
+// Enqueues kernel `k` on `s` with arguments converted to exactly its own
+// parameter types.  Events in `a` (either may be null) are bound to this
+// dispatch by hipExtLaunchKernel, so their elapsed time is the kernel's own
+// execution time, with no marker packets around it.
+template <typename... KP>
+hipError_t enqueue(void (*k)(KP...), dim3 grid, dim3 block, unsigned lds, hipStream_t s,
+                   const Args &a, typename exactly<KP>::type... args)
+{
+    void *argv[] = {(void *)&args...};
+    return hipExtLaunchKernel((const void *)k, grid, block, argv, lds, s, a.ev_start, a.ev_stop, 0);
+}
 
 // Per-path hooks.  `supported` and `plan` are pure host functions (no HIP
 // call); `launch` enqueues exactly one kernel on `stream`.
@@ -52,6 +69,11 @@ gconv_plan plan(const Problem &p);
 hipError_t launch(const Problem &p, const Args &a, hipStream_t s);
 }
 namespace igemm {
+bool supported(const Problem &p);
+gconv_plan plan(const Problem &p);
+hipError_t launch(const Problem &p, const Args &a, hipStream_t s);
+}
+namespace ighalo {
 bool supported(const Problem &p);
 gconv_plan plan(const Problem &p);
 hipError_t launch(const Problem &p, const Args &a, hipStream_t s);

@@ -403,9 +403,8 @@ hipError_t go3(const Problem &p, const Config &c, const Args &a, hipStream_t s)
     auto k = kernel<T, SH, DH>;
     if (c.lds > 64 * 1024)
         hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, c.lds);
-    hipLaunchKernelGGL(k, dim3(blocks), dim3(kBlock), c.lds, s, q, (const T *)a.x,
-                       (const T *)a.w, (const T *)a.bias, (T *)a.y);
-    return hipGetLastError();
+    return enqueue(k, dim3(blocks), dim3(kBlock), c.lds, s, a, q, (const T *)a.x,
+                   (const T *)a.w, (const T *)a.bias, (T *)a.y);
 }
 
 template <typename T>

@@ -55,9 +55,8 @@ hipError_t go(const Problem &p, const Args &a, hipStream_t s)
     using T = typename Elem<DT>::T;
     const int total = (int)p.y_elems();
     const int blocks = (total + kBlock - 1) / kBlock;
-    hipLaunchKernelGGL(kernel<T>, dim3(blocks), dim3(kBlock), 0, s, p,
-                       (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y, total);
-    return hipGetLastError();
+    return enqueue(kernel<T>, dim3(blocks), dim3(kBlock), 0, s, a, p,
+                   (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y, total);
 }
 
 }  // namespace

@@ -312,9 +312,8 @@ hipError_t go3(const Problem &p, const Config &c, const Args &a, hipStream_t s)
         hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         lds_set = true;
     }
-    hipLaunchKernelGGL(k, dim3(c.mtiles, c.ntiles, p.G), dim3(kBlock), c.lds, s, q,
-                       (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y);
-    return hipGetLastError();
+    return enqueue(k, dim3(c.mtiles, c.ntiles, p.G), dim3(kBlock), c.lds, s, a, q,
+                   (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y);
 }
 
 template <typename T>

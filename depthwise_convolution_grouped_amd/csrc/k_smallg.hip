@@ -385,9 +385,8 @@ hipError_t go4(const Problem &p, const Config &c, const Args &a, hipStream_t s)
         hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsTile);
         lds_set = true;
     }
-    hipLaunchKernelGGL(k, dim3(blocks), dim3(kBlock), c.lds, s, q, (const T *)a.x,
-                       (const T *)a.w, (const T *)a.bias, (T *)a.y);
-    return hipGetLastError();
+    return enqueue(k, dim3(blocks), dim3(kBlock), c.lds, s, a, q, (const T *)a.x,
+                   (const T *)a.w, (const T *)a.bias, (T *)a.y);
 }
 
 template <typename T, int CPGC>

@@ -39,12 +39,13 @@ GCONV_PATH_GENERIC = 0
 GCONV_PATH_DEPTHWISE = 1
 GCONV_PATH_SMALLG = 2
 GCONV_PATH_IGEMM = 3
-GCONV_NUM_PATHS = 4
-PATHS = {"generic": 0, "depthwise": 1, "smallg_mfma": 2, "igemm_mfma": 3}
+GCONV_PATH_IGHALO = 4
+GCONV_NUM_PATHS = 5
+PATHS = {"generic": 0, "depthwise": 1, "smallg_mfma": 2, "igemm_mfma": 3, "ighalo_mfma": 4}
 
 EXPORTS = ("gconv_validate", "gconv_out_dims", "gconv_select_path", "gconv_path_supported",
-           "gconv_get_plan", "gconv_fwd", "gconv_fwd_path", "gconv_status_str",
-           "gconv_path_name", "gconv_abi_version")
+           "gconv_get_plan", "gconv_fwd", "gconv_fwd_path", "gconv_fwd_timed",
+           "gconv_status_str", "gconv_path_name", "gconv_abi_version")
 
 
 class GconvUnavailable(RuntimeError):
@@ -98,13 +99,15 @@ def lib():
     L.gconv_get_plan.argtypes = [pd, ctypes.c_int, ctypes.POINTER(gconv_plan)]
     L.gconv_fwd.argtypes = [pd, vp, vp, vp, vp, vp]
     L.gconv_fwd_path.argtypes = [pd, ctypes.c_int, vp, vp, vp, vp, vp]
+    L.gconv_fwd_timed.argtypes = [pd, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp]
     L.gconv_status_str.argtypes = [ctypes.c_int]
     L.gconv_status_str.restype = ctypes.c_char_p
     L.gconv_path_name.argtypes = [ctypes.c_int]
     L.gconv_path_name.restype = ctypes.c_char_p
     L.gconv_abi_version.argtypes = []
     for name in ("gconv_validate", "gconv_out_dims", "gconv_select_path", "gconv_path_supported",
-                 "gconv_get_plan", "gconv_fwd", "gconv_fwd_path", "gconv_abi_version"):
+                 "gconv_get_plan", "gconv_fwd", "gconv_fwd_path", "gconv_fwd_timed",
+                 "gconv_abi_version"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -174,6 +177,13 @@ def gconv_fwd(d: gconv_desc, x: int, w: int, bias: Optional[int], y: int, stream
 def gconv_fwd_path(d: gconv_desc, path: int, x: int, w: int, bias: Optional[int], y: int,
                    stream: int = 0) -> int:
     return lib().gconv_fwd_path(ctypes.byref(d), int(path), x, w, bias or None, y, stream or None)
+
+
+def gconv_fwd_timed(d: gconv_desc, path: int, x: int, w: int, bias: Optional[int], y: int,
+                    stream: int, ev_start: int, ev_stop: int) -> int:
+    """gconv_fwd_path with two hipEvent_t handles bound to the kernel dispatch."""
+    return lib().gconv_fwd_timed(ctypes.byref(d), int(path), x, w, bias or None, y,
+                                 stream or None, ev_start or None, ev_stop or None)
 
 
 def gconv_status_str(status: int) -> str:

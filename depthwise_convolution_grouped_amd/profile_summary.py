@@ -35,10 +35,11 @@ PATH_SOURCES = {
     "depthwise": "k_depthwise.hip",
     "smallg_mfma": "k_smallg.hip",
     "igemm_mfma": "k_igemm.hip",
+    "ighalo_mfma": "k_ighalo.hip",
 }
 SHARED = ("device_common.h", "gconv_internal.h")
 KERNEL_TAGS = {"generic": "generic", "depthwise": "depthwise", "smallg_mfma": "smallg",
-               "igemm_mfma": "igemm"}
+               "igemm_mfma": "igemm", "ighalo_mfma": "ighalo"}
 
 
 def source_hash(path_name: str) -> str:

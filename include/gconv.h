@@ -77,8 +77,10 @@ typedef enum gconv_path {
     GCONV_PATH_GENERIC = 0,     /* one thread per output, any shape */
     GCONV_PATH_DEPTHWISE = 1,   /* Cpg = Kpg = 1: LDS halo tile, channel vectors, VALU */
     GCONV_PATH_SMALLG = 2,      /* small groups: LDS halo tile, block-diagonal MFMA */
-    GCONV_PATH_IGEMM = 3,       /* large groups: implicit GEMM, group on grid z, MFMA */
-    GCONV_NUM_PATHS = 4
+    GCONV_PATH_IGEMM = 3,       /* large groups: M-tiled implicit GEMM, group on grid z, MFMA */
+    GCONV_PATH_IGHALO = 4,      /* large groups: implicit GEMM over an LDS input box per
+                                   output block, persistent, MFMA */
+    GCONV_NUM_PATHS = 5
 } gconv_path;
 
 /* Problem descriptor.  Spatial arrays are (depth, height, width); a 2D
@@ -137,11 +139,20 @@ int gconv_fwd(const gconv_desc *d, const void *x, const void *w,
 
 /* As gconv_fwd, but on a caller-chosen path (GCONV_PATH_AUTO = select).
  * Returns GCONV_ERR_PATH_UNSUPPORTED when that path cannot take d, and
- * GCONV_ERR_MISALIGNED when its vector loads need 16-byte aligned pointers
- * and one is not.  Used by the tests to run every path on shapes several can
- * take. */
+ * GCONV_ERR_MISALIGNED when it is a vector path (every path but
+ * GCONV_PATH_GENERIC) and x, w, y or bias is not 16-byte aligned; gconv_fwd
+ * itself falls back to the generic path for such pointers.  Used by the tests to run every path on shapes several can take. */
 int gconv_fwd_path(const gconv_desc *d, int path, const void *x, const void *w,
                    const void *bias, void *y, void *stream);
+
+/* As gconv_fwd_path, and binds two HIP events (hipEvent_t, either may be
+ * NULL; created by the caller, with timing enabled) to the one kernel
+ * dispatch: hipEventElapsedTime(start, stop) is then that kernel's execution
+ * time, with no marker packets between the events and the kernel.  For
+ * measurement; the result in y is the same as gconv_fwd_path's. */
+int gconv_fwd_timed(const gconv_desc *d, int path, const void *x, const void *w,
+                    const void *bias, void *y, void *stream, void *ev_start,
+                    void *ev_stop);
 
 /* Static strings; never NULL. */
 const char *gconv_status_str(int status);

@@ -163,6 +163,44 @@ def test_deterministic_and_no_overrun(name):
     assert torch.all(buf[n:] == 7.0).item(), "kernel wrote past the end of y"
 
 
+@pytest.mark.parametrize("name", ["depthwise2d_f16", "grouped3d_f16_n1"])
+def test_timed_entry_matches_and_times_the_kernel(name):
+    """gconv_fwd_timed writes the same bits as gconv_fwd_path and its events
+    span the kernel (positive, and within the stream time around it)."""
+    import ctypes
+    wl = inputs.WORKLOADS[name]
+    p = wl.problem
+    t = inputs.workload_tensors(wl)
+    x, w, b = U.device_tensors(p, t)
+    y_ref = U.run(p, x, w, b, out=poisoned_out(p))
+    y = poisoned_out(p)
+    d = G.desc_from_problem(p)
+    path = G.gconv_select_path(d)
+    hip = ctypes.CDLL(next(l.split()[-1] for l in open("/proc/self/maps") if "libamdhip64.so" in l))
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    ev = [ctypes.c_void_p(), ctypes.c_void_p()]
+    for e in ev:
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+    s = torch.cuda.current_stream()
+    outer0 = torch.cuda.Event(enable_timing=True)
+    outer1 = torch.cuda.Event(enable_timing=True)
+    outer0.record(s)
+    rc = G.gconv_fwd_timed(d, path, x.data_ptr(), w.data_ptr(), b.data_ptr() if b is not None else None,
+                           y.data_ptr(), s.cuda_stream, ev[0].value, ev[1].value)
+    outer1.record(s)
+    assert rc == G.GCONV_OK
+    torch.cuda.synchronize()
+    ms = ctypes.c_float()
+    assert hip.hipEventElapsedTime(ctypes.byref(ms), ev[0], ev[1]) == 0
+    for e in ev:
+        hip.hipEventDestroy(e)
+    assert 0.0 < ms.value <= outer0.elapsed_time(outer1) + 1e-3
+    iv = torch.int16 if p.dtype != "f32" else torch.int32
+    assert torch.equal(y.view(iv), y_ref.view(iv))
+
+
 def test_misaligned_falls_back_or_errors():
     p = reduced(inputs.WORKLOADS["depthwise2d_f16"].problem, 1)
     t = inputs.make_tensors(p, 123)
@@ -256,11 +294,17 @@ IGEMM_CASES = [
     (2, "f16", 1, 4, 96, 64, (1, 10, 10), (1, 5, 3), 1, (0, 2, 1), 1, True),  # 5x3 filter, Cpg=96
     (3, "bf16", 1, 2, 64, 128, (4, 6, 7), (3, 3, 3), 1, 1, 1, True),
     (3, "f16", 2, 2, 32, 64, (5, 5, 5), (3, 1, 3), (2, 1, 1), 1, (1, 2, 1), False),
+    (2, "bf16", 8, 2, 128, 128, (1, 14, 14), (1, 3, 3), 1, 1, 1, True),     # 16 items, XCD-split ranges
+    (2, "f16", 33, 8, 64, 64, (1, 14, 14), (1, 3, 3), 1, 1, 1, True),       # 264 items: some workgroups take 2
+    (2, "bf16", 1, 1, 64, 64, (1, 30, 29), (1, 3, 3), 1, 1, 1, True),       # row blocks, ragged last block
+    (2, "bf16", 1, 1, 64, 128, (1, 3, 300), (1, 3, 3), 1, 1, 1, False),     # column blocks (Wo > 224)
+    (2, "f16", 2, 1, 256, 256, (1, 6, 6), (1, 3, 3), 1, 1, 1, True),        # 4 channel chunks, 2 channel blocks
 ]
 
 
+@pytest.mark.parametrize("path", ["igemm_mfma", "ighalo_mfma"])
 @pytest.mark.parametrize("case", range(len(IGEMM_CASES)))
-def test_igemm_shapes(case):
+def test_igemm_shapes(case, path):
     nd, dt, N, Gr, Cpg, Kpg, sp, fl, s, pd, dl, bias = IGEMM_CASES[case]
     tr = lambda v, fill: (v if isinstance(v, tuple) else (v, v, v))
     st, pad, dil = tr(s, 1), tr(pd, 0), tr(dl, 1)
@@ -268,10 +312,15 @@ def test_igemm_shapes(case):
         st, pad, dil = (1, st[1], st[2]), (0, pad[1], pad[2]), (1, dil[1], dil[2])
     p = inputs.Problem(nd, dt, N, Gr, Gr * Cpg, Gr * Kpg, sp, fl, st, pad, dil, bias)
     d = G.desc_from_problem(p)
-    assert G.gconv_path_supported(d, G.GCONV_PATH_IGEMM) == 1, "implicit-GEMM path should take %r" % (p,)
+    pid = G.PATHS[path]
+    if path == "ighalo_mfma" and Cpg % 64 != 0:
+        # its stages are one tap x 64 input channels
+        assert G.gconv_path_supported(d, pid) == 0
+        pytest.skip("ighalo_mfma needs Cpg % 64 == 0")
+    assert G.gconv_path_supported(d, pid) == 1, "%s should take %r" % (path, p)
     t = inputs.make_tensors(p, 7000 + case)
     sa, pa, da = p.spatial_args()
     ref, scale = oracle.conv_fwd(*U.oracle_inputs(p, t), p.G, sa, pa, da)
-    y = run_and_fetch(p, t, G.GCONV_PATH_IGEMM)
-    r = U.check(y, ref, scale, p.dtype, "igemm %r" % (IGEMM_CASES[case],))
-    print("igemm case %d max err/tol %.3f plan %s" % (case, r, G.gconv_get_plan(d, G.GCONV_PATH_IGEMM)))
+    y = run_and_fetch(p, t, pid)
+    r = U.check(y, ref, scale, p.dtype, "%s %r" % (path, IGEMM_CASES[case]))
+    print("%s case %d max err/tol %.3f plan %s" % (path, case, r, G.gconv_get_plan(d, pid)))

@@ -119,8 +119,8 @@ EXPECTED_PATH = {
     "grouped2d_resnext_bf16": "smallg_mfma",
     "grouped3d_f16_n1": "smallg_mfma",
     "grouped3d_f16_n8": "smallg_mfma",
-    "grouped2d_large_bf16": "igemm_mfma",
-    "grouped2d_large_dil2_bf16": "igemm_mfma",
+    "grouped2d_large_bf16": "ighalo_mfma",
+    "grouped2d_large_dil2_bf16": "ighalo_mfma",
 }
 
 
@@ -129,7 +129,8 @@ def _built_paths():
     out = {"generic"}
     for name, pid in G.PATHS.items():
         probe = {"depthwise": "depthwise2d_f16", "smallg_mfma": "grouped2d_resnext_bf16",
-                 "igemm_mfma": "grouped2d_large_bf16", "generic": "depthwise2d_f16"}[name]
+                 "igemm_mfma": "grouped2d_large_bf16", "ighalo_mfma": "grouped2d_large_bf16",
+                 "generic": "depthwise2d_f16"}[name]
         d = G.desc_from_problem(inputs.WORKLOADS[probe].problem)
         if G.gconv_path_supported(d, pid) == 1:
             out.add(name)
@@ -186,15 +187,19 @@ def test_forced_vector_path_needs_16_byte_alignment():
         if name == "generic" or name not in _built_paths():
             continue
         probe = {"depthwise": "depthwise2d_f16", "smallg_mfma": "grouped2d_resnext_bf16",
-                 "igemm_mfma": "grouped2d_large_bf16"}[name]
+                 "igemm_mfma": "grouped2d_large_bf16", "ighalo_mfma": "grouped2d_large_bf16"}[name]
         d = G.desc_from_problem(inputs.WORKLOADS[probe].problem)
         assert G.gconv_fwd_path(d, pid, 256 + 2, 256, None, 512) == G.GCONV_ERR_MISALIGNED
+        # bias is read in 16-byte vectors too
+        assert G.gconv_fwd_path(d, pid, 256, 256, 256 + 2, 512) == G.GCONV_ERR_MISALIGNED
+        assert G.gconv_fwd_path(d, pid, 256, 256, 256 + 8, 512) == G.GCONV_ERR_MISALIGNED
 
 
 def test_forced_unsupported_path():
     # fp32 grouped problem with 3 channels per group: no MFMA path takes it
     d = G.make_desc(2, "f32", 1, 2, 6, 6, (8, 8), (3, 3), (1, 1), (1, 1), (1, 1))
-    for pid in (G.GCONV_PATH_DEPTHWISE, G.GCONV_PATH_SMALLG, G.GCONV_PATH_IGEMM):
+    for pid in (G.GCONV_PATH_DEPTHWISE, G.GCONV_PATH_SMALLG, G.GCONV_PATH_IGEMM,
+                G.GCONV_PATH_IGHALO):
         assert G.gconv_path_supported(d, pid) == 0
         assert G.gconv_fwd_path(d, pid, 256, 256, None, 512) == G.GCONV_ERR_PATH_UNSUPPORTED
 
@@ -203,4 +208,4 @@ def test_status_strings():
     for s in range(-9, 1):
         assert isinstance(G.gconv_status_str(s), str) and G.gconv_status_str(s)
     assert G.gconv_path_name(G.GCONV_PATH_AUTO) == "auto"
-    assert [G.gconv_path_name(i) for i in range(4)] == list(G.PATHS)
+    assert [G.gconv_path_name(i) for i in range(G.GCONV_NUM_PATHS)] == list(G.PATHS)
