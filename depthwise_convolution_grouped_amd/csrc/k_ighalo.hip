@@ -1,5 +1,5 @@
 // Halo-staged implicit GEMM for groups with many channels (fp16 / bf16, 2D
-// and 3D, Cpg % 64 == 0, Kpg % 64 == 0), persistent and XCD-aware.
+// and 3D, Cpg % 32 == 0, Kpg % 64 == 0), persistent and XCD-aware.
 //
 // Per group the convolution is a GEMM with M = output pixels, N = Kpg output
 // channels and K = taps * Cpg, with K decoded into (tap, channel) and the
@@ -16,29 +16,28 @@
 // only per-stage transfer is the weight slice of one (tap, chunk), which the
 // group's items share through the L2 of their XCD.
 //
-// Pipelines, both filled by direct-to-LDS buffer loads (zero fill for
+// Pipelines, all filled by direct-to-LDS buffer loads (zero fill for
 // padding from the buffer range check):
-//   - input box: two chunk buffers; the next chunk's box (the next item's
-//     first chunk at an item's end) is loaded while the current one is used;
-//   - weights: four stage buffers; stage s+3 is loaded while s is used.
+//   - input box: two chunk buffers; at a chunk's first stage the next
+//     chunk's box (the next item's first chunk at an item's last chunk) is
+//     loaded into the other buffer;
+//   - weights: four stage buffers; stage s loads stage s+3;
+//   - bias: three 1 KB blocks; an item's first stage loads the next item's.
 // One barrier per stage.  Every wave waits only for its own loads with an
 // explicit s_waitcnt vmcnt (loads return in order), then the barrier makes
-// all waves' loads visible.  The MFMA fragments of stage s+1 are read from
-// LDS while the MFMAs of stage s run, so LDS latency and bandwidth overlap
-// the matrix pipe.
+// all waves' loads visible and ends every wave's previous stage, so the
+// buffers that stage used can be refilled.
 //
 // Four waves split the item 2 (pixels) x 2 (channels).  Each computes up to
 // 7 x NTW tiles of v_mfma_f32_16x16x32 with the weights as the first operand,
-// so each lane ends with four adjacent output channels of one pixel.  The
-// epilogue of an item (bias, one rounding, 8-byte stores) runs at the start
-// of the next item's first stage, after that stage's wait, so the stores
-// overlap the next item's first MFMAs instead of delaying its loads.
+// so each lane ends with four adjacent output channels of one pixel.  An
+// item's epilogue adds the bias, rounds once and stores 8 bytes per lane.
 //
-// Grid: one workgroup per CU (the LDS reservation is above half a CU's LDS),
-// at most 256 workgroups, each looping over its items.  Items are ordered
-// group-major and each XCD (workgroup id mod 8 under the round-robin
-// dispatch) takes one contiguous eighth of them, so an XCD's L2 holds the
-// weights of about G/8 groups.
+// Grid: two workgroups per CU where the LDS fits (it does for boxes up to
+// about 20 KB per 32 channels), at most 512 workgroups, each looping over
+// its items.  Items are ordered group-major and each XCD (workgroup id mod 8
+// under the round-robin dispatch) takes one contiguous eighth of them, so an
+// XCD's L2 holds the weights of about G/8 groups.
 #include <type_traits>
 
 #include "device_common.h"
@@ -51,12 +50,12 @@ namespace {
 constexpr int kBlock = 256;
 constexpr int kWaves = 4;
 constexpr int kMaxTiles = 14;         // M tiles (16 pixels) per item
-constexpr int kMaxHaloInstr = 64;      // halo DMA instructions per chunk
+constexpr int kMaxHaloInstr = 32;      // box load instructions per chunk (boxes up to 512 pixels)
 constexpr int kHaloLPW = kMaxHaloInstr / kWaves;
-constexpr int kGrid = 256;
-constexpr int kMinLds = 82 * 1024;     // > half of 160 KB: one workgroup per CU
+constexpr int kCUs = 256;              // MI355X compute units
 constexpr int kMaxLds = 160 * 1024;
 constexpr int kBiasBytes = 3 * 1024;   // three 1 KB bias blocks
+constexpr int kColdBytes = 128;        // per-item parameters (Cold), read from LDS
 constexpr int kWBuf = 4;               // weight stage buffers
 constexpr unsigned kOob = 0x80000000u;
 
@@ -145,11 +144,13 @@ struct Item {
 };
 
 // Parameters used once per chunk or item (item decode, box origin, output
-// addressing), held in VGPRs: the scalar register file is kept for the
-// per-stage state, and these are per-lane address arithmetic anyway.
+// addressing).  The kernel keeps them in LDS and reads them where they are
+// used, so they hold neither scalar nor vector registers across the stage
+// loop (two waves share each SIMD's register file).
 struct Cold {
     int N, Do, Ho, Wo, D, H, W, C, K, Kpg, Cpg, sd, sh, sw, pd, ph, pw, RH, CW, ncb, nrb, nnb;
 };
+static_assert(sizeof(Cold) <= kColdBytes, "Cold fits its LDS slot");
 
 __device__ __forceinline__ int in_vgpr(int v)
 {
@@ -170,29 +171,35 @@ __device__ __forceinline__ Item decode(const P &q, int it)
     return r;
 }
 
-// KT: input channels per chunk (64: two MFMA K steps); NTW: 16-channel N tiles per wave
-// (the item's channel block is BN = 32 * NTW); TPW: M tiles per wave (the
-// item has at most 2 TPW).  Every wave runs all TPW tiles without branches;
-// tiles past the item's end read box pixel 0 and are not stored.
+// NTW: 16-channel N tiles per wave (the item's channel block is
+// BN = 32 * NTW); TPW: M tiles per wave (the item has at most 2 TPW).  Every
+// wave runs all TPW tiles without branches; tiles past the item's end read
+// box pixel 0 and are not stored.  A stage is one tap x KT = 32 input
+// channels: one MFMA K step.
 //
-// LDS rows (a box pixel's KT channels, or a weight row's KT channels) are
-// SPR = KT/8 slots of 16 bytes with no padding; slot j of row r holds
-// channel vector j ^ key(r).  The XOR swizzle is applied when the row is
-// loaded (direct-to-LDS loads write each lane's 16 bytes at a fixed place,
-// so the lane picks which global vector to fetch), and it keeps the 16-byte
-// fragment reads of consecutive rows in distinct banks.
-template <typename T, int KT, int NTW, int TPW>
-__global__ __launch_bounds__(kBlock, 1) void kernel(Params q, const T *__restrict__ x,
+// LDS rows (a box pixel's 32 channels, or a weight row's 32 channels) are
+// four 16-byte slots with no padding; slot j of row r holds channel vector
+// j ^ key(r), key(r) = (r >> 1) & 3.  The XOR swizzle is applied when the
+// row is loaded (direct-to-LDS loads write each lane's 16 bytes at a fixed
+// place, so the lane picks which global vector to fetch) and keeps the
+// 16-byte fragment reads of eight consecutive rows in distinct banks.
+//
+// Two workgroups share a CU (LDS and registers are sized for it), so each
+// SIMD runs two waves: while one waits for LDS, loads or the barrier, the
+// other issues MFMAs.
+template <typename T, int NTW, int TPW>
+__global__ __launch_bounds__(kBlock, 2) void kernel(Params q, const T *__restrict__ x,
                                                     const T *__restrict__ w,
                                                     const T *__restrict__ bias, T *__restrict__ y)
 {
     typedef typename Mfma<T>::V V;
+    constexpr int KT = 32;
     constexpr int SPR = KT / 8;               // 16-byte slots per staged row
-    constexpr int KS = KT / 32;               // MFMA K steps per stage
     constexpr int BN = 2 * NTW * 16;
     constexpr int B_INSTR = BN * SPR / 64;    // load instructions per weight stage
     static_assert(B_INSTR % kWaves == 0, "weight stage loads split evenly over the waves");
     constexpr int B_LPW = B_INSTR / kWaves;
+    static_assert(B_LPW <= TPW, "weight loads are interleaved one per M tile");
     constexpr int B_BYTES = BN * SPR * 16;
     extern __shared__ uint4 lds[];
 
@@ -209,8 +216,9 @@ __global__ __launch_bounds__(kBlock, 1) void kernel(Params q, const T *__restric
     const unsigned wbuf_b = lds_b + 2u * (unsigned)q.hb_bytes;           // kWBuf weight stages
     const unsigned bias_b = wbuf_b + (unsigned)(kWBuf * B_BYTES);        // 3 bias blocks of 1 KB
     const char *lds_c = reinterpret_cast<const char *>(lds);
+    const int cold_off = 2 * q.hb_bytes + kWBuf * B_BYTES + kBiasBytes;
 
-    auto key = [](int r) { return SPR == 8 ? (r & 7) : ((r >> 1) & 3); };
+    auto key = [](int r) { return (r >> 1) & 3; };
 
     // ---- this workgroup's items
     int it0, itstep, nI;
@@ -230,14 +238,16 @@ __global__ __launch_bounds__(kBlock, 1) void kernel(Params q, const T *__restric
         }
     }
     if (nI <= 0) return;
-    Cold cq;
-    cq.N = in_vgpr(q.N); cq.Do = in_vgpr(q.Do); cq.Ho = in_vgpr(q.Ho); cq.Wo = in_vgpr(q.Wo);
-    cq.D = in_vgpr(q.D); cq.H = in_vgpr(q.H); cq.W = in_vgpr(q.W); cq.C = in_vgpr(q.C);
-    cq.K = in_vgpr(q.K); cq.Kpg = in_vgpr(q.Kpg); cq.Cpg = in_vgpr(q.Cpg);
-    cq.sd = in_vgpr(q.sd); cq.sh = in_vgpr(q.sh); cq.sw = in_vgpr(q.sw);
-    cq.pd = in_vgpr(q.pd); cq.ph = in_vgpr(q.ph); cq.pw = in_vgpr(q.pw);
-    cq.RH = in_vgpr(q.RH); cq.CW = in_vgpr(q.CW);
-    cq.ncb = in_vgpr(q.ncb); cq.nrb = in_vgpr(q.nrb); cq.nnb = in_vgpr(q.nnb);
+    if (t == 0) {
+        Cold cv;
+        cv.N = q.N; cv.Do = q.Do; cv.Ho = q.Ho; cv.Wo = q.Wo; cv.D = q.D; cv.H = q.H; cv.W = q.W;
+        cv.C = q.C; cv.K = q.K; cv.Kpg = q.Kpg; cv.Cpg = q.Cpg; cv.sd = q.sd; cv.sh = q.sh; cv.sw = q.sw;
+        cv.pd = q.pd; cv.ph = q.ph; cv.pw = q.pw; cv.RH = q.RH; cv.CW = q.CW; cv.ncb = q.ncb;
+        cv.nrb = q.nrb; cv.nnb = q.nnb;
+        *reinterpret_cast<Cold *>(reinterpret_cast<char *>(lds) + cold_off) = cv;
+    }
+    __syncthreads();
+    const Cold &cq = *reinterpret_cast<const Cold *>(lds_c + cold_off);
 
     // ---- per-lane load plans (fixed for the whole kernel).  Instruction
     // k = wave + 4 i of a buffer fills its slots 64k .. 64k+63.
@@ -248,24 +258,10 @@ __global__ __launch_bounds__(kBlock, 1) void kernel(Params q, const T *__restric
         const int row = L / SPR, j = L - row * SPR;
         wofs[i] = row * q.taps * q.Cpg + (j ^ key(row)) * 8;
     }
-    int hpack[kHaloLPW];  // box: packed (bz, by, bx, vector), -1 past the box
-    int nhw = 0;
+    int nhw = 0;          // box load instructions of this wave per chunk
 #pragma unroll
-    for (int i = 0; i < kHaloLPW; ++i) {
-        const int k = wave + kWaves * i;
-        hpack[i] = -1;
-        if (k < q.HI) {
-            nhw = i + 1;
-            const int L = k * 64 + lane;
-            const int p = L / SPR, j = L - p * SPR;
-            if (p < q.BP) {
-                const int plane = q.BH * q.BW;
-                const int bz = p / plane, r = p - bz * plane;
-                const int by = r / q.BW, bx = r - by * q.BW;
-                hpack[i] = (bz << 23) | (by << 13) | (bx << 3) | (j ^ key(p));
-            }
-        }
-    }
+    for (int i = 0; i < kHaloLPW; ++i)
+        if (wave + kWaves * i < q.HI) nhw = i + 1;
 
     // ---- fragment addressing
     // A: tile tm of this wave = item tile T = mh * ta + tm; lane pixel m = 16 T + l16
@@ -273,47 +269,19 @@ __global__ __launch_bounds__(kBlock, 1) void kernel(Params q, const T *__restric
     const int my_tiles = mh == 0 ? ta : q.MT - ta;
     const int tbase = mh * ta;     // ta <= TPW
     int apos[TPW];                 // the pixel's row in the box (before the tap shift)
-    int pix_rc[TPW];               // pixel's row << 16 | column in the item, -1 = padding lane
 #pragma unroll
     for (int tm = 0; tm < TPW; ++tm) {
         const int m = (tbase + tm) * 16 + l16;
         const int lr = m / q.CW, lc = m - lr * q.CW;
         const bool live = tm < my_tiles && lr < q.RH;
-        pix_rc[tm] = live ? (lr << 16) | lc : -1;
         apos[tm] = live ? lr * q.sh * q.BW + lc * q.sw : 0;
     }
-    unsigned boff[NTW];            // B: byte offset of this lane's first K-step vector
-#pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) {
-        const int r = (nh * NTW + nt) * 16 + l16;
-        boff[nt] = (unsigned)(r * SPR + (kq ^ key(r))) * 16u;
-    }
-    // K step ks of a row is slot (kq + 4 ks) ^ key = (kq ^ key) ^ 4 ks: byte offset ^ 64 ks
-    auto read_frags = [&](V (&wf)[KS][NTW], V (&xf)[KS][TPW], int hbuf, int wbuf, int tpx) {
-        const char *wb = lds_c + 2 * q.hb_bytes + wbuf * B_BYTES;
-        const char *hb = lds_c + hbuf * q.hb_bytes;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) {
-                const uint4 raw = *reinterpret_cast<const uint4 *>(wb + (boff[nt] ^ (unsigned)(64 * ks)));
-                wf[ks][nt] = *reinterpret_cast<const V *>(&raw);
-            }
-#pragma unroll
-        for (int tm = 0; tm < TPW; ++tm) {
-            const int P = apos[tm] + tpx;
-            const unsigned a0 = (unsigned)(P * SPR + (kq ^ key(P))) * 16u;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const uint4 raw = *reinterpret_cast<const uint4 *>(hb + (a0 ^ (unsigned)(64 * ks)));
-                xf[ks][tm] = *reinterpret_cast<const V *>(&raw);
-            }
-        }
-    };
+    // B: byte offset of this lane's vector for N tile 0 of a weight stage;
+    // tile nt is 1 KB further (16 rows, and the swizzle key only sees l16)
+    const unsigned boff0 = (unsigned)(((nh * NTW) * 16 + l16) * SPR + (kq ^ key(l16))) * 16u;
 
     // ---- stage sequence: item ii (local), chunk c, tap tp; stage s, chunk
-    // h = ii * nch + c.  A stage is two K steps of 32 (KT = 64).
-    static_assert(KS == 2, "a stage is two K steps");
+    // h = ii * nch + c
     const int SPI = q.nch * q.taps;   // stages per item
     const int S = nI * SPI;
     const int nH = nI * q.nch;
@@ -330,7 +298,7 @@ __global__ __launch_bounds__(kBlock, 1) void kernel(Params q, const T *__restric
     int w_vo[B_LPW];            // this lane's offsets for the next weight stage
     unsigned w_m0 = 0;          // its buffer's LDS byte address
     auto prep_w = [&]() {
-        const int rowbase = w_row + w_tp * cq.Cpg + w_c * KT;
+        const int rowbase = w_row + w_tp * q.Cpg + w_c * KT;
 #pragma unroll
         for (int i = 0; i < B_LPW; ++i) w_vo[i] = (rowbase + wofs[i]) * (int)es;
         w_m0 = wbuf_b + (unsigned)(w_buf * B_BYTES);
@@ -356,42 +324,52 @@ __global__ __launch_bounds__(kBlock, 1) void kernel(Params q, const T *__restric
     auto issue_w1 = [&](int i) {
         dma16((unsigned)w_vo[i], __builtin_amdgcn_readfirstlane(w_m0 + (unsigned)((wave + kWaves * i) * 1024)), rw);
     };
-    int mh_next = 0;            // mark of the last box issued
-    auto issue_h = [&](int h) {
-        const int c = h % q.nch;
-        const int ii = h / q.nch;
+    int mh_last = 0;            // mark of the last box issued
+    // This lane's box vectors for channel chunk 0 of the item whose box is
+    // being loaded: element offsets into x, -1 where the vector is padding
+    // or past the box.  Set once per item (the only division work of the
+    // box loads); chunk c adds c * KT.
+    int hoff[kHaloLPW];
+    auto set_box_item = [&](int ii) {
         const Item I = decode(cq, it0 + ii * itstep);
         const int iz0 = I.od * cq.sd - cq.pd;
         const int iy0 = I.rb * cq.RH * cq.sh - cq.ph;
         const int ix0 = I.cb * cq.CW * cq.sw - cq.pw;
-        const int cbase = I.g * cq.Cpg + c * KT;
-        const unsigned base = halo_b + (unsigned)((h & 1) * q.hb_bytes);
+        const int Dv = cq.D, Hv = cq.H, Wv = cq.W, Cv = cq.C;
+        const int cg = I.g * cq.Cpg;
+        const int plane = q.BH * q.BW;
+#pragma unroll
+        for (int i = 0; i < kHaloLPW; ++i) {
+            // instruction wave + 4 i fills box slots 64 (wave + 4 i) + lane:
+            // slot L is box pixel L / 4, vector (L % 4) ^ key(pixel)
+            const int L = (wave + kWaves * i) * 64 + lane;
+            const int p = L / SPR, j = L - p * SPR;
+            const int bz = p / plane, r = p - bz * plane;
+            const int by = r / q.BW, bx = r - by * q.BW;
+            const int iz = iz0 + bz, iy = iy0 + by, ix = ix0 + bx;
+            const bool in = p < q.BP && (unsigned)iz < (unsigned)Dv && (unsigned)iy < (unsigned)Hv &&
+                            (unsigned)ix < (unsigned)Wv;
+            hoff[i] = in ? (((I.n * Dv + iz) * Hv + iy) * Wv + ix) * Cv + cg + (j ^ key(p)) * 8 : -1;
+        }
+    };
+    // box of chunk c (of the item set above) into box buffer hbuf
+    auto issue_h = [&](int c, int hbuf) {
+        const unsigned base = halo_b + (unsigned)(hbuf * q.hb_bytes);
 #pragma unroll
         for (int i = 0; i < kHaloLPW; ++i) {
             if (i < nhw) {
-                unsigned vo = kOob;
-                int pk = hpack[i];
-                // opaque to the optimiser: the unpacked fields are recomputed
-                // here, once per chunk, instead of being held live in
-                // registers across the whole stage loop
-                asm volatile("" : "+v"(pk));
-                if (pk >= 0) {
-                    const int iz = iz0 + (pk >> 23), iy = iy0 + ((pk >> 13) & 1023),
-                              ix = ix0 + ((pk >> 3) & 1023);
-                    if (iz >= 0 && iz < cq.D && iy >= 0 && iy < cq.H && ix >= 0 && ix < cq.W)
-                        vo = ((unsigned)(((I.n * cq.D + iz) * cq.H + iy) * cq.W + ix) * (unsigned)cq.C +
-                              (unsigned)(cbase + (pk & 7) * 8)) * es;
-                }
-                dma16(vo, __builtin_amdgcn_readfirstlane(base + (unsigned)((wave + kWaves * i) * 1024)), rx);
+                const int o = hoff[i];
+                dma16(o >= 0 ? (unsigned)(o + c * KT) * es : kOob,
+                      __builtin_amdgcn_readfirstlane(base + (unsigned)((wave + kWaves * i) * 1024)), rx);
             }
         }
         issued += nhw;
-        mh_next = issued;
+        mh_last = issued;
     };
     // Item ii's BN bias values go to LDS by the same direct loads (wave 0,
     // one instruction, block ii % 3), one item ahead, so no global load
     // result has to be waited for by a full vmcnt(0) drain.
-    int mb_next = 0;            // mark of the last bias block issued (wave 0)
+    int mb_last = 0;            // mark of the last bias block issued (wave 0)
     auto issue_bias = [&](int ii) {
         if (!bias || wave != 0) return;
         const Item I = decode(cq, it0 + ii * itstep);
@@ -400,7 +378,7 @@ __global__ __launch_bounds__(kBlock, 1) void kernel(Params q, const T *__restric
                                 : kOob;
         dma16(vo, __builtin_amdgcn_readfirstlane(bias_b + (unsigned)((ii % 3) * 1024)), rb);
         issued += 1;
-        mb_next = issued;
+        mb_last = issued;
     };
 
     f32x4 acc[TPW][NTW];
@@ -423,10 +401,12 @@ __global__ __launch_bounds__(kBlock, 1) void kernel(Params q, const T *__restric
             }
 #pragma unroll
             for (int tm = 0; tm < TPW; ++tm) {
-                // opaque: address arithmetic is redone per item, not held live
-                const int rc = in_vgpr(pix_rc[tm]);
-                const int oh = oh0 + (rc >> 16), ow = ow0 + (rc & 0xffff);
-                if (rc >= 0 && oh < cq.Ho && ow < cq.Wo) {
+                // the lane's pixel in the item, recomputed here per item
+                const int m = (tbase + tm) * 16 + l16;
+                const int RHv = cq.RH, CWv = cq.CW;
+                const int lr = m / CWv, lc = m - lr * CWv;
+                const int oh = oh0 + lr, ow = ow0 + lc;
+                if (tm < my_tiles && lr < RHv && oh < cq.Ho && ow < cq.Wo) {
                     T o[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) o[i] = from_f32<T>(acc[tm][nt][i] + bv[i]);
@@ -437,48 +417,16 @@ __global__ __launch_bounds__(kBlock, 1) void kernel(Params q, const T *__restric
         }
     };
 
-    // ---- fragment sets: one K step of this wave's B (NTW) and A (TPW)
-    // vectors.  Set 0 holds K step 0 of a stage, set 1 K step 1; each is read
-    // while the other one multiplies.
-    V wf0[NTW], xf0[TPW], wf1[NTW], xf1[TPW];
-    auto read_step = [&](V (&wfs)[NTW], V (&xfs)[TPW], int hbuf, int wbuf, int tpx, int ks) {
-        const char *wb = lds_c + 2 * q.hb_bytes + wbuf * B_BYTES;
-        const char *hb = lds_c + hbuf * q.hb_bytes;
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
-            const uint4 raw = *reinterpret_cast<const uint4 *>(wb + (boff[nt] ^ (unsigned)(64 * ks)));
-            wfs[nt] = *reinterpret_cast<const V *>(&raw);
-        }
-#pragma unroll
-        for (int tm = 0; tm < TPW; ++tm) {
-            const int P = apos[tm] + tpx;
-            const unsigned a0 = (unsigned)(P * SPR + (kq ^ key(P))) * 16u;
-            const uint4 raw = *reinterpret_cast<const uint4 *>(hb + (a0 ^ (unsigned)(64 * ks)));
-            xfs[tm] = *reinterpret_cast<const V *>(&raw);
-        }
-    };
-    // MFMAs of one K step; weight load i of the stage being issued (if any)
-    // goes out after tile i, so its issue hides under the matrix pipe
-    auto mfma_step = [&](V (&wfs)[NTW], V (&xfs)[TPW], bool with_w) {
-#pragma unroll
-        for (int tm = 0; tm < TPW; ++tm) {
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) acc[tm][nt] = Mfma<T>::run(wfs[nt], xfs[tm], acc[tm][nt]);
-            if (tm < B_LPW && with_w) issue_w1(tm);
-        }
-    };
-
     // ---- prologue: first item's bias, first chunk's box, weight stages
-    // 0 .. kWBuf-1; stage 0's first K step; then the loads a first stage of
-    // a chunk and of an item issue (next chunk's box, next item's bias)
+    // 0 .. kWBuf-2 (stage s issues stage s + kWBuf - 1)
     issue_bias(0);
-    const int mb0 = mb_next;
-    issue_h(0);
-    const int mh0 = mh_next;
-    int mw0 = 0, mw1 = 0, mw2 = 0;      // marks of weight stages next, next+1, next+2
-    int mw3 = 0;
+    int mb_cur = mb_last, mb_nxt = 0;   // bias of the current item, of the next
+    set_box_item(0);
+    issue_h(0, 0);
+    int mh_cur = mh_last, mh_nxt = 0;   // box of the current chunk, of the next
+    int mw0 = 0, mw1 = 0, mw2 = 0;      // weight stages s, s+1, s+2
 #pragma unroll
-    for (int i = 0; i < kWBuf; ++i) {
+    for (int i = 0; i < kWBuf - 1; ++i) {
         int m = 0;
         if (w_next < S) {
             prep_w();
@@ -489,121 +437,114 @@ __global__ __launch_bounds__(kBlock, 1) void kernel(Params q, const T *__restric
         }
         if (i == 0) mw0 = m;
         else if (i == 1) mw1 = m;
-        else if (i == 2) mw2 = m;
-        else mw3 = m;
+        else mw2 = m;
     }
-    {
-        int need = mw0 > mh0 ? mw0 : mh0;
-        if (SPI == 1 && mb0 > need) need = mb0;
-        vm_wait(issued - need);
-        __syncthreads();
-        read_step(wf0, xf0, 0, 0, 0, 0);
-    }
-    mw0 = mw1;          // from here on the marks describe stage 1 onwards
-    mw1 = mw2;
-    mw2 = mw3;
-    if (1 < nH) issue_h(1);
-    if (1 < nI) issue_bias(1);
 
-    // Cursors: current stage s (tap offset cur_tpx, box buffer cur_hb,
-    // weight buffer cur_wb) and next stage s+1 (n_*).
-    int cur_tpx = 0, cur_hb = 0, cur_wb = 0;
-    int n_ii = 0, n_c = 0, n_tp = 0, n_kx = 0, n_ky = 0, n_kz = 0, n_wb = 0;
-    // mark bookkeeping: box of the next stage's chunk and of the chunk after
-    // it, bias of the next stage's item and of the item after it
-    int mh_for_next = mh0, mb_for_next = mb0;
-    int mh_pending = 1 < nH ? mh_next : 0, mb_pending = 1 < nI ? mb_next : 0;
-    auto advance_n = [&]() {
-        if (++n_wb == kWBuf) n_wb = 0;
-        if (++n_kx == q.X) {
-            n_kx = 0;
-            if (++n_ky == q.Y) {
-                n_ky = 0;
-                ++n_kz;
-            }
-        }
-        if (++n_tp == q.taps) {
-            n_tp = 0;
-            n_kx = n_ky = n_kz = 0;
-            mh_for_next = mh_pending;
-            mh_pending = 0;
-            if (++n_c == q.nch) {
-                n_c = 0;
-                ++n_ii;
-                mb_for_next = mb_pending;
-                mb_pending = 0;
-            }
-        }
-    };
-    advance_n();   // next = stage 1
-
-    int s = 0;
+    int s = 0, kx = 0, ky = 0, kz = 0, wb = 0;
     for (int ii = 0; ii < nI; ++ii) {
 #pragma unroll
         for (int a = 0; a < TPW; ++a)
 #pragma unroll
             for (int b = 0; b < NTW; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int j = 0; j < SPI; ++j, ++s) {
-            // step A: K step 1 of stage s into set 1; MFMAs of K step 0
-            read_step(wf1, xf1, cur_hb, cur_wb, cur_tpx, 1);
-            mfma_step(wf0, xf0, false);
-
-            // step B: stage s+1 becomes readable; its first K step into set 0;
-            // MFMAs of K step 1 with the weight loads that run ahead
-            bool more_w = false;
-            const bool have_next = s + 1 < S;
-            const bool next_ends_item = n_tp == q.taps - 1 && n_c == q.nch - 1;
-            {
-                // stage s+1's weights and box, and, if it ends its item, the
-                // item's bias: this wave's loads are in when no more than the
-                // loads issued after the latest of them remain.  The fragment
-                // reads of stage s are complete too (lgkmcnt(0)), so after the
-                // barrier every buffer stage s used is free.
-                int need = 0;
-                if (have_next) {
-                    need = mw0 > mh_for_next ? mw0 : mh_for_next;
-                    if (next_ends_item && mb_for_next > need) need = mb_for_next;
+        for (int c = 0; c < q.nch; ++c) {
+            const int h = ii * q.nch + c;
+            for (int tp = 0; tp < q.taps; ++tp, ++s) {
+                const bool last = tp == q.taps - 1 && c == q.nch - 1;
+                // This wave's loads of stage s's weights and box (and, in an
+                // item's last stage, of its bias) are in when no more than
+                // the loads issued after the latest of them remain; the
+                // barrier publishes every wave's loads.  It also ends every
+                // wave's MFMAs of stage s-1, whose fragments were read before
+                // them: the buffers stage s-1 used are free below.
+                {
+                    int need = mw0 > mh_cur ? mw0 : mh_cur;
+                    if (last && mb_cur > need) need = mb_cur;
+                    // Waiting until at most 2 B_LPW loads are outstanding is
+                    // exact when only the next two weight stages were issued
+                    // after the loads needed here, and stricter (waits for
+                    // some younger box or bias loads too, which are cheap by
+                    // then) when more were: one compare instead of the branch
+                    // tree that picks the counter immediate.  Only the last
+                    // stages, with fewer younger loads, take the tree.
+                    const int n = issued - need;
+                    if (n >= 2 * B_LPW)
+                        __builtin_amdgcn_s_waitcnt(((2 * B_LPW) & 15) | (7 << 4) | (15 << 8) |
+                                                   (((2 * B_LPW) >> 4) << 14));
+                    else
+                        vm_wait(n);
+                    __syncthreads();
                 }
-                __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
-                vm_wait(issued - need);
-                __syncthreads();
-            }
-            if (have_next) {
-                // loads that run ahead: at the first stage of a chunk the
-                // chunk after it; at an item's first stage the next item's
-                // bias; weight stage s+1+kWBuf-1 into the buffer of stage s
-                const int nh_ = n_ii * q.nch + n_c;
-                if (n_tp == 0 && nh_ + 1 < nH) {
-                    issue_h(nh_ + 1);
-                    mh_pending = mh_next;
+                // loads that run ahead: at a chunk's first stage the next
+                // chunk's box (into the buffer of chunk h-1), at an item's
+                // first stage the next item's bias, and weight stage
+                // s + kWBuf - 1 (into the buffer of stage s-1, between MFMAs)
+                if (tp == 0 && h + 1 < nH) {
+                    if (c + 1 < q.nch) {
+                        issue_h(c + 1, (h + 1) & 1);
+                    } else {
+                        set_box_item(ii + 1);
+                        issue_h(0, (h + 1) & 1);
+                    }
+                    mh_nxt = mh_last;
                 }
-                if (n_tp == 0 && n_c == 0 && n_ii + 1 < nI) {
-                    issue_bias(n_ii + 1);
-                    mb_pending = mb_next;
+                if (tp == 0 && c == 0 && ii + 1 < nI) {
+                    issue_bias(ii + 1);
+                    mb_nxt = mb_last;
                 }
-                more_w = w_next < S;
+                const bool more_w = w_next < S;
                 if (more_w) prep_w();
-                const int n_tpx = (n_kz * q.dd * q.BH + n_ky * q.dh) * q.BW + n_kx * q.dw;
-                read_step(wf0, xf0, nh_ & 1, n_wb, n_tpx, 0);
-                cur_tpx = n_tpx;
-                cur_hb = nh_ & 1;
-                cur_wb = n_wb;
+
+                // fragments of stage s
+                const int tpx = (kz * q.dd * q.BH + ky * q.dh) * q.BW + kx * q.dw;
+                const char *wbp = lds_c + 2 * q.hb_bytes + wb * B_BYTES;
+                const char *hbp = lds_c + (h & 1) * q.hb_bytes;
+                V wf[NTW], xf[TPW];
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) {
+                    const uint4 raw = *reinterpret_cast<const uint4 *>(wbp + boff0 + nt * 1024);
+                    wf[nt] = *reinterpret_cast<const V *>(&raw);
+                }
+#pragma unroll
+                for (int tm = 0; tm < TPW; ++tm) {
+                    const int P = apos[tm] + tpx;
+                    const uint4 raw = *reinterpret_cast<const uint4 *>(
+                        hbp + (unsigned)(P * SPR + (kq ^ key(P))) * 16u);
+                    xf[tm] = *reinterpret_cast<const V *>(&raw);
+                }
+                // MFMAs; weight load i goes out after tile i so its issue
+                // hides under the matrix pipe
+#pragma unroll
+                for (int tm = 0; tm < TPW; ++tm) {
+#pragma unroll
+                    for (int nt = 0; nt < NTW; ++nt) acc[tm][nt] = Mfma<T>::run(wf[nt], xf[tm], acc[tm][nt]);
+                    if (tm < B_LPW && more_w) issue_w1(tm);
+                }
+                if (more_w) finish_w();
+                mw0 = mw1;
+                mw1 = mw2;
+                mw2 = more_w ? w_last : 0;
+
+                if (++wb == kWBuf) wb = 0;
+                if (++kx == q.X) {
+                    kx = 0;
+                    if (++ky == q.Y) {
+                        ky = 0;
+                        ++kz;
+                    }
+                }
             }
-            mfma_step(wf1, xf1, more_w);
-            if (more_w) finish_w();
-            mw0 = mw1;
-            mw1 = mw2;
-            mw2 = more_w ? w_last : 0;
-            advance_n();
+            kx = ky = kz = 0;
+            mh_cur = mh_nxt;
         }
         finish_item(ii);
+        mb_cur = mb_nxt;
     }
 }
 
 // ----------------------------------------------------------------- host side
 
 struct Config {
-    int KT, NTW, TPW;
+    int NTW, TPW;
     int RH, CW, nrb, ncb, nnb;
     int BD, BH, BW, BP, HI, MT;
     int items, nch, taps, grid, xcd_split;
@@ -613,25 +554,24 @@ struct Config {
 bool configure(const Problem &p, Config &c)
 {
     if (p.dtype != GCONV_F16 && p.dtype != GCONV_BF16) return false;
-    // a stage is one tap x 64 input channels (two MFMA K steps)
-    if (p.Cpg % 64 != 0 || p.Kpg % 64 != 0) return false;
+    // a stage is one tap x 32 input channels; a channel block is 64 or 128
+    if (p.Cpg % 32 != 0 || p.Kpg % 64 != 0) return false;
     const long long xb = (long long)p.N * p.D * p.H * p.W * p.C() * 2;
     const long long wb = (long long)p.K() * p.taps() * p.Cpg * 2;
     if (xb >= (1LL << 31) || wb >= (1LL << 31)) return false;
-    c.KT = 64;
+    constexpr int KT = 32, SPR = KT / 8;
     c.NTW = p.Kpg % 128 == 0 ? 4 : 2;
     const int BN = 32 * c.NTW;
-    const int SPR = c.KT / 8;
     const int b_bytes = BN * SPR * 16;
     c.nnb = p.Kpg / BN;
-    c.nch = p.Cpg / c.KT;
+    c.nch = p.Cpg / KT;
     c.taps = p.taps();
     c.BD = (p.Z - 1) * p.dd + 1;
     if (c.BD > 255) return false;
     // Pick the item shape (RH rows x CW columns of output) that minimises the
-    // MFMA time: rounds of items over the grid x tiles per wave, then the
-    // input box overhead; the box must fit two box buffers next to the
-    // weight stage buffers.
+    // MFMA time: rounds of items over the workgroup slots (two per CU when
+    // the LDS fits half a CU, else one) x tiles per wave, then the input box
+    // overhead; the box must fit two box buffers next to the weight stages.
     bool found = false;
     double best = 0.0;
     for (int CW = p.Wo < kMaxTiles * 16 ? p.Wo : kMaxTiles * 16; CW >= 1; --CW) {
@@ -648,15 +588,19 @@ bool configure(const Problem &p, Config &c)
             const long long HI = (BP * SPR + 63) / 64;
             if (HI > kMaxHaloInstr) continue;
             const long long hb = HI * 1024;
-            if (2 * hb + kWBuf * b_bytes + kBiasBytes > kMaxLds) continue;
+            const long long lds = 2 * hb + kWBuf * b_bytes + kBiasBytes + kColdBytes;
+            if (lds > kMaxLds) continue;
+            const int per_cu = lds <= kMaxLds / 2 ? 2 : 1;
+            const long long slots = (long long)kCUs * per_cu;
             const long long nrb = (p.Ho + RH - 1) / RH, ncb = (p.Wo + CW - 1) / CW;
             const long long items = (long long)p.G * c.nnb * p.N * p.Do * nrb * ncb;
             if (items >= (1LL << 30)) continue;
-            const long long grid = items < kGrid ? items : kGrid;
+            const long long grid = items < slots ? items : slots;
             const long long rounds = (items + grid - 1) / grid;
             const int tpw = (MT + 1) / 2 <= 4 ? 4 : 7;
-            const double t_mfma = (double)rounds * tpw * 16.0;   // per-wave pixel rows
-            const double useful = (double)p.N * p.Do * p.Ho * p.Wo * p.G * c.nnb / grid;
+            // per-SIMD MFMA work: rounds x waves per SIMD x tiles per wave
+            const double t_mfma = (double)rounds * per_cu * tpw;
+            const double useful = (double)p.N * p.Do * p.Ho * p.Wo * p.G * c.nnb / (double)kCUs;
             const double box_over = (double)BP / (M * (double)p.sh * p.sw);
             const double score = useful / t_mfma / (0.9 + 0.1 * box_over);
             if (!found || score > best) {
@@ -665,18 +609,17 @@ bool configure(const Problem &p, Config &c)
                 c.RH = RH; c.CW = CW; c.nrb = (int)nrb; c.ncb = (int)ncb; c.TPW = tpw;
                 c.BH = BH; c.BW = BW; c.BP = (int)BP; c.HI = (int)HI; c.MT = MT;
                 c.items = (int)items; c.grid = (int)grid; c.hb_bytes = (int)hb;
+                c.lds = (int)lds;
             }
         }
     }
     if (!found) return false;
     c.xcd_split = c.grid % 8 == 0 ? 1 : 0;
-    c.lds = 2 * c.hb_bytes + kWBuf * b_bytes + kBiasBytes;
-    if (c.lds < kMinLds) c.lds = kMinLds;
     return true;
 }
 
-template <typename T, int KT, int NTW, int TPW>
-hipError_t go4(const Problem &p, const Config &c, const Args &a, hipStream_t s)
+template <typename T, int NTW, int TPW>
+hipError_t go3(const Problem &p, const Config &c, const Args &a, hipStream_t s)
 {
     Params q;
     q.N = p.N; q.G = p.G; q.Cpg = p.Cpg; q.Kpg = p.Kpg; q.C = p.C(); q.K = p.K();
@@ -690,7 +633,7 @@ hipError_t go4(const Problem &p, const Config &c, const Args &a, hipStream_t s)
     q.hb_bytes = c.hb_bytes;
     q.x_bytes = (unsigned)((long long)p.N * p.D * p.H * p.W * p.C() * 2);
     q.w_bytes = (unsigned)((long long)p.K() * p.taps() * p.Cpg * 2);
-    auto k = kernel<T, KT, NTW, TPW>;
+    auto k = kernel<T, NTW, TPW>;
     static bool lds_set = false;
     if (!lds_set) {
         (void)hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
@@ -700,16 +643,11 @@ hipError_t go4(const Problem &p, const Config &c, const Args &a, hipStream_t s)
                    (const T *)a.bias, (T *)a.y);
 }
 
-template <typename T, int KT, int NTW>
-hipError_t go3(const Problem &p, const Config &c, const Args &a, hipStream_t s)
-{
-    return c.TPW == 7 ? go4<T, KT, NTW, 7>(p, c, a, s) : go4<T, KT, NTW, 4>(p, c, a, s);
-}
-
 template <typename T>
 hipError_t go(const Problem &p, const Config &c, const Args &a, hipStream_t s)
 {
-    return c.NTW == 4 ? go3<T, 64, 4>(p, c, a, s) : go3<T, 64, 2>(p, c, a, s);
+    if (c.NTW == 4) return c.TPW == 7 ? go3<T, 4, 7>(p, c, a, s) : go3<T, 4, 4>(p, c, a, s);
+    return c.TPW == 7 ? go3<T, 2, 7>(p, c, a, s) : go3<T, 2, 4>(p, c, a, s);
 }
 
 }  // namespace

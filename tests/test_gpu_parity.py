@@ -313,10 +313,6 @@ def test_igemm_shapes(case, path):
     p = inputs.Problem(nd, dt, N, Gr, Gr * Cpg, Gr * Kpg, sp, fl, st, pad, dil, bias)
     d = G.desc_from_problem(p)
     pid = G.PATHS[path]
-    if path == "ighalo_mfma" and Cpg % 64 != 0:
-        # its stages are one tap x 64 input channels
-        assert G.gconv_path_supported(d, pid) == 0
-        pytest.skip("ighalo_mfma needs Cpg % 64 == 0")
     assert G.gconv_path_supported(d, pid) == 1, "%s should take %r" % (path, p)
     t = inputs.make_tensors(p, 7000 + case)
     sa, pa, da = p.spatial_args()
