@@ -1,36 +1,42 @@
-// Depthwise direct convolution (Cpg = Kpg = 1, 2D): input rows streamed into an
-// LDS ring by direct-to-LDS buffer loads, 16-byte channel vectors, fp32 FMA on
-// the VALU, fused bias/convert epilogue.
+// Depthwise direct convolution (Cpg = Kpg = 1, 2D, 3x3 window): every wave
+// streams its own input rows straight into registers, with 16-byte channel
+// vectors, fp32 accumulation on the VALU and a fused bias/convert epilogue.
 //
 // Depthwise conv is the G == C case of the grouped forward conv (TileOPs PR
 // 1568 review, summary: MobileNetV2 depthwise benchmark cases).  With one
 // input and one output channel per group there is no contraction for the
 // matrix cores; the work is bound by HBM traffic (about 4.5 FLOP per byte for
-// 3x3 fp16), so the kernel is built to read x and write y once each with long
-// coalesced vector accesses and to keep many bytes in flight.
+// 3x3 fp16), so the kernel is built like a copy: each byte of x and y crosses
+// HBM once, every access is a long coalesced 16-byte-per-lane buffer access,
+// and nothing makes waves wait for one another (no LDS, no barriers).
 //
-// Work decomposition.  A workgroup (4 waves) owns one image n, a strip of TW
-// output columns, a slab of CV channel vectors (VEC channels, 16 bytes each)
-// and a chunk of output rows.  Thread t computes channel vector t % CV of
-// output column t / CV.  In NHWC a row segment of the strip is IW * CV
-// vectors; when the slab spans all channels it is one contiguous run.
+// Work decomposition.  An output row of one image, flattened NHWC style, is
+// Wo * Cv channel vectors (Cv = C / VEC, VEC channels per 16 bytes).  A wave
+// owns 64 consecutive ones of them (lane -> output column ow and channel
+// vector cv) over R consecutive output rows; a workgroup is four such waves
+// side by side.  The wave walks the (R - 1) * SH + 2 * DH + 1 input rows that
+// the R output rows need, in order.  Each input row costs three 16-byte loads
+// per lane (the three window columns; a neighbour's loads of the same bytes
+// hit in the caches) and is folded into every output row whose window covers
+// it (input stationary), so an output row is written as soon as its last
+// input row has been folded in.  The whole walk is unrolled into one basic
+// block of straight-line code: the compiler is free to issue loads for rows
+// far ahead of the arithmetic, which is what hides the HBM latency.
 //
-// Input rows live in an LDS ring of NR rows (ring row rr = ih + pad_h ->
-// slot rr % NR).  Each row is fetched with buffer_load_dwordx4 ... lds: one
-// instruction moves 64 consecutive 16-byte vectors (lane l -> LDS + 16 l)
-// without passing through registers; offsets outside the image (padding,
-// slab tail) are out of the buffer range and land as zeros.  Output rows are
-// produced in bands of RB rows; a band needs IR = (RB-1)*SH + (Y-1)*DH + 1
-// input rows and brings NEW = RB*SH new ones.  The loads of the next DEPTH
-// bands are always in flight.  With NR = IR + (DEPTH+1)*NEW, the band issued
-// at the top of iteration b lands in slots last read in iteration b-1, so one
-// barrier per band orders every reuse of a slot.
+// Zero padding and ragged edges cost no branches: a column outside the image
+// (or a lane past the row) gets a buffer offset beyond the buffer's range, so
+// its loads return zeros and its stores are dropped by the hardware; a row
+// outside the image gets the same treatment for all lanes.
 //
-// The compiler does not see these loads (inline asm), so it inserts no
-// conservative wait before the LDS reads; each wave waits with s_waitcnt
-// vmcnt for its own loads of the band it is about to read (loads return in
-// order, and only loads issued after that band are allowed to stay
-// outstanding), then the barrier makes every wave's rows visible.
+// fp16: no element is ever converted.  The taps of window columns 0 and 1
+// go through v_dot2_f32_f16 (two fp16 products summed into an fp32
+// accumulator) on (x[dx=0], x[dx=1]) pairs built once per input row with one
+// byte permute per channel, and column 2 through v_fma_mix_f32, which reads
+// both fp16 factors in place (either half of a register) and accumulates in
+// fp32.  Both run at the same rate, so 9 taps cost 6 instructions.  bf16 and
+// fp32 convert the input once per load and keep the weights in fp32.
+#include <utility>
+
 #include "device_common.h"
 #include "gconv_internal.h"
 
@@ -40,291 +46,249 @@ namespace {
 
 constexpr int kBlock = 256;
 constexpr int kWaves = kBlock / 64;
-constexpr int kLds = 160 * 1024;      // LDS per CU on gfx950
-constexpr int kMaxLw = 12;            // ring-load instructions per wave per band
-constexpr unsigned kOob = 0x80000000u; // buffer offset past any image: reads zero
+constexpr int kTargetWaves = 1024;      // one wave per SIMD
+constexpr unsigned kOob = 0x80000000u;   // buffer offset past any image: loads zero, stores dropped
+constexpr int kRawBuffer = 0x00020000;   // buffer descriptor word 3: raw 32-bit dwords
+// Cache policy of the accesses (buffer instruction bits: 1 sc0, 2 nt,
+// 16 sc1).  y is written once and never read back, so its stores are
+// non-temporal, which lets the memory system stream them (measured: about
+// 10% faster for this kernel).  x stays on the default policy: its halo rows
+// and the neighbouring window columns are re-read from L1/L2, and
+// non-temporal loads lose those hits.
+constexpr int kLoadPolicy = 0;
+constexpr int kStorePolicy = 2;
 
 struct Params {
-    int N, C, Cv;          // images, channels, channel vectors
+    int C, Cv;             // channels, channel vectors per pixel
     int H, W, Ho, Wo;
     int sw, dw, ph, pw;
-    int CV, TW, IW, P, NCH;// slab vectors, strip width out/in, vectors per row, 64-vector chunks per row
-    int RH;                // output rows per workgroup (multiple of RB)
-    int ncol, nslab, nchunk;
-    int DEPTH, NR;         // bands in flight, ring rows
-    unsigned img_bytes;    // bytes of one image of x
-    unsigned w_bytes, b_bytes;  // bytes of w and of bias (0: no bias)
+    int nseg;              // 64-vector segments per output row
+    int nsb, nchunk;       // segment blocks (4 segments) per row, row chunks per image
+    unsigned in_row, out_row;       // bytes of one row of x / of y
+    unsigned img_bytes, oimg_bytes; // bytes of one image of x / of y
+    unsigned w_bytes, b_bytes;      // bytes of w and of bias (0: no bias)
 };
 
-template <typename T> struct VecOf;
-template <> struct VecOf<float> { static constexpr int n = 4; };
-template <> struct VecOf<_Float16> { static constexpr int n = 8; };
-template <> struct VecOf<__bf16> { static constexpr int n = 8; };
+template <typename T> struct VecOf { static constexpr int n = 16 / (int)sizeof(T); };
 
-typedef int rsrc_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void *base, unsigned bytes)
+// f(integral_constant<int, I>) for I = 0, 1, ..., in order
+template <int... Is, class F>
+__device__ __forceinline__ void static_for(std::integer_sequence<int, Is...>, F &&f)
 {
-    const unsigned long long a = (unsigned long long)base;
-    rsrc_t r;
-    r.x = (int)(unsigned)(a & 0xffffffffull);
-    r.y = (int)(unsigned)((a >> 32) & 0xffffull);   // stride 0
-    r.z = (int)bytes;                                // num_records (bytes)
-    r.w = 0x00020000;                                // raw 32-bit dword format
-    return r;
+    (f(std::integral_constant<int, Is>{}), ...);
 }
 
-// One direct-to-LDS 16-byte load per active lane: lane l writes LDS[m0 + 16 l].
-__device__ __forceinline__ void dma16(unsigned voffset, unsigned lds_byte, rsrc_t r)
+typedef unsigned u4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+// acc += a.lo * b.lo + a.hi * b.hi (fp16 pairs, fp32 accumulation)
+__device__ __forceinline__ float dot2(unsigned a, unsigned b, float acc)
 {
-    asm volatile("s_mov_b32 m0, %1\n\t"
-                 "s_nop 0\n\t"
-                 "buffer_load_dwordx4 %0, %2, 0 offen lds"
-                 :
-                 : "v"(voffset), "s"(lds_byte), "s"(r)
-                 : "memory", "m0");
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, a), __builtin_bit_cast(h2, b), acc, false);
+}
+// (half S0 of r0, half S1 of r1) as one fp16 pair
+template <int S0, int S1> __device__ __forceinline__ unsigned pair_halves(unsigned r0, unsigned r1)
+{
+    constexpr unsigned sel = (2u * S0) | ((2u * S0 + 1u) << 8) | ((4u + 2u * S1) << 16) | ((5u + 2u * S1) << 24);
+    return __builtin_amdgcn_perm(r1, r0, sel);
 }
 
-// s_waitcnt vmcnt(n) for a wave-uniform n (other counters not waited on).
-__device__ __forceinline__ void vm_wait(int n)
+// acc + x.half(XS) * w.half(WS), both fp16, accumulated in fp32: written as
+// a plain fma of widened halves, which the compiler emits as one
+// v_fma_mix_f32 (op_sel picks the halves), and being ordinary code it is
+// covered by the compiler's hazard checks.
+template <int XS, int WS>
+__device__ __forceinline__ float fma_mix(unsigned xr, unsigned wr, float acc)
 {
-#define GCONV_VMW(k) \
-    case k: __builtin_amdgcn_s_waitcnt(((k) & 15) | (7 << 4) | (15 << 8) | (((k) >> 4) << 14)); break;
-    switch (__builtin_amdgcn_readfirstlane(n)) {
-        GCONV_VMW(1) GCONV_VMW(2) GCONV_VMW(3) GCONV_VMW(4) GCONV_VMW(5) GCONV_VMW(6)
-        GCONV_VMW(7) GCONV_VMW(8) GCONV_VMW(9) GCONV_VMW(10) GCONV_VMW(11) GCONV_VMW(12)
-        GCONV_VMW(13) GCONV_VMW(14) GCONV_VMW(15) GCONV_VMW(16) GCONV_VMW(17) GCONV_VMW(18)
-        GCONV_VMW(19) GCONV_VMW(20) GCONV_VMW(21) GCONV_VMW(22) GCONV_VMW(23) GCONV_VMW(24)
-        GCONV_VMW(25) GCONV_VMW(26) GCONV_VMW(27) GCONV_VMW(28) GCONV_VMW(29) GCONV_VMW(30)
-        GCONV_VMW(31) GCONV_VMW(32) GCONV_VMW(33) GCONV_VMW(34) GCONV_VMW(35) GCONV_VMW(36)
-    default: __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); break;   // vmcnt(0)
-    }
-#undef GCONV_VMW
+    const h2 xh = __builtin_bit_cast(h2, xr), wh = __builtin_bit_cast(h2, wr);
+    return __builtin_fmaf((float)xh[XS], (float)wh[WS], acc);
 }
 
-template <typename T, int SH, int DH>
-struct Shape {
-    static constexpr int Y = 3, X = 3;
-    static constexpr int RB = 2;                          // output rows per band
-    static constexpr int IR = (RB - 1) * SH + (Y - 1) * DH + 1;
-    static constexpr int NEW = RB * SH;
-};
+// Element e of a 16-byte vector as fp32 (bf16 / fp32 inputs).
+template <typename T> __device__ __forceinline__ float elem_f32(const u4 &v, int e);
+template <> __device__ __forceinline__ float elem_f32<float>(const u4 &v, int e)
+{
+    const unsigned r = v[e];   // (bit-casting the element expression itself reads element 0)
+    return __builtin_bit_cast(float, r);
+}
+template <> __device__ __forceinline__ float elem_f32<__bf16>(const u4 &v, int e)
+{
+    const unsigned r = v[e >> 1];
+    return __builtin_bit_cast(float, (e & 1) ? (r & 0xffff0000u) : (r << 16));
+}
 
-template <typename T, int SH, int DH>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, unsigned bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRawBuffer);
+}
+
+template <typename T, int SH, int DH, int R, int PF>
 __global__ __launch_bounds__(kBlock) void kernel(Params q, const T *__restrict__ x,
                                                  const T *__restrict__ w,
                                                  const T *__restrict__ bias, T *__restrict__ y)
 {
-    using S = Shape<T, SH, DH>;
-    constexpr int VEC = VecOf<T>::n, Y = S::Y, X = S::X, RB = S::RB, IR = S::IR, NEW = S::NEW;
-    typedef T vecT __attribute__((ext_vector_type(VEC)));
-    extern __shared__ uint4 ring[];
+    constexpr int VEC = VecOf<T>::n;
+    constexpr int NI = (R - 1) * SH + 2 * DH + 1;      // input rows of R output rows
+    constexpr bool kF16 = __is_same(T, _Float16);
 
-    // ---- tile (XCD-aware order, column strips fastest)
-    const int nblocks = q.ncol * q.nslab * q.nchunk * q.N;
-    int tile = xcd_tile((int)blockIdx.x, nblocks);
-    const int col = tile % q.ncol;   tile /= q.ncol;
-    const int slab = tile % q.nslab; tile /= q.nslab;
+    // ---- tile: (image, row chunk, block of 4 segments); neighbours in the
+    //      tile order share halo rows and columns, so keep them on one XCD
+    int tile = xcd_tile((int)blockIdx.x, (int)gridDim.x);
+    const int sb = tile % q.nsb;   tile /= q.nsb;
     const int chunk = tile % q.nchunk;
     const int n = tile / q.nchunk;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int lane = (int)threadIdx.x & 63;
+    const int seg = sb * kWaves + wave;
+    if (seg >= q.nseg) return;     // whole wave idle (last block of a row)
 
-    const int t = threadIdx.x;
-    const int wave = t >> 6, lane = t & 63;
-    const int ow0 = col * q.TW;
-    const int cv0 = slab * q.CV;
-    const int oh_begin = chunk * q.RH;
-    const int oh_end = min(oh_begin + q.RH, q.Ho);
-    const int nbands = (oh_end - oh_begin + RB - 1) / RB;
-    const int iw0 = ow0 * q.sw - q.pw;
-    const unsigned ring_lds = (unsigned)(size_t)ring;
-    const unsigned row_bytes = (unsigned)q.P * 16u;
-    const rsrc_t rs = make_rsrc(x + (size_t)n * q.H * q.W * q.C, q.img_bytes);
+    const int j = seg * 64 + lane;
+    const bool jok = j < q.Wo * q.Cv;
+    const int ow = j / q.Cv, cv = j - (j / q.Cv) * q.Cv;
     const unsigned es = (unsigned)sizeof(T);
-
-    // Column part of the buffer offset of vector j of a ring row, or kOob.
-    auto col_voff = [&](int j) -> unsigned {
-        const int px = j / q.CV, cvl = j - (j / q.CV) * q.CV;
-        const int iw = iw0 + px, cv = cv0 + cvl;
-        if (iw < 0 || iw >= q.W || cv >= q.Cv) return kOob;
-        return ((unsigned)iw * (unsigned)q.C + (unsigned)cv * VEC) * es;
-    };
-    auto row_voff = [&](int rr) -> int {   // ring row -> image row offset, or -1 outside
-        const int ih = rr - q.ph;
-        return (ih >= 0 && ih < q.H) ? ih * q.W * q.C * (int)es : -1;
-    };
-
-    // ---- this thread's output column / channel vector
-    const int cvl = t % q.CV;
-    const int owl = t / q.CV;
-    const int ow = ow0 + owl;
-    const int cv = cv0 + cvl;
-    const bool active = owl < q.TW && ow < q.Wo && cv < q.Cv;
-
-    // ---- prologue.  First the slab's weights and bias (the VEC channels of
-    // one vector own Y*X*VEC consecutive weights, [c][y][x] with G = C and
-    // Kpg = Cpg = 1, i.e. Y*X whole vectors; the slab's are contiguous), then
-    // the first band's IR rows.  All of it travels by the same direct-to-LDS
-    // loads, so nothing waits before the ring starts.
-    constexpr int WV = Y * X * VEC * (int)sizeof(T) / 16;   // weight vectors per channel vector
-    static_assert(Y * X * VEC * sizeof(T) % 16 == 0, "weight block must be whole vectors");
-    const unsigned wlds = ring_lds + (unsigned)q.NR * row_bytes;   // CV * WV vectors
-    const unsigned blds = wlds + (unsigned)(q.CV * WV) * 16u;      // CV vectors
-    {
-        const rsrc_t rw = make_rsrc(w + (size_t)cv0 * VEC * Y * X, q.w_bytes - (unsigned)cv0 * WV * 16u);
-        const int nwv = q.CV * WV, nwc = (nwv + 63) / 64;
-        for (int c = wave; c < nwc; c += kWaves)
-            if (c * 64 + lane < nwv)
-                dma16((unsigned)(c * 64 + lane) * 16u, __builtin_amdgcn_readfirstlane(wlds + (unsigned)c * 1024u), rw);
-        if (q.b_bytes && wave == kWaves - 1) {
-            const rsrc_t rb = make_rsrc(bias + (size_t)cv0 * VEC, q.b_bytes - (unsigned)cv0 * 16u);
-            for (int c = 0; c * 64 < q.CV; ++c)
-                if (c * 64 + lane < q.CV)
-                    dma16((unsigned)(c * 64 + lane) * 16u, __builtin_amdgcn_readfirstlane(blds + (unsigned)c * 1024u), rb);
-        }
+    unsigned coff[3];              // byte offset of the lane's vector in an input row, per window column
+#pragma unroll
+    for (int dx = 0; dx < 3; ++dx) {
+        const int iw = ow * q.sw - q.pw + dx * q.dw;
+        coff[dx] = (jok && iw >= 0 && iw < q.W) ? ((unsigned)iw * (unsigned)q.C + (unsigned)cv * VEC) * es : kOob;
     }
-    const int rr_first = oh_begin * SH;
-    {
-        const int total = IR * q.NCH;
-        for (int k = wave; k < total; k += kWaves) {
-            const int r = k / q.NCH, c = k - (k / q.NCH) * q.NCH;
-            const int j = c * 64 + lane;
-            if (j < q.P) {
-                const int ro = row_voff(rr_first + r);
-                const unsigned cvo = col_voff(j);
-                const unsigned vo = (ro < 0 || cvo == kOob) ? kOob : (unsigned)ro + cvo;
-                const unsigned m0 = ring_lds + (unsigned)((rr_first + r) % q.NR) * row_bytes + (unsigned)c * 1024u;
-                dma16(vo, __builtin_amdgcn_readfirstlane(m0), rs);
-            }
-        }
-    }
-    // Deeper bands are requested only once band 0 has landed: band 0 of every
-    // workgroup then reaches the front of the memory queues first.
+    const unsigned ooff = jok ? ((unsigned)ow * (unsigned)q.C + (unsigned)cv * VEC) * es : kOob;
 
-    // (computed while the prologue loads are in flight)
-    // ---- per-thread plan of one band's loads: instruction k = wave + 4 i
-    //      covers row k / NCH of the band and 64-vector chunk k % NCH.
-    const int band_instr = NEW * q.NCH;
-    int lw = 0;                                  // this wave's instructions per band
-    unsigned plan_col[kMaxLw];                   // column offset (or kOob) of this lane
-    int plan_row[kMaxLw], plan_chunk[kMaxLw];
-    bool plan_lane[kMaxLw];                      // lane has a vector in that chunk
+    const auto rx = rsrc(x + (size_t)n * q.H * q.W * q.C, q.img_bytes);
+    const auto ry = rsrc(y + (size_t)n * q.Ho * q.Wo * q.C, q.oimg_bytes);
+
+    // ---- weights of the lane's VEC channels: [c][y][x], 9 * VEC consecutive
+    //      elements = 9 vectors; bias: one vector (zeros without bias)
+    const auto rw = rsrc(w, q.w_bytes);
+    u4 wraw[9];
 #pragma unroll
-    for (int i = 0; i < kMaxLw; ++i) {
-        const int k = wave + kWaves * i;
-        plan_row[i] = 0; plan_chunk[i] = 0; plan_col[i] = kOob; plan_lane[i] = false;
-        if (k < band_instr) {
-            ++lw;
-            plan_row[i] = k / q.NCH;
-            plan_chunk[i] = k - plan_row[i] * q.NCH;
-            const int j = plan_chunk[i] * 64 + lane;
-            plan_lane[i] = j < q.P;
-            if (plan_lane[i]) plan_col[i] = col_voff(j);
-        }
-    }
-    // issue the NEW rows starting at ring row rr0; band index beyond the chunk -> all zeros
-    auto issue_band = [&](int rr0, bool real) {
-        int slot0 = rr0 % q.NR;
+    for (int i = 0; i < 9; ++i) wraw[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, (unsigned)(cv * 9 + i) * 16u, 0, 0);
+    const auto rb = rsrc(bias, q.b_bytes);
+    const u4 braw = __builtin_amdgcn_raw_buffer_load_b128(rb, q.b_bytes ? (unsigned)cv * 16u : kOob, 0, 0);
+    // weight (e, dy, dx) is element e * 9 + dy * 3 + dx of the lane's 9 * VEC.
+    // fp16: the (dx = 0, dx = 1) weights of each (e, dy) as one fp16 pair for
+    // v_dot2, and the dx = 2 weights of channels (2m, 2m + 1) as one pair for
+    // v_fma_mix (36 registers in all, like the raw block).
+    unsigned wp[kF16 ? 3 : 1][kF16 ? VEC : 1];
+    unsigned w2[kF16 ? 3 : 1][kF16 ? VEC / 2 : 1];
+    if constexpr (kF16) {
 #pragma unroll
-        for (int i = 0; i < kMaxLw; ++i) {
-            if (i < lw) {
-                int slot = slot0 + plan_row[i];
-                if (slot >= q.NR) slot -= q.NR;
-                const int ro = real ? row_voff(rr0 + plan_row[i]) : -1;
-                const unsigned vo = (ro < 0 || plan_col[i] == kOob) ? kOob : (unsigned)ro + plan_col[i];
-                const unsigned m0 = ring_lds + (unsigned)slot * row_bytes + (unsigned)plan_chunk[i] * 1024u;
-                if (plan_lane[i]) dma16(vo, __builtin_amdgcn_readfirstlane(m0), rs);
+        for (int m = 0; m < VEC / 2; ++m)
+#pragma unroll
+            for (int dy = 0; dy < 3; ++dy) {
+                const int k0 = 2 * m * 9 + dy * 3 + 2, k1 = k0 + 9;
+                const unsigned r0 = wraw[k0 >> 3][(k0 & 7) >> 1], r1 = wraw[k1 >> 3][(k1 & 7) >> 1];
+                if (k0 & 1) w2[dy][m] = pair_halves<1, 0>(r0, r1);   // k1 = k0 + 9 has the other parity
+                else w2[dy][m] = pair_halves<0, 1>(r0, r1);
             }
-        }
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+#pragma unroll
+            for (int dy = 0; dy < 3; ++dy) {
+                const int k = e * 9 + dy * 3;
+                const unsigned lo = wraw[k >> 3][(k & 7) >> 1];
+                const int k1 = k + 1;
+                const unsigned hi = wraw[k1 >> 3][(k1 & 7) >> 1];
+                wp[dy][e] = (k & 1) ? pair_halves<1, 0>(lo, hi) : lo;
+            }
+    }
+    float wf[kF16 ? 1 : VEC][3][3];
+    if constexpr (!kF16) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+#pragma unroll
+            for (int t = 0; t < 9; ++t) {
+                const int k = e * 9 + t;
+                wf[e][t / 3][t % 3] = elem_f32<T>(wraw[k / VEC], k % VEC);
+            }
+    }
+
+    const int oh0 = chunk * R;
+    const int ih0 = oh0 * SH - q.ph;
+    float acc[R][VEC];
+#pragma unroll
+    for (int o = 0; o < R; ++o)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[o][e] = 0.f;
+
+    // Input row i, three window columns (zeros outside the image).
+    u4 xbuf[NI][3];
+    auto load_row = [&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        const int ih = ih0 + i;
+        const bool rok = ih >= 0 && ih < q.H;
+        const unsigned soff = rok ? (unsigned)ih * q.in_row : 0u;
+#pragma unroll
+        for (int dx = 0; dx < 3; ++dx)
+            xbuf[i][dx] = __builtin_amdgcn_raw_buffer_load_b128(rx, rok ? coff[dx] : kOob, soff, kLoadPolicy);
     };
-
-    T *yn = y + (size_t)n * q.Ho * q.Wo * q.C;
-    const int cbase = owl * q.sw * q.CV + cvl;
-    float wf[Y][X][VEC];
-    float bf[VEC];
-    for (int b = 0; b < nbands; ++b) {
-        const int oh0 = oh_begin + b * RB;
-        const int rr0 = oh0 * SH;
-        // this wave's loads of band b are done when at most DEPTH * lw younger
-        // ones remain (none yet for band 0)
-        vm_wait(b == 0 ? 0 : q.DEPTH * lw);
-        __syncthreads();
-        if (b == 0) {
-            // bands 1 .. DEPTH+1: the ring slots they use are all still free
-            for (int d = 1; d <= q.DEPTH + 1; ++d)
-                issue_band(rr_first + IR + (d - 1) * NEW, d < nbands);
-        } else {
-            // band b+DEPTH+1 lands in the slots band b-1 read before the barrier
-            issue_band(rr0 + IR + q.DEPTH * NEW, b + 1 + q.DEPTH < nbands);
+    // The loads run PF rows ahead of the arithmetic; the scheduling barriers
+    // keep the compiler from sinking them next to their use.
+    static_for(std::make_integer_sequence<int, (PF < NI ? PF : NI)>{}, load_row);
+    // one input row per step; i is a compile-time constant in each step, so
+    // the row -> output-row mapping below costs nothing at run time
+    static_for(std::make_integer_sequence<int, NI>{}, [&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i + PF < NI) load_row(std::integral_constant<int, i + PF>{});
+        __builtin_amdgcn_sched_barrier(0);
+        const u4 *xv = xbuf[i];
+        unsigned xp[kF16 ? VEC : 1];   // fp16: (dx = 0, dx = 1) input pair of each channel
+        if constexpr (kF16) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                xp[e] = (e & 1) ? pair_halves<1, 1>(xv[0][e >> 1], xv[1][e >> 1])
+                                : pair_halves<0, 0>(xv[0][e >> 1], xv[1][e >> 1]);
         }
-        if (b == 0) {   // weights and bias arrived with the first band
-            const uint4 *wl = reinterpret_cast<const uint4 *>(ring + q.NR * q.P) + (active ? cvl : 0) * WV;
-            uint4 wraw[WV];
+        float xf[kF16 ? 1 : 3][VEC];
+        if constexpr (!kF16) {
 #pragma unroll
-            for (int i = 0; i < WV; ++i) wraw[i] = wl[i];
-            uint4 braw = make_uint4(0, 0, 0, 0);
-            if (q.b_bytes) braw = (reinterpret_cast<const uint4 *>(ring + q.NR * q.P + q.CV * WV))[active ? cvl : 0];
-            const T *wel = reinterpret_cast<const T *>(wraw);
-            const T *bel = reinterpret_cast<const T *>(&braw);
+            for (int dx = 0; dx < 3; ++dx)
 #pragma unroll
-            for (int j = 0; j < VEC; ++j) {
-#pragma unroll
-                for (int yy = 0; yy < Y; ++yy)
-#pragma unroll
-                    for (int xx = 0; xx < X; ++xx) wf[yy][xx][j] = to_f32(wel[(j * Y + yy) * X + xx]);
-                bf[j] = q.b_bytes ? to_f32(bel[j]) : 0.f;
-            }
+                for (int e = 0; e < VEC; ++e) xf[dx][e] = elem_f32<T>(xv[dx], e);
         }
-
-        float acc[RB][VEC];
+        // fold row i into every output row o with o * SH + dy * DH == i
+        static_for(std::make_integer_sequence<int, 3>{}, [&](auto dyc) __attribute__((always_inline)) {
+            constexpr int dy = decltype(dyc)::value;
+            constexpr int d = i - dy * DH;
+            if constexpr (d >= 0 && d % SH == 0 && d / SH < R) {
+                constexpr int o = d / SH;
+                if constexpr (kF16) {
+                    // dx = 0 and 1 in one v_dot2, dx = 2 by v_fma_mix
 #pragma unroll
-        for (int r = 0; r < RB; ++r)
-#pragma unroll
-            for (int j = 0; j < VEC; ++j) acc[r][j] = 0.f;
-        if (active) {
-            const int slot0 = rr0 % q.NR;
-#pragma unroll
-            for (int ir = 0; ir < IR; ++ir) {
-                int slot = slot0 + ir;
-                if (slot >= q.NR) slot -= q.NR;
-                const uint4 *row = ring + slot * q.P + cbase;
-#pragma unroll
-                for (int xx = 0; xx < X; ++xx) {
-                    uint4 raw = row[xx * q.dw * q.CV];
-                    vecT v = *reinterpret_cast<vecT *>(&raw);
-                    float vf[VEC];
-#pragma unroll
-                    for (int j = 0; j < VEC; ++j) vf[j] = to_f32(v[j]);
-#pragma unroll
-                    for (int r = 0; r < RB; ++r) {
-                        const int dy = ir - r * SH;      // compile-time after unrolling
-                        if (dy >= 0 && dy % DH == 0 && dy / DH < Y) {
-#pragma unroll
-                            for (int j = 0; j < VEC; ++j)
-                                acc[r][j] = fmaf(vf[j], wf[dy / DH][xx][j], acc[r][j]);
-                        }
+                    for (int e = 0; e < VEC; ++e) {
+                        acc[o][e] = dot2(xp[e], wp[dy][e], acc[o][e]);
+                        if (e & 1) acc[o][e] = fma_mix<1, 1>(xv[2][e >> 1], w2[dy][e >> 1], acc[o][e]);
+                        else acc[o][e] = fma_mix<0, 0>(xv[2][e >> 1], w2[dy][e >> 1], acc[o][e]);
                     }
+                } else {
+#pragma unroll
+                    for (int dx = 0; dx < 3; ++dx)
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e)
+                            acc[o][e] = fmaf(xf[dx][e], wf[e][dy][dx], acc[o][e]);
                 }
             }
+        });
+        // the output row whose window ends at input row i is complete
+        constexpr int dl = i - 2 * DH;
+        if constexpr (dl >= 0 && dl % SH == 0 && dl / SH < R) {
+            constexpr int o = dl / SH;
+            const int oh = oh0 + o;
+            const T *bel = reinterpret_cast<const T *>(&braw);
+            T ov[VEC];
 #pragma unroll
-            for (int r = 0; r < RB; ++r) {
-                const int oh = oh0 + r;
-                if (oh < oh_end) {
-                    vecT o;
-#pragma unroll
-                    for (int j = 0; j < VEC; ++j) o[j] = from_f32<T>(acc[r][j] + bf[j]);
-                    *reinterpret_cast<vecT *>(yn + ((size_t)oh * q.Wo + ow) * q.C + cv * VEC) = o;
-                }
-            }
+            for (int e = 0; e < VEC; ++e) ov[e] = from_f32<T>(acc[o][e] + to_f32(bel[e]));
+            const u4 packed = *reinterpret_cast<const u4 *>(ov);
+            const bool ook = oh < q.Ho;
+            __builtin_amdgcn_raw_buffer_store_b128(packed, ry, ook ? ooff : kOob, ook ? (unsigned)oh * q.out_row : 0u, kStorePolicy);
         }
-    }
-    // drain: no ring load may still be writing LDS when the workgroup retires
-    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+    });
 }
 
 // ----------------------------------------------------------------- host side
 
 struct Config {
-    int RB, IR, NEW, CV, TW, IW, P, NCH, RH, ncol, nslab, nchunk, DEPTH, NR, lds;
+    int R, nseg, nsb, nchunk;
 };
 
 int vec_of(int dtype) { return dtype == GCONV_F32 ? 4 : 8; }
@@ -335,83 +299,71 @@ bool shape_ok(const Problem &p)
     if ((p.G % vec_of(p.dtype)) != 0) return false;
     if (p.Y != 3 || p.X != 3) return false;
     if ((p.sh != 1 && p.sh != 2) || (p.dh != 1 && p.dh != 2)) return false;
-    // one image must be addressable by a 32-bit buffer offset
-    if ((long long)p.H * p.W * p.G * elem_size(p.dtype) >= (1LL << 31)) return false;
+    // one image of x and of y must be addressable by a 32-bit buffer offset
+    const long long es = elem_size(p.dtype);
+    if ((long long)p.H * p.W * p.G * es >= (1LL << 31)) return false;
+    if ((long long)p.Ho * p.Wo * p.G * es >= (1LL << 31)) return false;
     return true;
 }
 
 bool configure(const Problem &p, Config &c)
 {
-    const int VEC = vec_of(p.dtype);
-    const int Cv = p.G / VEC;
-    c.RB = 2;
-    c.IR = (c.RB - 1) * p.sh + (p.Y - 1) * p.dh + 1;
-    c.NEW = c.RB * p.sh;
-    c.CV = Cv < 64 ? Cv : 64;
-    c.TW = kBlock / c.CV;
-    if (c.TW > p.Wo) c.TW = p.Wo;
-    // largest strip whose ring fits; prefer deeper prefetch, then two workgroups per CU
-    for (;;) {
-        c.IW = (c.TW - 1) * p.sw + (p.X - 1) * p.dw + 1;
-        c.P = c.IW * c.CV;
-        c.NCH = (c.P + 63) / 64;
-        bool fits = false;
-        for (int depth = 3; depth >= 1 && !fits; --depth) {
-            const int nr = c.IR + (depth + 1) * c.NEW;
-            const int lw = (c.NEW * c.NCH + kWaves - 1) / kWaves;
-            if (nr * c.P * 16 + c.CV * 10 * 16 <= kLds && lw <= kMaxLw && depth * lw <= 36) {
-                c.DEPTH = depth;
-                c.NR = nr;
-                fits = true;
-            }
-        }
-        if (fits) break;
-        if (c.TW == 1) return false;
-        --c.TW;
-    }
-    c.lds = c.NR * c.P * 16 + c.CV * 9 * 16 + c.CV * 16;
-    const int per_cu = kLds / c.lds;
-    c.ncol = (p.Wo + c.TW - 1) / c.TW;
-    c.nslab = (Cv + c.CV - 1) / c.CV;
-    // row chunks: about one workgroup per resident slot, whole bands each
-    const long long strips = (long long)c.ncol * c.nslab * p.N;
-    const long long slots = 256LL * (per_cu > 0 ? per_cu : 1);
-    long long chunks = (slots + strips - 1) / strips;
-    const int max_chunks = (p.Ho + c.RB - 1) / c.RB;
-    if (chunks > max_chunks) chunks = max_chunks;
-    if (chunks < 1) chunks = 1;
-    const int bands = (int)(((p.Ho + chunks - 1) / chunks + c.RB - 1) / c.RB);
-    c.RH = bands * c.RB;
-    c.nchunk = (p.Ho + c.RH - 1) / c.RH;
-    return strips * c.nchunk < (1LL << 31);
+    const int Cv = p.G / vec_of(p.dtype);
+    const long long row_vecs = (long long)p.Wo * Cv;
+    c.nseg = (int)((row_vecs + 63) / 64);
+    c.nsb = (c.nseg + kWaves - 1) / kWaves;
+    // Rows per wave: long runs amortise the 2 * DH halo rows and the setup
+    // (weights, offsets), short runs give more waves to hide latency with.
+    // Measured on the MobileNetV2 shapes, about one wave per SIMD (1024 in
+    // all) with the longest run that gives is best; R comes from a small menu
+    // of compiled run lengths (shorter for stride 2, whose runs read twice
+    // the rows).
+    const long long wave_rows = (long long)p.Ho * c.nseg * p.N;
+    const long long want = (wave_rows + kTargetWaves - 1) / kTargetWaves;
+    c.R = 4;
+    for (int r : {7, 14, 28})
+        if (r <= want && (p.sh == 1 || r <= 14)) c.R = r;
+    c.nchunk = (p.Ho + c.R - 1) / c.R;
+    return row_vecs < (1LL << 30) && (long long)c.nsb * c.nchunk * p.N < (1LL << 31);
 }
 
-template <typename T, int SH, int DH>
-hipError_t go3(const Problem &p, const Config &c, const Args &a, hipStream_t s)
+template <typename T, int SH, int DH, int R, int PF>
+hipError_t go4(const Problem &p, const Config &c, const Args &a, hipStream_t s)
 {
     Params q;
-    q.N = p.N; q.C = p.G; q.Cv = p.G / VecOf<T>::n;
+    q.C = p.G; q.Cv = p.G / VecOf<T>::n;
     q.H = p.H; q.W = p.W; q.Ho = p.Ho; q.Wo = p.Wo;
     q.sw = p.sw; q.dw = p.dw; q.ph = p.ph; q.pw = p.pw;
-    q.CV = c.CV; q.TW = c.TW; q.IW = c.IW; q.P = c.P; q.NCH = c.NCH; q.RH = c.RH;
-    q.ncol = c.ncol; q.nslab = c.nslab; q.nchunk = c.nchunk;
-    q.DEPTH = c.DEPTH; q.NR = c.NR;
+    q.nseg = c.nseg; q.nsb = c.nsb; q.nchunk = c.nchunk;
+    q.in_row = (unsigned)((long long)p.W * p.G * sizeof(T));
+    q.out_row = (unsigned)((long long)p.Wo * p.G * sizeof(T));
     q.img_bytes = (unsigned)((long long)p.H * p.W * p.G * sizeof(T));
-    q.w_bytes = (unsigned)((long long)p.G * p.Y * p.X * sizeof(T));
+    q.oimg_bytes = (unsigned)((long long)p.Ho * p.Wo * p.G * sizeof(T));
+    q.w_bytes = (unsigned)((long long)p.G * 9 * sizeof(T));
     q.b_bytes = a.bias ? (unsigned)(p.G * sizeof(T)) : 0u;
-    const int blocks = c.ncol * c.nslab * c.nchunk * p.N;
-    auto k = kernel<T, SH, DH>;
-    if (c.lds > 64 * 1024)
-        hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, c.lds);
-    return enqueue(k, dim3(blocks), dim3(kBlock), c.lds, s, a, q, (const T *)a.x,
+    const int blocks = c.nsb * c.nchunk * p.N;
+    return enqueue(kernel<T, SH, DH, R, PF>, dim3(blocks), dim3(kBlock), 0, s, a, q, (const T *)a.x,
                    (const T *)a.w, (const T *)a.bias, (T *)a.y);
+}
+
+template <typename T, int R>
+hipError_t go3(const Problem &p, const Config &c, const Args &a, hipStream_t s)
+{
+    if (p.sh == 1) return p.dh == 1 ? go4<T, 1, 1, R, 3>(p, c, a, s) : go4<T, 1, 2, R, 3>(p, c, a, s);
+    if constexpr (R <= 14)
+        return p.dh == 1 ? go4<T, 2, 1, R, 3>(p, c, a, s) : go4<T, 2, 2, R, 3>(p, c, a, s);
+    return hipErrorInvalidValue;   // configure() never picks R > 14 for stride 2
 }
 
 template <typename T>
 hipError_t go(const Problem &p, const Config &c, const Args &a, hipStream_t s)
 {
-    if (p.sh == 1) return p.dh == 1 ? go3<T, 1, 1>(p, c, a, s) : go3<T, 1, 2>(p, c, a, s);
-    return p.dh == 1 ? go3<T, 2, 1>(p, c, a, s) : go3<T, 2, 2>(p, c, a, s);
+    switch (c.R) {
+    case 4: return go3<T, 4>(p, c, a, s);
+    case 7: return go3<T, 7>(p, c, a, s);
+    case 14: return go3<T, 14>(p, c, a, s);
+    default: return go3<T, 28>(p, c, a, s);
+    }
 }
 
 }  // namespace
@@ -428,11 +380,11 @@ gconv_plan plan(const Problem &p)
     configure(p, c);
     gconv_plan pl{};
     pl.path = GCONV_PATH_DEPTHWISE;
-    pl.grid[0] = (uint32_t)(c.ncol * c.nslab * c.nchunk * p.N);
+    pl.grid[0] = (uint32_t)(c.nsb * c.nchunk * p.N);
     pl.grid[1] = pl.grid[2] = 1;
     pl.block = kBlock;
-    pl.lds_bytes = (uint32_t)c.lds;
-    pl.groups_per_tile = (uint32_t)(c.CV * vec_of(p.dtype));
+    pl.lds_bytes = 0;
+    pl.groups_per_tile = (uint32_t)vec_of(p.dtype);
     return pl;
 }
 

@@ -69,20 +69,6 @@ __device__ __forceinline__ void dma16(unsigned voffset, unsigned lds_byte, rsrc_
                  : "memory", "m0");
 }
 
-// s_waitcnt vmcnt(n) for a wave-uniform n (other counters not waited on).
-__device__ __forceinline__ void vm_wait(int n)
-{
-#define GCONV_VMW(k) \
-    case k: __builtin_amdgcn_s_waitcnt(((k) & 15) | (7 << 4) | (15 << 8) | (((k) >> 4) << 14)); break;
-    switch (__builtin_amdgcn_readfirstlane(n)) {
-        GCONV_VMW(1) GCONV_VMW(2) GCONV_VMW(3) GCONV_VMW(4) GCONV_VMW(5) GCONV_VMW(6)
-        GCONV_VMW(7) GCONV_VMW(8) GCONV_VMW(9) GCONV_VMW(10) GCONV_VMW(11) GCONV_VMW(12)
-        GCONV_VMW(13) GCONV_VMW(14) GCONV_VMW(15) GCONV_VMW(16) GCONV_VMW(17) GCONV_VMW(18)
-        GCONV_VMW(19) GCONV_VMW(20) GCONV_VMW(21) GCONV_VMW(22) GCONV_VMW(23) GCONV_VMW(24)
-    default: __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); break;   // vmcnt(0)
-    }
-#undef GCONV_VMW
-}
 
 template <typename T> struct Mfma;
 template <> struct Mfma<_Float16> {

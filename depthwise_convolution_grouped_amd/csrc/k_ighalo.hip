@@ -106,22 +106,6 @@ __device__ __forceinline__ void dma16(unsigned voffset, unsigned lds_byte, rsrc_
                  : "memory", "m0");
 }
 
-// s_waitcnt vmcnt(n) for a wave-uniform n (other counters not waited on).
-__device__ __forceinline__ void vm_wait(int n)
-{
-#define GCONV_VMW(k) \
-    case k: __builtin_amdgcn_s_waitcnt(((k) & 15) | (7 << 4) | (15 << 8) | (((k) >> 4) << 14)); break;
-    switch (__builtin_amdgcn_readfirstlane(n)) {
-        GCONV_VMW(1) GCONV_VMW(2) GCONV_VMW(3) GCONV_VMW(4) GCONV_VMW(5) GCONV_VMW(6)
-        GCONV_VMW(7) GCONV_VMW(8) GCONV_VMW(9) GCONV_VMW(10) GCONV_VMW(11) GCONV_VMW(12)
-        GCONV_VMW(13) GCONV_VMW(14) GCONV_VMW(15) GCONV_VMW(16) GCONV_VMW(17) GCONV_VMW(18)
-        GCONV_VMW(19) GCONV_VMW(20) GCONV_VMW(21) GCONV_VMW(22) GCONV_VMW(23) GCONV_VMW(24)
-        GCONV_VMW(25) GCONV_VMW(26) GCONV_VMW(27) GCONV_VMW(28) GCONV_VMW(29) GCONV_VMW(30)
-        GCONV_VMW(31) GCONV_VMW(32)
-    default: __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); break;   // vmcnt(0)
-    }
-#undef GCONV_VMW
-}
 
 template <typename T> struct Mfma;
 template <> struct Mfma<_Float16> {
@@ -459,19 +443,7 @@ __global__ __launch_bounds__(kBlock, 2) void kernel(Params q, const T *__restric
                 {
                     int need = mw0 > mh_cur ? mw0 : mh_cur;
                     if (last && mb_cur > need) need = mb_cur;
-                    // Waiting until at most 2 B_LPW loads are outstanding is
-                    // exact when only the next two weight stages were issued
-                    // after the loads needed here, and stricter (waits for
-                    // some younger box or bias loads too, which are cheap by
-                    // then) when more were: one compare instead of the branch
-                    // tree that picks the counter immediate.  Only the last
-                    // stages, with fewer younger loads, take the tree.
-                    const int n = issued - need;
-                    if (n >= 2 * B_LPW)
-                        __builtin_amdgcn_s_waitcnt(((2 * B_LPW) & 15) | (7 << 4) | (15 << 8) |
-                                                   (((2 * B_LPW) >> 4) << 14));
-                    else
-                        vm_wait(n);
+                    vm_wait(issued - need);
                     __syncthreads();
                 }
                 // loads that run ahead: at a chunk's first stage the next

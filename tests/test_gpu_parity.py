@@ -233,6 +233,9 @@ DW_CASES = [
     ("bf16", 2, 264, 30, 3, 1, 1, 2),
     ("f16", 1, 16, 64, 1, 1, 1, 1),     # one column
     ("f16", 1, 16, 1, 64, 2, 1, 1),     # one row
+    ("f16", 1, 1024, 82, 82, 1, 1, 1),  # 14-row runs
+    ("bf16", 1, 1024, 118, 118, 1, 2, 2),  # 28-row runs, dilation 2
+    ("f32", 1, 512, 164, 164, 2, 1, 1),  # 14-row runs at stride 2
 ]
 
 
