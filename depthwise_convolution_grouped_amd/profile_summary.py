@@ -59,18 +59,19 @@ def _rows(d, name):
         return list(csv.DictReader(f))
 
 
-def counter_per_dispatch(d, counter, kernel_tag, grid_items):
+def counter_per_dispatch(d, counter, kernel_name, grid_items):
     """(values for dispatches of our kernel, values for the calibration copies).
 
-    Our kernel is told apart from other instances of the same path by its
-    total grid size in work-items."""
+    Our kernel is the exact symbol picked from the trace, with our grid size
+    in work-items (other configs of a workload may run another instance of
+    the same template, or the same instance on another grid)."""
     ours, copies = [], []
     for r in _rows(d, "*counter_collection.csv"):
         if r["Counter_Name"] != counter:
             continue
         name = r["Kernel_Name"]
         v = float(r["Counter_Value"])
-        if "gconv" in name and kernel_tag in name and int(r["Grid_Size"]) == grid_items:
+        if name == kernel_name and int(r["Grid_Size"]) == grid_items:
             ours.append(v)
         elif "copyBuffer" in name:
             copies.append(v)
@@ -107,10 +108,16 @@ def main(argv=None):
              if "gconv" in r["Kernel_Name"] and tag in r["Kernel_Name"] and
              int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]) == grid_items]
     grids = "%s x %d threads" % (tuple(plan["grid"]), plan["block"])
-    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0 for r in trace]
-
     if not trace:
         raise SystemExit("no dispatch of the %s kernel with %d work-items in %s" % (path, grid_items, a.trace))
+    # several template instances of the path can share the grid (a workload's
+    # second config): ours is the one with the most kernel time
+    total = {}
+    for r in trace:
+        total[r["Kernel_Name"]] = total.get(r["Kernel_Name"], 0) + int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    kernel_name = max(total, key=total.get)
+    trace = [r for r in trace if r["Kernel_Name"] == kernel_name]
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0 for r in trace]
     lines = ["# %s kernel on %s" % (path, a.workload), "",
              "Workload: %s." % inputs.WORKLOADS[a.workload].about, "",
              "Algorithmic work per launch: %d FLOP, %d bytes (x, w, bias and y once each)."
@@ -128,8 +135,8 @@ def main(argv=None):
                                               alg_flop / med / 1e6, grids)]
     entry = None
     if a.fetch and a.write:
-        f_ours, f_copy = counter_per_dispatch(a.fetch, "FETCH_SIZE", tag, grid_items)
-        w_ours, w_copy = counter_per_dispatch(a.write, "WRITE_SIZE", tag, grid_items)
+        f_ours, f_copy = counter_per_dispatch(a.fetch, "FETCH_SIZE", kernel_name, grid_items)
+        w_ours, w_copy = counter_per_dispatch(a.write, "WRITE_SIZE", kernel_name, grid_items)
         ref_kib = a.copy_mib * 1024.0
         # the calibration copies are the largest copyBuffer dispatches (MIB MiB each)
         f_ref = max(f_copy) if f_copy else None
