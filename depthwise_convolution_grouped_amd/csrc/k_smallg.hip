@@ -24,27 +24,14 @@
 // zero, which is where lanes of an unused K slice read.  Each wave owns NTW
 // tiles, keeps their weight fragments in registers and walks the box's
 // 16-pixel M tiles, ending in the fused epilogue (bias, round, store).
-#include "device_common.h"
-#include "gconv_internal.h"
+#include "smallg_common.h"
 
 namespace gconv {
 namespace smallg {
 namespace {
 
-constexpr int kBlock = 256;
-constexpr int kWaves = kBlock / 64;
 constexpr int kLdsTile = 80 * 1024;          // halo box budget (two workgroups per CU)
-constexpr unsigned kOob = 0x80000000u;
 
-typedef int rsrc_t __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-
-// n / d for 0 <= n < 2^16 and 1 <= d < 2^16 as umulhi(n, m) with
-// m = ceil(2^32 / d): the rounding error n * (m - 2^32 / d) / 2^32 stays below
-// 1 / d when n * d < 2^32, so the floor is exact.  d = 1 would need m = 2^32
-// and is passed through unchanged.
 struct Div {
     unsigned m;
     int d;
@@ -71,43 +58,6 @@ struct Params {
     Div dVS, dTW, dTH, dIH, dCPR;
     int CPR;                                      // 64-slot chunks per halo row
     unsigned img_bytes;
-};
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void *base, unsigned bytes)
-{
-    const unsigned long long a = (unsigned long long)base;
-    rsrc_t r;
-    r.x = (int)(unsigned)(a & 0xffffffffull);
-    r.y = (int)(unsigned)((a >> 32) & 0xffffull);
-    r.z = (int)bytes;
-    r.w = 0x00020000;
-    return r;
-}
-
-__device__ __forceinline__ void dma16(unsigned voffset, unsigned lds_byte, rsrc_t r)
-{
-    asm volatile("s_mov_b32 m0, %1\n\t"
-                 "s_nop 0\n\t"
-                 "buffer_load_dwordx4 %0, %2, 0 offen lds"
-                 :
-                 : "v"(voffset), "s"(lds_byte), "s"(r)
-                 : "memory", "m0");
-}
-
-template <typename T> struct Mfma;
-template <> struct Mfma<_Float16> {
-    typedef f16x8 V;
-    static __device__ __forceinline__ f32x4 run(V a, V b, f32x4 c)
-    {
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-    }
-};
-template <> struct Mfma<__bf16> {
-    typedef bf16x8 V;
-    static __device__ __forceinline__ f32x4 run(V a, V b, f32x4 c)
-    {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-    }
 };
 
 // NMF: MFMAs per tile (>= nmf), NTW: merged-group tiles per wave, CPGC: the
@@ -192,35 +142,7 @@ __global__ __launch_bounds__(kBlock) void kernel(Params q, const T *__restrict__
             const int xx = tap % q.X, yy = (tap / q.X) % q.Y, zz = tap / (q.X * q.Y);
             const int tp = ((zz * q.dd) * q.IH + yy * q.dh) * q.IW + xx * q.dw;
             aoff[j][s] = (live ? tp * q.VS + tl * q.CH8 + c : q.VPP) * 16;
-            uint4 raw = make_uint4(0, 0, 0, 0);
-            if constexpr (CPGC == 8) {
-                // all 8 channels of the slice belong to group (8c) / Cpg
-                const bool hit = live && (8 * c) / q.Cpg == gout;
-                const uint4 v = *reinterpret_cast<const uint4 *>(wk + tap * q.Cpg + (8 * c) % q.Cpg);
-                raw.x = hit ? v.x : 0u; raw.y = hit ? v.y : 0u;
-                raw.z = hit ? v.z : 0u; raw.w = hit ? v.w : 0u;
-            } else {
-                // group gout's CPGC channels sit at e0 = gout*CPGC - 8c of the slice
-                const int e0 = gout * CPGC - 8 * c;
-                const bool hit = live && e0 >= 0 && e0 < 8;
-                const T *src = wk + tap * CPGC;
-                unsigned d0, d1 = 0u;
-                if constexpr (CPGC == 4) {
-                    const uint2 v = *reinterpret_cast<const uint2 *>(src);
-                    d0 = v.x; d1 = v.y;
-                } else if constexpr (CPGC == 2) {
-                    d0 = *reinterpret_cast<const unsigned *>(src);
-                } else {
-                    d0 = *reinterpret_cast<const unsigned short *>(src);
-                }
-                const int dwi = e0 >> 1;                        // dword holding element e0
-                const unsigned lo = hit ? ((e0 & 1) ? (d0 << 16) : d0) : 0u;
-                const unsigned hi = hit ? d1 : 0u;
-                raw.x = dwi == 0 ? lo : 0u;
-                raw.y = dwi == 1 ? lo : (dwi == 0 ? hi : 0u);
-                raw.z = dwi == 2 ? lo : 0u;
-                raw.w = dwi == 3 ? lo : (dwi == 2 ? hi : 0u);
-            }
+            const uint4 raw = wslice<T, CPGC>(wk, tap, c, gout, q.Cpg, live);
             wfrag[j][s] = *reinterpret_cast<const V *>(&raw);
         }
     }
@@ -278,6 +200,7 @@ __global__ __launch_bounds__(kBlock) void kernel(Params q, const T *__restrict__
         }
     }
 }
+
 
 // ----------------------------------------------------------------- host side
 
@@ -421,6 +344,28 @@ bool supported(const Problem &p)
 
 gconv_plan plan(const Problem &p)
 {
+    RingConfig gc;
+    if (ring_configure(p, gc)) {
+        gconv_plan pl{};
+        pl.path = GCONV_PATH_SMALLG;
+        pl.grid[0] = (uint32_t)(gc.nmt * gc.nchunk * gc.ntb * p.N);
+        pl.grid[1] = pl.grid[2] = 1;
+        pl.block = kBlock;
+        pl.lds_bytes = (uint32_t)gc.lds;
+        pl.groups_per_tile = (uint32_t)gc.GN;
+        return pl;
+    }
+    RowConfig rc;
+    if (rows_configure(p, rc)) {
+        gconv_plan pl{};
+        pl.path = GCONV_PATH_SMALLG;
+        pl.grid[0] = (uint32_t)(rc.nmt * rc.ntb * p.N);
+        pl.grid[1] = pl.grid[2] = 1;
+        pl.block = kBlock;
+        pl.lds_bytes = 0;
+        pl.groups_per_tile = (uint32_t)rc.GN;
+        return pl;
+    }
     Config c;
     configure(p, c);
     gconv_plan pl{};
@@ -435,6 +380,14 @@ gconv_plan plan(const Problem &p)
 
 hipError_t launch(const Problem &p, const Args &a, hipStream_t s)
 {
+    // 2D 3x3 windows (stride 1 or 2, no dilation) stream rows; the rest
+    // stages halo boxes
+    RingConfig gc;
+    if (shape_ok(p) && ring_configure(p, gc))
+        return ring_launch(p, gc, a, s);
+    RowConfig rc;
+    if (shape_ok(p) && rows_configure(p, rc))
+        return rows_launch(p, rc, a, s);
     Config c;
     if (!configure(p, c)) return hipErrorInvalidValue;
     if (p.dtype == GCONV_F16) return go<_Float16>(p, c, a, s);

@@ -33,7 +33,7 @@ TRAFFIC = os.path.join(PROFILES, "traffic.json")
 PATH_SOURCES = {
     "generic": "k_generic.hip",
     "depthwise": "k_depthwise.hip",
-    "smallg_mfma": "k_smallg.hip",
+    "smallg_mfma": ("k_smallg.hip", "k_smallg_rows.hip", "k_smallg_ring.hip", "smallg_common.h"),
     "igemm_mfma": "k_igemm.hip",
     "ighalo_mfma": "k_ighalo.hip",
 }
@@ -45,7 +45,8 @@ KERNEL_TAGS = {"generic": "generic", "depthwise": "depthwise", "smallg_mfma": "s
 def source_hash(path_name: str) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(PKG, "csrc")
-    for f in (PATH_SOURCES[path_name],) + SHARED:
+    own = PATH_SOURCES[path_name]
+    for f in (own if isinstance(own, tuple) else (own,)) + SHARED:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
