@@ -138,10 +138,32 @@ __global__ __launch_bounds__(kBlock) void ring_kernel(RingParams q, const T *__r
             const int ch = (lt0 + j) * CH8 + c;
             foff[j][s2] = (unsigned)(pp * q.CVr + (ch ^ ((pp / S) & 15))) * 16u;
         }
-    // output: pixel (oh0 + o, ow0 + nn), channels (t0 + j) 16 + 4 kq .. + 3
+    // ---- output.  A completed output row goes through an LDS staging
+    // buffer (two, alternating): each lane drops its four channels of pixel
+    // nn there, and after the next barrier the workgroup writes the row's 16
+    // pixels x TPB * 32 bytes with one 16-byte store per thread and chunk --
+    // whole TPB * 32-byte pixel runs instead of 8-byte pieces of 16 pixels,
+    // which the texture path handles far better.  y is written once and not
+    // read back, so the stores are non-temporal (measured a few % faster).
+    constexpr int kNonTemporal = 2;
+    constexpr int kStageChunks = kWaves * NTW * 2;           // 16-byte chunks per staged pixel
+    constexpr int kStagePitch = kStageChunks * 16 + 16;      // bytes per staged pixel (padded)
+    const unsigned stage_lds = zero_slot + 16u;
+    const unsigned stage_w = (unsigned)(nn * kStagePitch + lt0 * 32 + kq * 8);   // this lane's 8 bytes
     const auto ry = buf_rsrc(y + (size_t)n * q.Ho * q.Wo * q.K, q.oimg_bytes);
-    const bool col_ok = ow0 + nn < q.Wo;
-    const unsigned obase = ((unsigned)(oh0 * q.Wo + ow0 + nn) * (unsigned)q.K + (unsigned)(t0 * 16 + 4 * kq)) * 2u;
+    auto flush = [&](int o, int buf) __attribute__((always_inline)) {
+        const unsigned sb = stage_lds + (unsigned)buf * 16u * kStagePitch;
+#pragma unroll
+        for (int k = (int)threadIdx.x; k < 16 * kStageChunks; k += kBlock) {
+            const int pix = k / kStageChunks, ck = k - (k / kStageChunks) * kStageChunks;
+            const uint4 v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(ring) +
+                                                            (sb - ring_lds) + pix * kStagePitch + ck * 16);
+            const bool ok = ow0 + pix < q.Wo && oh0 + o < q.Ho;
+            const unsigned go = ((unsigned)((oh0 + o) * q.Wo + ow0 + pix) * (unsigned)q.K + (unsigned)(tb * q.TPB * 16)) * 2u +
+                                (unsigned)ck * 16u;
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, ry, ok ? go : kOob, 0, kNonTemporal);
+        }
+    };
 
     // ---- prologue: the zero slot, then the first PF rows
     if (threadIdx.x == 0) *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(ring) + (size_t)NR * row_bytes) = make_uint4(0, 0, 0, 0);
@@ -155,8 +177,11 @@ __global__ __launch_bounds__(kBlock) void ring_kernel(RingParams q, const T *__r
 #pragma unroll
         for (int j = 0; j < NTW; ++j) acc[o][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // stores issued at step st (compile time): NTW when an output row completes
-    auto stores_at = [](int st) constexpr { return (st >= 2 && (st - 2) % S == 0 && (st - 2) / S < R) ? NTW : 0; };
+    // stores issued at step st (compile time): the flush of the output row
+    // completed at step st - 1, 16 * kStageChunks / kBlock per wave
+    auto stores_at = [](int st) constexpr {
+        return (st >= 3 && (st - 3) % S == 0 && (st - 3) / S < R) ? (16 * kStageChunks + kBlock - 1) / kBlock : 0;
+    };
     static_for(std::make_integer_sequence<int, NI>{}, [&](auto ic) __attribute__((always_inline)) {
         constexpr int i = decltype(ic)::value;
         // this wave's DMAs of row i are done when only later rows' DMAs and
@@ -171,6 +196,9 @@ __global__ __launch_bounds__(kBlock) void ring_kernel(RingParams q, const T *__r
         __syncthreads();
         // the slot of row i + PF was last read at step i - 1: refill it
         if constexpr (i + PF < NI) issue_row(i + PF);
+        // the output row completed at step i - 1 is staged: write it out
+        constexpr int dp = i - 3;
+        if constexpr (dp >= 0 && dp % S == 0 && dp / S < R) flush(dp / S, (dp / S) & 1);
         const unsigned rb = ring_lds + (unsigned)(i % NR) * row_bytes;
         V xf[NTW][NSR];
 #pragma unroll
@@ -196,19 +224,19 @@ __global__ __launch_bounds__(kBlock) void ring_kernel(RingParams q, const T *__r
         constexpr int dl = i - 2;
         if constexpr (dl >= 0 && dl % S == 0 && dl / S < R) {
             constexpr int o = dl / S;
-            const bool ook = col_ok && oh0 + o < q.Ho;
+            char *sb = reinterpret_cast<char *>(ring) + (stage_lds - ring_lds) + (o & 1) * 16 * kStagePitch + stage_w;
 #pragma unroll
             for (int j = 0; j < NTW; ++j) {
                 T ov[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) ov[e] = from_f32<T>(acc[o][j][e] + bias_v[j][e]);
-                const u32x2 packed = *reinterpret_cast<const u32x2 *>(ov);
-                __builtin_amdgcn_raw_buffer_store_b64(
-                    packed, ry, ook ? obase + (unsigned)(o * q.Wo) * (unsigned)q.K * 2u + (unsigned)(j * 32) : kOob,
-                    0, 0);
+                *reinterpret_cast<uint2 *>(sb + j * 32) = *reinterpret_cast<const uint2 *>(ov);
             }
         }
     });
+    // the last output row (completed at the last step) is still staged
+    __syncthreads();
+    flush(R - 1, (R - 1) & 1);
     // no DMA may still be writing LDS when the workgroup retires
     __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
 }
@@ -254,8 +282,8 @@ hipError_t ring_go3(const Problem &p, const RingConfig &c, const Args &a, hipStr
 template <typename T>
 hipError_t ring_launch_t(const Problem &p, const RingConfig &c, const Args &a, hipStream_t s)
 {
-    if (p.sh == 1) return c.R == 14 ? ring_go3<T, 1, 14>(p, c, a, s) : ring_go3<T, 1, 7>(p, c, a, s);
-    return c.R == 14 ? ring_go3<T, 2, 14>(p, c, a, s) : ring_go3<T, 2, 7>(p, c, a, s);
+    if (p.sh == 1) return c.R == 28 ? ring_go3<T, 1, 28>(p, c, a, s) : ring_go3<T, 1, 14>(p, c, a, s);
+    return ring_go3<T, 2, 14>(p, c, a, s);
 }
 
 }  // namespace
@@ -285,12 +313,14 @@ bool ring_configure(const Problem &p, RingConfig &c)
     c.RS = (c.IW * c.CV + 63) / 64 * 64;
     c.NINS = c.RS / 64;
     if (c.NINS > 8 * kWaves) return false;
-    c.lds = 4 * c.RS * 16 + 16;                          // NR = 4 ring rows + the zero slot
+    // NR = 4 ring rows, the zero slot, two staging rows of 16 padded pixels
+    c.lds = 4 * c.RS * 16 + 16 + 2 * 16 * (c.TPB * 2 * 16 + 16);
     c.nmt = (p.Wo + 15) / 16;
-    // rows per workgroup from {7, 14}: the longer run while the grid still
-    // gives every CU two workgroups
-    c.R = 7;
-    if ((long long)c.nmt * ((p.Ho + 13) / 14) * c.ntb * p.N >= 512) c.R = 14;
+    // rows per workgroup from {14, 28}: the longer run while the grid still
+    // gives every CU two workgroups (long runs amortise the two halo rows)
+    // (stride 2 keeps 14: its runs read twice the rows)
+    c.R = 14;
+    if (p.sh == 1 && (long long)c.nmt * ((p.Ho + 27) / 28) * c.ntb * p.N >= 512) c.R = 28;
     c.nchunk = (p.Ho + c.R - 1) / c.R;
     return (long long)c.nmt * c.nchunk * c.ntb * p.N < (1LL << 31);
 }
