@@ -1,10 +1,15 @@
-// Generic direct kernel: one thread per output element, any shape, any
-// dtype.  It is the fallback for shapes the tiled paths do not take and the
-// first, simplest HIP form of the operation declared in gconv.h.
+// Generic direct kernel: any shape, any dtype.  It is the fallback for
+// shapes the tiled paths do not take and the first, simplest HIP form of the
+// operation declared in gconv.h.
 //
-// Thread e owns y[n][od][oh][ow][g][k] (flat NDHWGK index e), walks the
-// window taps (z, y, x) and the group's Cpg input channels, accumulates in
-// fp32 and ends in the shared bias/convert epilogue.
+// L consecutive threads own y[n][od][oh][ow][g][k] (flat NDHWGK index e):
+// thread j of the L walks the window taps (z, y, x) and the input channels
+// c = j, j + L, ... of the group, accumulating in fp32; the L partial sums
+// are added by cross-lane exchanges (L divides the wave) and the first
+// thread ends in the shared bias/convert epilogue.  L = 1 for large outputs;
+// small problems (few outputs, long reductions) spread each reduction over
+// up to 16 threads, so the whole chip works and each thread's loads are few
+// and independent instead of one long dependent chain per output.
 #include "device_common.h"
 #include "gconv_internal.h"
 
@@ -14,49 +19,77 @@ namespace {
 
 constexpr int kBlock = 256;
 
-template <typename T>
+template <typename T, int L>
 __global__ __launch_bounds__(kBlock) void kernel(Problem p, const T *__restrict__ x,
                                                  const T *__restrict__ w,
                                                  const T *__restrict__ bias, T *__restrict__ y,
                                                  int total)
 {
-    int e = blockIdx.x * kBlock + threadIdx.x;
-    if (e >= total) return;
-    int r = e;
-    const int k = r % p.Kpg;  r /= p.Kpg;
-    const int g = r % p.G;    r /= p.G;
-    const int ow = r % p.Wo;  r /= p.Wo;
-    const int oh = r % p.Ho;  r /= p.Ho;
-    const int od = r % p.Do;  r /= p.Do;
-    const int n = r;
-    const int C = p.G * p.Cpg;
+    const int tid = blockIdx.x * kBlock + threadIdx.x;
+    const int e = tid / L, part = tid - (tid / L) * L;
     float acc = 0.f;
-    for (int z = 0; z < p.Z; ++z) {
-        const int id = od * p.sd - p.pd + z * p.dd;
-        if (id < 0 || id >= p.D) continue;
-        for (int yy = 0; yy < p.Y; ++yy) {
-            const int ih = oh * p.sh - p.ph + yy * p.dh;
-            if (ih < 0 || ih >= p.H) continue;
-            for (int xx = 0; xx < p.X; ++xx) {
-                const int iw = ow * p.sw - p.pw + xx * p.dw;
-                if (iw < 0 || iw >= p.W) continue;
-                const T *xp = x + ((((n * p.D + id) * p.H + ih) * p.W + iw) * C + g * p.Cpg);
-                const T *wp = w + ((((g * p.Kpg + k) * p.Z + z) * p.Y + yy) * p.X + xx) * p.Cpg;
-                for (int c = 0; c < p.Cpg; ++c) acc = fmaf(to_f32(xp[c]), to_f32(wp[c]), acc);
+    int g = 0, k = 0;
+    if (e < total) {
+        int r = e;
+        k = r % p.Kpg;  r /= p.Kpg;
+        g = r % p.G;    r /= p.G;
+        const int ow = r % p.Wo;  r /= p.Wo;
+        const int oh = r % p.Ho;  r /= p.Ho;
+        const int od = r % p.Do;  r /= p.Do;
+        const int n = r;
+        const int C = p.G * p.Cpg;
+        for (int z = 0; z < p.Z; ++z) {
+            const int id = od * p.sd - p.pd + z * p.dd;
+            if (id < 0 || id >= p.D) continue;
+            for (int yy = 0; yy < p.Y; ++yy) {
+                const int ih = oh * p.sh - p.ph + yy * p.dh;
+                if (ih < 0 || ih >= p.H) continue;
+                for (int xx = 0; xx < p.X; ++xx) {
+                    const int iw = ow * p.sw - p.pw + xx * p.dw;
+                    if (iw < 0 || iw >= p.W) continue;
+                    const T *xp = x + ((((n * p.D + id) * p.H + ih) * p.W + iw) * C + g * p.Cpg);
+                    const T *wp = w + ((((g * p.Kpg + k) * p.Z + z) * p.Y + yy) * p.X + xx) * p.Cpg;
+                    for (int c = part; c < p.Cpg; c += L) acc = fmaf(to_f32(xp[c]), to_f32(wp[c]), acc);
+                }
             }
         }
     }
-    y[e] = finish<T>(acc, bias, g * p.Kpg + k);
+    // the L partial sums of one output sit in L consecutive lanes of a wave
+#pragma unroll
+    for (int m = L / 2; m >= 1; m /= 2) acc += __shfl_xor(acc, m);
+    if (e < total && part == 0) y[e] = finish<T>(acc, bias, g * p.Kpg + k);
+}
+
+// threads per output: enough threads to fill the chip, at most the channels
+// a thread would otherwise walk alone
+int lanes_for(const Problem &p)
+{
+    const long long outs = p.y_elems();
+    int L = 1;
+    while (L < 16 && outs * L < 256LL * kBlock && 2 * L <= p.Cpg * p.taps()) L *= 2;
+    return L;
+}
+
+template <int DT, int L>
+hipError_t go2(const Problem &p, const Args &a, hipStream_t s)
+{
+    using T = typename Elem<DT>::T;
+    const int total = (int)p.y_elems();
+    const int blocks = (int)(((long long)total * L + kBlock - 1) / kBlock);
+    return enqueue(kernel<T, L>, dim3(blocks), dim3(kBlock), 0, s, a, p,
+                   (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y, total);
 }
 
 template <int DT>
 hipError_t go(const Problem &p, const Args &a, hipStream_t s)
 {
-    using T = typename Elem<DT>::T;
-    const int total = (int)p.y_elems();
-    const int blocks = (total + kBlock - 1) / kBlock;
-    return enqueue(kernel<T>, dim3(blocks), dim3(kBlock), 0, s, a, p,
-                   (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y, total);
+    switch (lanes_for(p)) {
+    case 1: return go2<DT, 1>(p, a, s);
+    case 2: return go2<DT, 2>(p, a, s);
+    case 4: return go2<DT, 4>(p, a, s);
+    case 8: return go2<DT, 8>(p, a, s);
+    default: return go2<DT, 16>(p, a, s);
+    }
 }
 
 }  // namespace
@@ -67,7 +100,7 @@ gconv_plan plan(const Problem &p)
 {
     gconv_plan pl{};
     pl.path = GCONV_PATH_GENERIC;
-    pl.grid[0] = (uint32_t)((p.y_elems() + kBlock - 1) / kBlock);
+    pl.grid[0] = (uint32_t)((p.y_elems() * lanes_for(p) + kBlock - 1) / kBlock);
     pl.grid[1] = pl.grid[2] = 1;
     pl.block = kBlock;
     pl.lds_bytes = 0;

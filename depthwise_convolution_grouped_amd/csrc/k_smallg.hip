@@ -32,22 +32,6 @@ namespace {
 
 constexpr int kLdsTile = 80 * 1024;          // halo box budget (two workgroups per CU)
 
-struct Div {
-    unsigned m;
-    int d;
-};
-inline Div make_div(int d)
-{
-    Div r;
-    r.d = d;
-    r.m = d > 1 ? (unsigned)((0x100000000ull + (unsigned long long)d - 1) / (unsigned long long)d) : 0u;
-    return r;
-}
-__device__ __forceinline__ int fdiv(int n, Div v)
-{
-    return v.d == 1 ? n : (int)__umulhi((unsigned)n, v.m);
-}
-
 struct Params {
     int N, G, Cpg, Kpg, C, K;
     int D, H, W, Do, Ho, Wo, Z, Y, X;
@@ -56,7 +40,10 @@ struct Params {
     int TD, TH, TW, ID, IH, IW, MT;              // output box, halo box, M tiles per box
     int ntd, nth, ntw, nslab;
     Div dVS, dTW, dTH, dIH, dCPR;
+    Div dCH8, dX, dY, dKpg, dCpg;                 // divisors of the fragment set-up
     int CPR;                                      // 64-slot chunks per halo row
+    int stage_off, SP;                            // LDS byte offset of the output staging, bytes per staged pixel
+    Div dSC;                                      // 16-byte chunks per staged pixel (2 NS)
     unsigned img_bytes;
 };
 
@@ -129,20 +116,21 @@ __global__ __launch_bounds__(kBlock) void kernel(Params q, const T *__restrict__
         const int ntile = slab * q.NS + tl;
         const bool tile_ok = ntile < q.NT && tl < q.NS;
         const int g0 = tile_ok ? ntile * q.GN : 0;
-        const int gout = nn / q.Kpg, kout = nn - gout * q.Kpg;      // group within tile, channel
+        const int gout = fdiv(nn, q.dKpg), kout = nn - gout * q.Kpg;   // group within tile, channel
         const T *wk = w + ((size_t)(g0 + gout) * q.Kpg + kout) * taps * q.Cpg;
 #pragma unroll
         for (int s = 0; s < NMF; ++s) {
             const int k8 = 4 * s + kq;
             const bool live = tile_ok && s < q.nmf && k8 < q.slices;
             const int kk = live ? k8 : 0;
-            const int tap = kk / q.CH8, c = kk - tap * q.CH8;
+            const int tap = fdiv(kk, q.dCH8), c = kk - tap * q.CH8;
             // input slice: tap offset inside the halo box, chunk of this tile;
             // an unused slice reads the zero slot of the lane's own pixel
-            const int xx = tap % q.X, yy = (tap / q.X) % q.Y, zz = tap / (q.X * q.Y);
+            const int t1 = fdiv(tap, q.dX), xx = tap - t1 * q.X;
+            const int zz = fdiv(t1, q.dY), yy = t1 - zz * q.Y;
             const int tp = ((zz * q.dd) * q.IH + yy * q.dh) * q.IW + xx * q.dw;
             aoff[j][s] = (live ? tp * q.VS + tl * q.CH8 + c : q.VPP) * 16;
-            const uint4 raw = wslice<T, CPGC>(wk, tap, c, gout, q.Cpg, live);
+            const uint4 raw = wslice<T, CPGC>(wk, tap, c, gout, q.dCpg, live);
             wfrag[j][s] = *reinterpret_cast<const V *>(&raw);
         }
     }
@@ -165,6 +153,7 @@ __global__ __launch_bounds__(kBlock) void kernel(Params q, const T *__restrict__
     const int box = q.TD * q.TH * q.TW;
     const int Do_Ho_Wo = q.Do * q.Ho * q.Wo;
     const char *hb = reinterpret_cast<const char *>(halo);
+    char *stage = reinterpret_cast<char *>(halo) + q.stage_off;
     for (int mt = 0; mt < q.MT; ++mt) {
         // lane's pixel: m = lane % 16 of this M tile (reads clamped inside the box)
         const int pix = mt * 16 + nn;
@@ -172,9 +161,6 @@ __global__ __launch_bounds__(kBlock) void kernel(Params q, const T *__restrict__
         const int r1 = fdiv(pc, q.dTW), ax = pc - r1 * q.TW;
         const int az = fdiv(r1, q.dTH), ay = r1 - az * q.TH;
         const char *pbase = hb + (size_t)((((az * q.sd) * q.IH + ay * q.sh) * q.IW + ax * q.sw) * q.VS) * 16;
-        const int gd = od0 + az, gh = oh0 + ay, gw = ow0 + ax;
-        const bool store_ok = pix < box && gd < q.Do && gh < q.Ho && gw < q.Wo;
-        T *yrow = y + ((size_t)n * Do_Ho_Wo + ((size_t)gd * q.Ho + gh) * q.Wo + gw) * q.K;
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
             const int tl = wave * NTW + j;               // tile within the slab
@@ -191,13 +177,33 @@ __global__ __launch_bounds__(kBlock) void kernel(Params q, const T *__restrict__
 #pragma unroll
             for (int s = 0; s < NMF; ++s) acc = Mfma<T>::run(wfrag[j][s], afrag[s], acc);
             // acc[i] = output channel ntile*16 + 4 kq + i (= g*Kpg + k) of this lane's pixel
-            if (store_ok) {
+            if (pix < box) {
                 T o[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) o[i] = from_f32<T>(acc[i] + bias_v[j][i]);
-                *reinterpret_cast<uint2 *>(yrow + ntile * 16 + 4 * kq) = *reinterpret_cast<const uint2 *>(o);
+                *reinterpret_cast<uint2 *>(stage + pix * q.SP + tl * 32 + kq * 8) = *reinterpret_cast<const uint2 *>(o);
             }
         }
+    }
+    // ---- the box's outputs leave from the LDS staging area as whole runs of
+    // the slab's channels per pixel (NS x 32 bytes), one 16-byte
+    // non-temporal store per thread and chunk: 8-byte pieces of 16 pixels per
+    // lane are much slower through the texture path
+    __syncthreads();
+    const int sc = 2 * q.NS;                        // 16-byte chunks per staged pixel
+    const int ch0 = slab * q.NS * 16;               // first output channel of the slab
+    const auto ry = __builtin_amdgcn_make_buffer_rsrc(y + (size_t)n * Do_Ho_Wo * q.K, (short)0,
+                                                      (int)((unsigned)Do_Ho_Wo * (unsigned)q.K * 2u), 0x00020000);
+    for (int k = t; k < box * sc; k += kBlock) {
+        const int pix = fdiv(k, q.dSC), ck = k - pix * sc;
+        const int r1 = fdiv(pix, q.dTW), ax = pix - r1 * q.TW;
+        const int az = fdiv(r1, q.dTH), ay = r1 - az * q.TH;
+        const int gd = od0 + az, gh = oh0 + ay, gw = ow0 + ax;
+        const int ch = ch0 + ck * 8;
+        const bool ok = gd < q.Do && gh < q.Ho && gw < q.Wo && ch < q.K;
+        const uint4 v = *reinterpret_cast<const uint4 *>(stage + pix * q.SP + ck * 16);
+        const unsigned go = ((unsigned)((gd * q.Ho + gh) * q.Wo + gw) * (unsigned)q.K + (unsigned)ch) * 2u;
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, ry, ok ? go : kOob, 0, 2);
     }
 }
 
@@ -206,7 +212,7 @@ __global__ __launch_bounds__(kBlock) void kernel(Params q, const T *__restrict__
 
 struct Config {
     int GN, CH8, slices, nmf, NMF, NTW, NT, NS, VPP, VS, CPR;
-    int TD, TH, TW, ID, IH, IW, MT, ntd, nth, ntw, nslab, lds;
+    int TD, TH, TW, ID, IH, IW, MT, ntd, nth, ntw, nslab, lds, stage_off;
 };
 
 int pick_nmf(int nmf)
@@ -228,6 +234,8 @@ bool shape_ok(const Problem &p)
     const int slices = p.taps() * GN * p.Cpg / 8;
     if (pick_nmf((slices + 3) / 4) == 0) return false;
     if ((long long)p.D * p.H * p.W * p.G * p.Cpg * 2 >= (1LL << 31)) return false;
+    // one image of y must be addressable by a 32-bit buffer offset
+    if ((long long)p.Do * p.Ho * p.Wo * p.G * p.Kpg * 2 >= (1LL << 31)) return false;
     return true;
 }
 
@@ -260,7 +268,8 @@ bool configure(const Problem &p, Config &c)
                 const int IH = (TH - 1) * p.sh + (p.Y - 1) * p.dh + 1;
                 const int IW = (TW - 1) * p.sw + (p.X - 1) * p.dw + 1;
                 const long long slots = (long long)ID * IH * IW * c.VS;
-                if (slots * 16 > kLdsTile || slots >= 65536) continue;
+                const long long stage_bytes = (long long)((pix + 15) / 16 * 16) * (c.NS * 32 + 16);
+                if (slots * 16 + stage_bytes > kLdsTile || slots >= 65536) continue;
                 const int MT = (pix + 15) / 16;
                 const int ntd = (p.Do + TD - 1) / TD, nth = (p.Ho + TH - 1) / TH, ntw = (p.Wo + TW - 1) / TW;
                 const double useful = (double)p.Do * p.Ho * p.Wo / ((double)ntd * nth * ntw);
@@ -272,7 +281,8 @@ bool configure(const Problem &p, Config &c)
                     found = true;
                     c.TD = TD; c.TH = TH; c.TW = TW; c.ID = ID; c.IH = IH; c.IW = IW;
                     c.MT = MT; c.ntd = ntd; c.nth = nth; c.ntw = ntw;
-                    c.lds = (int)(slots * 16);
+                    c.lds = (int)(slots * 16 + stage_bytes);
+                    c.stage_off = (int)(slots * 16);
                 }
             }
         }
@@ -300,6 +310,9 @@ hipError_t go4(const Problem &p, const Config &c, const Args &a, hipStream_t s)
     q.ntd = c.ntd; q.nth = c.nth; q.ntw = c.ntw; q.nslab = c.nslab;
     q.dVS = make_div(c.VS); q.dTW = make_div(c.TW); q.dTH = make_div(c.TH);
     q.dIH = make_div(c.IH); q.dCPR = make_div(c.CPR); q.CPR = c.CPR;
+    q.stage_off = c.stage_off; q.SP = c.NS * 32 + 16; q.dSC = make_div(2 * c.NS);
+    q.dCH8 = make_div(c.CH8); q.dX = make_div(p.X); q.dY = make_div(p.Y);
+    q.dKpg = make_div(p.Kpg); q.dCpg = make_div(p.Cpg);
     q.img_bytes = (unsigned)((long long)p.D * p.H * p.W * p.C() * 2);
     const int blocks = c.ntw * c.nth * c.ntd * c.nslab * p.N;
     auto k = kernel<T, NMF, NTW, CPGC>;

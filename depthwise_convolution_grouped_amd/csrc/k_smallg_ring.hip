@@ -26,6 +26,7 @@ namespace smallg {
 namespace {
 
 struct RingParams {
+    Div dCpg, dKpg;
     int H, W, Ho, Wo, C, K, Cpg, Kpg, GN, NT;
     int ph, pw;
     int CVr, IW, RS;              // chunks per ring pixel, ring pixels per row, slots per ring row (mult. of 64)
@@ -96,7 +97,7 @@ __global__ __launch_bounds__(kBlock) void ring_kernel(RingParams q, const T *__r
 
     // ---- weight fragments of all taps: W[j][dy][s2], lane (row nn, slice kq)
     V wfrag[NTW][3][NSR];
-    const int gout = nn / q.Kpg, kout = nn - (nn / q.Kpg) * q.Kpg;
+    const int gout = fdiv(nn, q.dKpg), kout = nn - gout * q.Kpg;
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
         const int g0 = (t0 + j) * q.GN;
@@ -108,7 +109,7 @@ __global__ __launch_bounds__(kBlock) void ring_kernel(RingParams q, const T *__r
                 const int k8 = 4 * s2 + kq;
                 const bool live = k8 < NSL;
                 const int dx = live ? k8 / CH8 : 0, c = live ? k8 - (k8 / CH8) * CH8 : 0;
-                const uint4 raw = wslice<T, CPGC>(wk, live ? dy * 3 + dx : 0, c, gout, q.Cpg, live);
+                const uint4 raw = wslice<T, CPGC>(wk, live ? dy * 3 + dx : 0, c, gout, q.dCpg, live);
                 wfrag[j][dy][s2] = *reinterpret_cast<const V *>(&raw);
             }
     }
@@ -247,6 +248,7 @@ hipError_t ring_go(const Problem &p, const RingConfig &c, const Args &a, hipStre
     RingParams q;
     q.H = p.H; q.W = p.W; q.Ho = p.Ho; q.Wo = p.Wo; q.C = p.C(); q.K = p.K();
     q.Cpg = p.Cpg; q.Kpg = p.Kpg; q.GN = c.GN; q.NT = c.NT;
+    q.dCpg = make_div(p.Cpg); q.dKpg = make_div(p.Kpg);
     q.ph = p.ph; q.pw = p.pw;
     q.CVr = c.CV; q.IW = c.IW; q.RS = c.RS; q.NINS = c.NINS;
     q.TPB = c.TPB; q.ntb = c.ntb;

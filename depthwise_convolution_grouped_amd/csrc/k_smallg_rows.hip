@@ -22,6 +22,7 @@ namespace smallg {
 namespace {
 
 struct RowParams {
+    Div dCpg, dKpg;
     int H, W, Ho, Wo, C, K, Cpg, Kpg, GN, NT;
     int sw, ph, pw;
     int nchunk, nmt, ntb;         // row chunks per image, M tiles per image, tile blocks
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(kBlock) void rows_kernel(RowParams q, const T *__re
 
     // ---- weight fragments of all taps: W[j][dy][s2], lane (row nn, slice kq)
     V wfrag[NTW][3][NSR];
-    const int gout = nn / q.Kpg, kout = nn - (nn / q.Kpg) * q.Kpg;
+    const int gout = fdiv(nn, q.dKpg), kout = nn - gout * q.Kpg;
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
         const bool tile_ok = t0 + j < q.NT;
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(kBlock) void rows_kernel(RowParams q, const T *__re
                 const int k8 = 4 * s2 + kq;
                 const bool live = tile_ok && k8 < NSL;
                 const int dx = live ? k8 / CH8 : 0, c = live ? k8 - (k8 / CH8) * CH8 : 0;
-                const uint4 raw = wslice<T, CPGC>(wk, live ? dy * 3 + dx : 0, c, gout, q.Cpg, live);
+                const uint4 raw = wslice<T, CPGC>(wk, live ? dy * 3 + dx : 0, c, gout, q.dCpg, live);
                 wfrag[j][dy][s2] = *reinterpret_cast<const V *>(&raw);
             }
     }
@@ -175,6 +176,7 @@ hipError_t rows_go(const Problem &p, const RowConfig &c, const Args &a, hipStrea
     RowParams q;
     q.H = p.H; q.W = p.W; q.Ho = p.Ho; q.Wo = p.Wo; q.C = p.C(); q.K = p.K();
     q.Cpg = p.Cpg; q.Kpg = p.Kpg; q.GN = c.GN; q.NT = c.NT;
+    q.dCpg = make_div(p.Cpg); q.dKpg = make_div(p.Kpg);
     q.sw = p.sw; q.ph = p.ph; q.pw = p.pw;
     q.nchunk = c.nchunk; q.nmt = c.nmt; q.ntb = c.ntb;
     q.in_row = (unsigned)((long long)p.W * p.C() * 2);

@@ -25,6 +25,22 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // m = ceil(2^32 / d): the rounding error n * (m - 2^32 / d) / 2^32 stays below
 // 1 / d when n * d < 2^32, so the floor is exact.  d = 1 would need m = 2^32
 // and is passed through unchanged.
+struct Div {
+    unsigned m;
+    int d;
+};
+inline Div make_div(int d)
+{
+    Div r;
+    r.d = d;
+    r.m = d > 1 ? (unsigned)((0x100000000ull + (unsigned long long)d - 1) / (unsigned long long)d) : 0u;
+    return r;
+}
+__device__ __forceinline__ int fdiv(int n, Div v)
+{
+    return v.d == 1 ? n : (int)__umulhi((unsigned)n, v.m);
+}
+
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, unsigned bytes)
 {
     const unsigned long long a = (unsigned long long)base;
@@ -70,13 +86,15 @@ template <> struct Mfma<__bf16> {
 // loads are unconditional (callers pass tap = c8 = 0 for a dead slice), so
 // they issue together; the zeroing happens afterwards.
 template <typename T, int CPGC>
-__device__ __forceinline__ uint4 wslice(const T *wk, int tap, int c8, int gout, int Cpg, bool live)
+__device__ __forceinline__ uint4 wslice(const T *wk, int tap, int c8, int gout, Div dCpg, bool live)
 {
     uint4 raw = make_uint4(0, 0, 0, 0);
     if constexpr (CPGC == 8) {
         // all 8 channels of the slice belong to group (8 c8) / Cpg
-        const bool hit = live && (8 * c8) / Cpg == gout;
-        const uint4 v = *reinterpret_cast<const uint4 *>(wk + tap * Cpg + (8 * c8) % Cpg);
+        const int Cpg = dCpg.d;
+        const int gs = fdiv(8 * c8, dCpg);
+        const bool hit = live && gs == gout;
+        const uint4 v = *reinterpret_cast<const uint4 *>(wk + tap * Cpg + (8 * c8 - gs * Cpg));
         raw.x = hit ? v.x : 0u; raw.y = hit ? v.y : 0u;
         raw.z = hit ? v.z : 0u; raw.w = hit ? v.w : 0u;
     } else {
