@@ -361,7 +361,7 @@ gconv_plan plan(const Problem &p)
     if (ring_configure(p, gc)) {
         gconv_plan pl{};
         pl.path = GCONV_PATH_SMALLG;
-        pl.grid[0] = (uint32_t)(gc.nmt * gc.nchunk * gc.ntb * p.N);
+        pl.grid[0] = (uint32_t)gc.blocks;
         pl.grid[1] = pl.grid[2] = 1;
         pl.block = kBlock;
         pl.lds_bytes = (uint32_t)gc.lds;

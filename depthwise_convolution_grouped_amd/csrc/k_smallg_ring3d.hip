@@ -1,0 +1,25 @@
+// Instances of the LDS-ring small-group kernel (smallg_ring.h) for 3D 3x3x3
+// windows at stride 1: a ring row holds the three input planes' row
+// segments, so each step folds 3 planes x 3 window rows into the output rows.
+#include "smallg_ring.h"
+
+namespace gconv {
+namespace smallg {
+namespace {
+
+template <typename T>
+hipError_t ring3d_launch_t(const Problem &p, const RingConfig &c, const Args &a, hipStream_t s)
+{
+    if (c.CH8 == 1) return c.NTW == 4 ? ring_go4<T, 1, 7, 1, 4, 3>(p, c, a, s) : ring_go4<T, 1, 7, 1, 2, 3>(p, c, a, s);
+    return c.NTW == 2 ? ring_go4<T, 1, 7, 2, 2, 3>(p, c, a, s) : ring_go4<T, 1, 7, 2, 1, 3>(p, c, a, s);
+}
+
+}  // namespace
+
+hipError_t ring3d_launch(const Problem &p, const RingConfig &c, const Args &a, hipStream_t s)
+{
+    return p.dtype == GCONV_F16 ? ring3d_launch_t<_Float16>(p, c, a, s) : ring3d_launch_t<__bf16>(p, c, a, s);
+}
+
+}  // namespace smallg
+}  // namespace gconv

@@ -143,13 +143,16 @@ struct RowConfig {
 bool rows_configure(const Problem &p, RowConfig &c);
 hipError_t rows_launch(const Problem &p, const RowConfig &c, const Args &a, hipStream_t s);
 
-// LDS-ring variant (k_smallg_ring.hip): the same windows on images whose
-// channel rows fill the ring's swizzle (C a multiple of 128).
+// LDS-ring variant (smallg_ring.h): 2D 3x3 windows (stride 1 or 2) and 3D
+// 3x3x3 windows (stride 1), no dilation, when the channel tiles group into
+// ring pixels of 16 (or, in 3D, 8) chunks.  The 2D instances live in
+// k_smallg_ring.hip, the 3D ones in k_smallg_ring3d.hip.
 struct RingConfig {
-    int GN, CH8, NT, NTW, TPB, ntb, R, CV, IW, RS, NINS, nmt, nchunk, lds;
+    int GN, CH8, NT, NTW, TPB, ntb, DZ, R, CV, IW, RS, NINS, nmt, nchunk, blocks, lds;
 };
 bool ring_configure(const Problem &p, RingConfig &c);
 hipError_t ring_launch(const Problem &p, const RingConfig &c, const Args &a, hipStream_t s);
+hipError_t ring3d_launch(const Problem &p, const RingConfig &c, const Args &a, hipStream_t s);
 
 }  // namespace smallg
 }  // namespace gconv

@@ -33,7 +33,8 @@ TRAFFIC = os.path.join(PROFILES, "traffic.json")
 PATH_SOURCES = {
     "generic": "k_generic.hip",
     "depthwise": "k_depthwise.hip",
-    "smallg_mfma": ("k_smallg.hip", "k_smallg_rows.hip", "k_smallg_ring.hip", "smallg_common.h"),
+    "smallg_mfma": ("k_smallg.hip", "k_smallg_rows.hip", "k_smallg_ring.hip", "k_smallg_ring3d.hip",
+                    "smallg_common.h", "smallg_ring.h"),
     "igemm_mfma": "k_igemm.hip",
     "ighalo_mfma": "k_ighalo.hip",
 }
