@@ -73,6 +73,13 @@ bool supported(const Problem &p);
 gconv_plan plan(const Problem &p);
 hipError_t launch(const Problem &p, const Args &a, hipStream_t s);
 }
+// The halo path's variant with the whole input box resident in LDS; the
+// halo path runs it whenever it takes the problem.
+namespace ighalo_box {
+bool supported(const Problem &p);
+gconv_plan plan(const Problem &p);
+hipError_t launch(const Problem &p, const Args &a, hipStream_t s);
+}
 namespace ighalo {
 bool supported(const Problem &p);
 gconv_plan plan(const Problem &p);

@@ -627,11 +627,12 @@ hipError_t go(const Problem &p, const Config &c, const Args &a, hipStream_t s)
 bool supported(const Problem &p)
 {
     Config c;
-    return configure(p, c);
+    return ighalo_box::supported(p) || configure(p, c);
 }
 
 gconv_plan plan(const Problem &p)
 {
+    if (ighalo_box::supported(p)) return ighalo_box::plan(p);
     Config c;
     configure(p, c);
     gconv_plan pl{};
@@ -647,6 +648,7 @@ gconv_plan plan(const Problem &p)
 
 hipError_t launch(const Problem &p, const Args &a, hipStream_t s)
 {
+    if (ighalo_box::supported(p)) return ighalo_box::launch(p, a, s);
     Config c;
     if (!configure(p, c)) return hipErrorInvalidValue;
     if (p.dtype == GCONV_F16) return go<_Float16>(p, c, a, s);

@@ -36,7 +36,7 @@ PATH_SOURCES = {
     "smallg_mfma": ("k_smallg.hip", "k_smallg_rows.hip", "k_smallg_ring.hip", "k_smallg_ring3d.hip",
                     "smallg_common.h", "smallg_ring.h"),
     "igemm_mfma": "k_igemm.hip",
-    "ighalo_mfma": "k_ighalo.hip",
+    "ighalo_mfma": ("k_ighalo.hip", "k_ighalo_box.hip"),
 }
 SHARED = ("device_common.h", "gconv_internal.h")
 KERNEL_TAGS = {"generic": "generic", "depthwise": "depthwise", "smallg_mfma": "smallg",

@@ -302,6 +302,9 @@ IGEMM_CASES = [
     (2, "bf16", 1, 1, 64, 64, (1, 30, 29), (1, 3, 3), 1, 1, 1, True),       # row blocks, ragged last block
     (2, "bf16", 1, 1, 64, 128, (1, 3, 300), (1, 3, 3), 1, 1, 1, False),     # column blocks (Wo > 224)
     (2, "f16", 2, 1, 256, 256, (1, 6, 6), (1, 3, 3), 1, 1, 1, True),        # 4 channel chunks, 2 channel blocks
+    (2, "f16", 70, 8, 64, 64, (1, 14, 14), (1, 3, 3), 1, 1, 1, True),       # 560 items: next box loads under the stores
+    (3, "bf16", 1, 2, 128, 64, (5, 6, 7), (3, 3, 3), 1, 1, (2, 1, 1), True),  # depth dilation, one workgroup per CU
+    (2, "bf16", 3, 2, 128, 128, (1, 17, 15), (1, 3, 3), 2, 1, 1, False),    # stride 2, whole-box variant
 ]
 
 
