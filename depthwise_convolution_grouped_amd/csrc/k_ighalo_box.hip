@@ -270,10 +270,11 @@ __global__ __launch_bounds__(kBlock, 2) void kernel(Params q, const T *__restric
                 __builtin_amdgcn_sched_barrier(0);
                 const int ncc = cc + NB < CC ? cc + NB : cc + NB - CC;
                 const bool nxt_tap = cc + NB >= CC;
-                if (!nxt_tap || more) {
+                // unconditional (past the last tap it reloads the last tap's
+                // weights, in bounds and unused): a branch here would make
+                // the compiler's wait counts at the join conservative
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) bq[b][nt] = wload(nxt_tap ? tap + 1 : tap, ncc, nt);
-                }
+                for (int nt = 0; nt < NT; ++nt) bq[b][nt] = wload(nxt_tap && more ? tap + 1 : tap, ncc, nt);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (++kx == q.X) {
@@ -392,6 +393,7 @@ bool configure(const Problem &p, Config &c)
             const long long lds = HI * 1024 > stage ? HI * 1024 : stage;
             if (lds > kMaxLds) continue;
             const int per_cu = lds <= kMaxLds / 2 ? 2 : 1;
+            // the two-wave kernel needs two workgroups per CU to fill its SIMDs
             const long long slots = (long long)kCUs * per_cu;
             const long long nrb = (p.Ho + RH - 1) / RH, ncb = (p.Wo + CW - 1) / CW;
             const long long items = (long long)p.G * c.nnb * p.N * p.Do * nrb * ncb;
@@ -423,8 +425,7 @@ bool configure(const Problem &p, Config &c)
     return true;
 }
 
-template <typename T, int WM, int NT, int TPW, int CC>
-hipError_t go4(const Problem &p, const Config &c, const Args &a, hipStream_t s)
+Params params(const Problem &p, const Config &c)
 {
     Params q;
     q.N = p.N; q.G = p.G; q.Cpg = p.Cpg; q.Kpg = p.Kpg; q.C = p.C(); q.K = p.K();
@@ -437,6 +438,13 @@ hipError_t go4(const Problem &p, const Config &c, const Args &a, hipStream_t s)
     q.items = c.items; q.taps = p.taps(); q.xcd_split = c.xcd_split;
     q.x_bytes = (unsigned)((long long)p.N * p.D * p.H * p.W * p.C() * 2);
     q.w_bytes = (unsigned)((long long)p.K() * p.taps() * p.Cpg * 2);
+    return q;
+}
+
+template <typename T, int WM, int NT, int TPW, int CC>
+hipError_t go4(const Problem &p, const Config &c, const Args &a, hipStream_t s)
+{
+    Params q = params(p, c);
     auto k = kernel<T, WM, NT, TPW, CC>;
     static bool lds_set = false;
     if (!lds_set) {
