@@ -55,12 +55,25 @@ struct Params {
     int D, H, W, Do, Ho, Wo, Y, X;
     int sd, sh, sw, pd, ph, pw, dd, dh, dw;
     int RH, CW, nrb, ncb, nnb;   // item = RH x CW output pixels of one plane; blocks per axis
+    int VW;                      // pixels per output row in the tile order (CW, or BW: see below)
     int BH, BW, BP;              // input box rows, columns, pixels (BD planes)
     int HI;                      // box load instructions (64 lanes x 16 bytes each)
     int MT;                      // M tiles of 16 pixels per item
     int items, taps, xcd_split;
     unsigned x_bytes, w_bytes;
+    float rplane, rbw;           // 1 / (BH BW), 1 / BW
 };
+
+// n / d for 0 <= n < 2^22 from a float reciprocal of d: the estimate is off
+// by at most one, which the remainder test corrects.
+__device__ __forceinline__ int fdiv(int n, int d, float rd)
+{
+    int v = (int)((float)n * rd);
+    const int r = n - v * d;
+    v += r >= d ? 1 : 0;
+    v -= r < 0 ? 1 : 0;
+    return v;
+}
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, unsigned bytes)
 {
@@ -174,7 +187,7 @@ __global__ __launch_bounds__(kBlock, 2) void kernel(Params q, const T *__restric
 #pragma unroll
     for (int tm = 0; tm < TPW; ++tm) {
         const int m = (tbase + tm) * 16 + l16;
-        const int lr = m / q.CW, lc = m - lr * q.CW;
+        const int lr = m / q.VW, lc = m - lr * q.VW;
         const bool live = tm < my_tiles && lr < q.RH;
         const int P = live ? lr * q.sh * q.BW + lc * q.sw : 0;
         aoff[tm] = P * PS + kq * 16;
@@ -192,11 +205,13 @@ __global__ __launch_bounds__(kBlock, 2) void kernel(Params q, const T *__restric
         const int ix0 = I.cb * q.CW * q.sw - q.pw;
         const int plane = q.BH * q.BW;
         const int cg = I.g * q.Cpg;
-        for (int k = wave; k < q.HI; k += kWaves) {
+        // wave-uniform loop (scalar branch); the box-pixel divisions use
+        // host-computed reciprocals and one exact correction step
+        for (int k = __builtin_amdgcn_readfirstlane(wave); k < q.HI; k += kWaves) {
             const int L = k * 64 + lane;
             const int p = L / SPP, j = L - p * SPP;
-            const int bz = p / plane, r = p - bz * plane;
-            const int by = r / q.BW, bx = r - by * q.BW;
+            const int bz = fdiv(p, plane, q.rplane), r = p - bz * plane;
+            const int by = fdiv(r, q.BW, q.rbw), bx = r - by * q.BW;
             const int iz = iz0 + bz, iy = iy0 + by, ix = ix0 + bx;
             const bool in = j < SPP - 1 && p < q.BP && (unsigned)iz < (unsigned)q.D &&
                             (unsigned)iy < (unsigned)q.H && (unsigned)ix < (unsigned)q.W;
@@ -238,45 +253,27 @@ __global__ __launch_bounds__(kBlock, 2) void kernel(Params q, const T *__restric
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
 
-        int kx = 0, ky = 0, kz = 0;
-        for (int tap = 0; tap < q.taps; ++tap) {
-            const int tofs = ((kz * q.dd * q.BH + ky * q.dh) * q.BW + kx * q.dw) * PS;
-            const bool more = tap + 1 < q.taps;
+        // Pixel fragments go in runs of R <= 7 tiles (bounded registers),
+        // double-buffered: the next run's LDS reads are issued before this
+        // run's MFMAs, so they are in flight while the matrix pipe works.
+        // Within a step the order reads, MFMAs, then the weight loads for
+        // a later step is kept (loads return in order: a load issued before
+        // these MFMAs would have to be back before they could start).
+        constexpr int R = TPW < 7 ? TPW : 7;
+        constexpr int NR = (TPW + R - 1) / R;       // runs per step; CC * NR is even
+        V af[2][R];
+        auto read_run = [&](V *dst, int tofs_, int cc_, int r_) {
 #pragma unroll
-            for (int cc = 0; cc < CC; ++cc) {
-                const int b = cc % NB;
-                // pixel fragments in runs of at most 7 tiles (bounded
-                // registers); the order reads, MFMAs, next loads is kept:
-                // loads return in order, so a load issued before these
-                // MFMAs would have to be back before they could start
-#pragma unroll
-                for (int t0 = 0; t0 < TPW; t0 += 7) {
-                    constexpr int R = TPW < 7 ? TPW : 7;
-                    V af[R];
-#pragma unroll
-                    for (int i = 0; i < R; ++i) {
-                        const uint4 raw = *reinterpret_cast<const uint4 *>(lds_c + aoff[t0 + i] + tofs + cc * 64);
-                        af[i] = *reinterpret_cast<const V *>(&raw);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                    for (int i = 0; i < R; ++i)
-#pragma unroll
-                        for (int nt = 0; nt < NT; ++nt)
-                            acc[t0 + i][nt] = Mfma<T>::run(bq[b][nt], af[i], acc[t0 + i][nt]);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                // step s + NB: same tap while cc + NB < CC, else the next tap
-                __builtin_amdgcn_sched_barrier(0);
-                const int ncc = cc + NB < CC ? cc + NB : cc + NB - CC;
-                const bool nxt_tap = cc + NB >= CC;
-                // unconditional (past the last tap it reloads the last tap's
-                // weights, in bounds and unused): a branch here would make
-                // the compiler's wait counts at the join conservative
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) bq[b][nt] = wload(nxt_tap && more ? tap + 1 : tap, ncc, nt);
-                __builtin_amdgcn_sched_barrier(0);
+            for (int i = 0; i < R; ++i) {
+                const uint4 raw = *reinterpret_cast<const uint4 *>(lds_c + aoff[r_ * R + i] + tofs_ + cc_ * 64);
+                dst[i] = *reinterpret_cast<const V *>(&raw);
             }
+        };
+        int kx = 0, ky = 0, kz = 0;
+        int tofs = 0;                                // tap 0 reads the box at offset 0
+        read_run(af[0], 0, 0, 0);
+        for (int tap = 0; tap < q.taps; ++tap) {
+            const bool more = tap + 1 < q.taps;
             if (++kx == q.X) {
                 kx = 0;
                 if (++ky == q.Y) {
@@ -284,6 +281,37 @@ __global__ __launch_bounds__(kBlock, 2) void kernel(Params q, const T *__restric
                     ++kz;
                 }
             }
+            // the next tap's offset (the last tap re-reads its own: in
+            // bounds, unused; a branch would make the wait counts at the
+            // join conservative)
+            const int tofs_n = more ? ((kz * q.dd * q.BH + ky * q.dh) * q.BW + kx * q.dw) * PS : tofs;
+#pragma unroll
+            for (int cc = 0; cc < CC; ++cc) {
+                const int b = cc % NB;
+#pragma unroll
+                for (int r = 0; r < NR; ++r) {
+                    const int cur = (cc * NR + r) & 1;
+                    if (r + 1 < NR) read_run(af[cur ^ 1], tofs, cc, r + 1);
+                    else if (cc + 1 < CC) read_run(af[cur ^ 1], tofs, cc + 1, 0);
+                    else read_run(af[cur ^ 1], tofs_n, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int i = 0; i < R; ++i)
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt)
+                            acc[r * R + i][nt] = Mfma<T>::run(bq[b][nt], af[cur][i], acc[r * R + i][nt]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                // step s + NB: same tap while cc + NB < CC, else the next tap
+                // (unconditional: past the last tap it reloads the last
+                // tap's weights, in bounds and unused)
+                const int ncc = cc + NB < CC ? cc + NB : cc + NB - CC;
+                const bool nxt_tap = cc + NB >= CC;
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) bq[b][nt] = wload(nxt_tap && more ? tap + 1 : tap, ncc, nt);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            tofs = tofs_n;
         }
 
         // The results leave through LDS (the box is dead once every wave is
@@ -324,12 +352,12 @@ __global__ __launch_bounds__(kBlock, 2) void kernel(Params q, const T *__restric
             constexpr int PPP = kBlock / CPP;                 // pixels per pass
             const int ck = t % CPP;
             const int oh0 = I.rb * q.RH, ow0 = I.cb * q.CW;
-            const int M = q.RH * q.CW;
+            const int M = q.RH * q.VW;
             const size_t plane = (size_t)(I.n * q.Do + I.od) * q.Ho;
             for (int m = t / CPP; m < M; m += PPP) {
-                const int lr = m / q.CW, lc = m - lr * q.CW;
+                const int lr = m / q.VW, lc = m - lr * q.VW;
                 const int oh = oh0 + lr, ow = ow0 + lc;
-                if (oh < q.Ho && ow < q.Wo) {
+                if (lc < q.CW && oh < q.Ho && ow < q.Wo) {
                     typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
                     const u32x4 v = *reinterpret_cast<const u32x4 *>(lds_c + m * OP + ck * 16);
                     T *dst = y + ((plane + oh) * q.Wo + ow) * q.K + kb + ck * 8;
@@ -347,7 +375,7 @@ __global__ __launch_bounds__(kBlock, 2) void kernel(Params q, const T *__restric
 
 struct Config {
     int WM, NT, TPW, CC;
-    int RH, CW, nrb, ncb, nnb;
+    int RH, CW, nrb, ncb, nnb, VW;
     int BH, BW, BP, HI, MT;
     int items, grid, xcd_split, lds;
 };
@@ -379,18 +407,32 @@ bool configure(const Problem &p, Config &c)
         int RH = max_tiles * 16 / CW;
         if (RH > p.Ho) RH = p.Ho;
         for (; RH >= 1; --RH) {
-            const int M = RH * CW;
-            const int MT = (M + 15) / 16;
-            if (MT > max_tiles) continue;
             const long long BH = (long long)(RH - 1) * p.sh + (long long)(p.Y - 1) * p.dh + 1;
             const long long BW = (long long)(CW - 1) * p.sw + (long long)(p.X - 1) * p.dw + 1;
+            if (BW > max_tiles * 16) continue;
+            // At stride 1 the tiles run over whole box rows (VW = BW pixels
+            // per row, the last BW - CW of them computed and dropped): then
+            // the 16 pixels of a tile are 16 consecutive box pixels, whose
+            // rows (PS = 17 x 16 bytes apart) start in 16 distinct 16-byte
+            // bank groups.  Over output rows only, a tile straddling a row
+            // end skips the halo pixels and two of its lanes share a bank
+            // group with two others (measured: LDS bank conflicts were
+            // about half of the LDS cycles).
+            const int VW = p.sw == 1 ? (int)BW : CW;
+            const int M = RH * VW;
+            const int MT = (M + 15) / 16;
+            if (MT > max_tiles) continue;
             const long long BP = BD * BH * BW;
             const long long slots_needed = BP * (c.CC * 4 + 1);
             const long long HI = (slots_needed + 63) / 64;
             // the box (whole load instructions, >= BP * PS), and the staged
             // output rows, which reuse it
             const long long stage = ((long long)MT * 16 * (BN * 2 + 16) + 1023) / 1024 * 1024;
-            const long long lds = HI * 1024 > stage ? HI * 1024 : stage;
+            // the dropped columns of the last rows read up to (X-1) dw
+            // pixels past the box
+            long long lds = HI * 1024 > stage ? HI * 1024 : stage;
+            const long long reach = (BP + (long long)(p.X - 1) * p.dw) * (c.CC * 4 + 1) * 16;
+            if (reach > lds) lds = (reach + 1023) / 1024 * 1024;
             if (lds > kMaxLds) continue;
             const int per_cu = lds <= kMaxLds / 2 ? 2 : 1;
             // the two-wave kernel needs two workgroups per CU to fill its SIMDs
@@ -409,12 +451,12 @@ bool configure(const Problem &p, Config &c)
             // little of the LDS and load latency (measured about 1.3x)
             const double t_mfma = (double)rounds * per_cu * tpw * (per_cu == 1 ? 1.3 : 1.0);
             const double useful = (double)p.N * p.Do * p.Ho * p.Wo * p.G * c.nnb / (double)kCUs;
-            const double box_over = (double)BP / (M * (double)p.sh * p.sw);
+            const double box_over = (double)BP / ((double)RH * CW * p.sh * p.sw);
             const double score = useful / t_mfma / (0.9 + 0.1 * box_over);
             if (!found || score > best) {
                 found = true;
                 best = score;
-                c.RH = RH; c.CW = CW; c.nrb = (int)nrb; c.ncb = (int)ncb; c.TPW = tpw;
+                c.RH = RH; c.CW = CW; c.VW = VW; c.nrb = (int)nrb; c.ncb = (int)ncb; c.TPW = tpw;
                 c.BH = (int)BH; c.BW = (int)BW; c.BP = (int)BP; c.HI = (int)HI; c.MT = MT;
                 c.items = (int)items; c.grid = (int)grid; c.lds = (int)lds;
             }
@@ -433,11 +475,13 @@ Params params(const Problem &p, const Config &c)
     q.Y = p.Y; q.X = p.X;
     q.sd = p.sd; q.sh = p.sh; q.sw = p.sw; q.pd = p.pd; q.ph = p.ph; q.pw = p.pw;
     q.dd = p.dd; q.dh = p.dh; q.dw = p.dw;
-    q.RH = c.RH; q.CW = c.CW; q.nrb = c.nrb; q.ncb = c.ncb; q.nnb = c.nnb;
+    q.RH = c.RH; q.CW = c.CW; q.VW = c.VW; q.nrb = c.nrb; q.ncb = c.ncb; q.nnb = c.nnb;
     q.BH = c.BH; q.BW = c.BW; q.BP = c.BP; q.HI = c.HI; q.MT = c.MT;
     q.items = c.items; q.taps = p.taps(); q.xcd_split = c.xcd_split;
     q.x_bytes = (unsigned)((long long)p.N * p.D * p.H * p.W * p.C() * 2);
     q.w_bytes = (unsigned)((long long)p.K() * p.taps() * p.Cpg * 2);
+    q.rplane = 1.0f / (float)(c.BH * c.BW);
+    q.rbw = 1.0f / (float)c.BW;
     return q;
 }
 
