@@ -309,8 +309,10 @@ def main():
         roof = {"bound": "hbm", "achieved": dom_cfg["gbs"], "peak": metrics.PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": dom_cfg["gbs"] / metrics.PEAK_HBM_GBS}
     else:
-        roof = {"bound": "mfma", "achieved": dom_cfg["tflops"], "peak": peak_tf,
-                "unit": "TFLOP/s", "frac": dom_cfg["tflops"] / peak_tf}
+        # fp32 runs on the vector ALUs (fp32 FMA, 256 FLOP/clk/CU x 256 CUs x
+        # 2.4 GHz = 157.3 TFLOP/s); half types on the matrix cores
+        roof = {"bound": "alu" if dp.dtype == "f32" else "mfma", "achieved": dom_cfg["tflops"],
+                "peak": peak_tf, "unit": "TFLOP/s", "frac": dom_cfg["tflops"] / peak_tf}
     roof["traffic"] = stored_traffic(dominant, dom_cfg["path"])
     roof["kernel"] = dom_cfg["path"]
     roof["workload"] = dominant
