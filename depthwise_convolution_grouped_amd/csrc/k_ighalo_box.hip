@@ -60,6 +60,7 @@ struct Params {
     int HI;                      // box load instructions (64 lanes x 16 bytes each)
     int MT;                      // M tiles of 16 pixels per item
     int items, taps, xcd_split;
+    int nch;                     // channel chunks per group (32 CC channels each), one box each
     unsigned x_bytes, w_bytes;
     float rplane, rbw;           // 1 / (BH BW), 1 / BW
 };
@@ -197,14 +198,15 @@ __global__ __launch_bounds__(kBlock, 2) void kernel(Params q, const T *__restric
     const unsigned woff_lane = (unsigned)(((nh * NT * 16 + l16) * kstride + kq * 8) * (int)sizeof(T));
     const unsigned wtile_b = (unsigned)(16 * kstride * (int)sizeof(T));   // N tile stride in bytes
 
-    // the box of item ii: direct-to-LDS loads, instruction k fills slots 64k .. 64k+63
-    auto issue_box = [&](int ii) {
+    // the box of item ii, channel chunk ch: direct-to-LDS loads, instruction
+    // k fills slots 64k .. 64k+63
+    auto issue_box = [&](int ii, int ch) {
         const Item I = decode(q, it0 + ii * itstep);
         const int iz0 = I.od * q.sd - q.pd;
         const int iy0 = I.rb * q.RH * q.sh - q.ph;
         const int ix0 = I.cb * q.CW * q.sw - q.pw;
         const int plane = q.BH * q.BW;
-        const int cg = I.g * q.Cpg;
+        const int cg = I.g * q.Cpg + ch * 32 * CC;
         // wave-uniform loop (scalar branch); the box-pixel divisions use
         // host-computed reciprocals and one exact correction step
         for (int k = __builtin_amdgcn_readfirstlane(wave); k < q.HI; k += kWaves) {
@@ -223,31 +225,39 @@ __global__ __launch_bounds__(kBlock, 2) void kernel(Params q, const T *__restric
         }
     };
 
-    issue_box(0);
+    issue_box(0, 0);
     for (int ii = 0; ii < nI; ++ii) {
         const Item I = decode(q, it0 + ii * itstep);
         // weights of this item's channel block: a wave-uniform byte offset
         // (soffset) plus this lane's row and channel slot (voffset)
         const int wg_b = (I.g * q.Kpg + I.nb * BN) * kstride * (int)sizeof(T);
+        int cho = 0;    // byte offset of the current channel chunk in a weight row's tap
         auto wload = [&](int tap, int cc, int nt) -> V {
-            const int so = wg_b + nt * (int)wtile_b + (tap * q.Cpg + cc * 32) * (int)sizeof(T);
+            const int so = wg_b + nt * (int)wtile_b + (tap * q.Cpg + cc * 32) * (int)sizeof(T) + cho;
             return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)woff_lane,
                                                                                __builtin_amdgcn_readfirstlane(so), 0));
         };
-        // weight fragments of two steps in flight: step s = (tap, cc) uses
-        // buffer cc & 1, which is refilled with step s + 2 after its MFMAs
+        f32x4 acc[TPW][NT];
+#pragma unroll
+        for (int a = 0; a < TPW; ++a)
+#pragma unroll
+            for (int b = 0; b < NT; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        for (int ch = 0; ch < q.nch; ++ch) {
+        if (ch > 0) {
+            // every wave is done with the previous chunk's box
+            __syncthreads();
+            issue_box(ii, ch);
+        }
+        cho = ch * 32 * CC * (int)sizeof(T);
+        // the weight fragments of one whole tap in flight: step (tap, cc)
+        // uses buffer cc, refilled with (tap + 1, cc) after its MFMAs
         constexpr int NB = CC;
         V bq[NB][NT];
 #pragma unroll
         for (int cc = 0; cc < NB; ++cc)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) bq[cc][nt] = wload(0, cc, nt);
-
-        f32x4 acc[TPW][NT];
-#pragma unroll
-        for (int a = 0; a < TPW; ++a)
-#pragma unroll
-            for (int b = 0; b < NT; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
         // the box is in once this wave's loads are back and every wave has passed here
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -313,6 +323,7 @@ __global__ __launch_bounds__(kBlock, 2) void kernel(Params q, const T *__restric
             }
             tofs = tofs_n;
         }
+        }   // channel chunks
 
         // The results leave through LDS (the box is dead once every wave is
         // past the loop): each lane drops its four channels (bias added,
@@ -367,28 +378,24 @@ __global__ __launch_bounds__(kBlock, 2) void kernel(Params q, const T *__restric
         }
         // every wave has read its staged results: the next box may load
         __syncthreads();
-        if (ii + 1 < nI) issue_box(ii + 1);
+        if (ii + 1 < nI) issue_box(ii + 1, 0);
     }
 }
 
 // ----------------------------------------------------------------- host side
 
 struct Config {
-    int WM, NT, TPW, CC;
+    int WM, NT, TPW, CC, nch;
     int RH, CW, nrb, ncb, nnb, VW;
     int BH, BW, BP, HI, MT;
     int items, grid, xcd_split, lds;
 };
 
-bool configure(const Problem &p, Config &c)
+// The item shape for boxes of 32 CC channels (Cpg / (32 CC) chunks).
+bool search(const Problem &p, Config &c, int CC)
 {
-    if (p.dtype != GCONV_F16 && p.dtype != GCONV_BF16) return false;
-    if (p.Cpg != 64 && p.Cpg != 128) return false;
-    if (p.Kpg % 64 != 0) return false;
-    const long long xb = (long long)p.N * p.D * p.H * p.W * p.C() * 2;
-    const long long wb = (long long)p.K() * p.taps() * p.Cpg * 2;
-    if (xb >= (1LL << 31) || wb >= (1LL << 31)) return false;
-    c.CC = p.Cpg / 32;
+    c.CC = CC;
+    c.nch = p.Cpg / (32 * CC);
     // Channel blocks of 128 are split over the four waves (each wave takes
     // every pixel tile of the item and two N tiles, so no two waves of a
     // workgroup load the same weights); blocks of 64 over two waves.
@@ -409,7 +416,6 @@ bool configure(const Problem &p, Config &c)
         for (; RH >= 1; --RH) {
             const long long BH = (long long)(RH - 1) * p.sh + (long long)(p.Y - 1) * p.dh + 1;
             const long long BW = (long long)(CW - 1) * p.sw + (long long)(p.X - 1) * p.dw + 1;
-            if (BW > max_tiles * 16) continue;
             // At stride 1 the tiles run over whole box rows (VW = BW pixels
             // per row, the last BW - CW of them computed and dropped): then
             // the 16 pixels of a tile are 16 consecutive box pixels, whose
@@ -418,7 +424,7 @@ bool configure(const Problem &p, Config &c)
             // end skips the halo pixels and two of its lanes share a bank
             // group with two others (measured: LDS bank conflicts were
             // about half of the LDS cycles).
-            const int VW = p.sw == 1 ? (int)BW : CW;
+            const int VW = p.sw == 1 && RH * BW <= max_tiles * 16 ? (int)BW : CW;
             const int M = RH * VW;
             const int MT = (M + 15) / 16;
             if (MT > max_tiles) continue;
@@ -467,6 +473,19 @@ bool configure(const Problem &p, Config &c)
     return true;
 }
 
+bool configure(const Problem &p, Config &c)
+{
+    if (p.dtype != GCONV_F16 && p.dtype != GCONV_BF16) return false;
+    if (p.Cpg % 64 != 0 || p.Kpg % 64 != 0) return false;
+    const long long xb = (long long)p.N * p.D * p.H * p.W * p.C() * 2;
+    const long long wb = (long long)p.K() * p.taps() * p.Cpg * 2;
+    if (xb >= (1LL << 31) || wb >= (1LL << 31)) return false;
+    // the whole Cpg in one box where it fits, else chunks of 128, else of 64
+    if ((p.Cpg == 64 || p.Cpg == 128) && search(p, c, p.Cpg / 32)) return true;
+    if (p.Cpg % 128 == 0 && p.Cpg > 128 && search(p, c, 4)) return true;
+    return p.Cpg > 64 && search(p, c, 2);
+}
+
 Params params(const Problem &p, const Config &c)
 {
     Params q;
@@ -477,7 +496,7 @@ Params params(const Problem &p, const Config &c)
     q.dd = p.dd; q.dh = p.dh; q.dw = p.dw;
     q.RH = c.RH; q.CW = c.CW; q.VW = c.VW; q.nrb = c.nrb; q.ncb = c.ncb; q.nnb = c.nnb;
     q.BH = c.BH; q.BW = c.BW; q.BP = c.BP; q.HI = c.HI; q.MT = c.MT;
-    q.items = c.items; q.taps = p.taps(); q.xcd_split = c.xcd_split;
+    q.items = c.items; q.taps = p.taps(); q.xcd_split = c.xcd_split; q.nch = c.nch;
     q.x_bytes = (unsigned)((long long)p.N * p.D * p.H * p.W * p.C() * 2);
     q.w_bytes = (unsigned)((long long)p.K() * p.taps() * p.Cpg * 2);
     q.rplane = 1.0f / (float)(c.BH * c.BW);

@@ -305,6 +305,9 @@ IGEMM_CASES = [
     (2, "f16", 70, 8, 64, 64, (1, 14, 14), (1, 3, 3), 1, 1, 1, True),       # 560 items: next box loads under the stores
     (3, "bf16", 1, 2, 128, 64, (5, 6, 7), (3, 3, 3), 1, 1, (2, 1, 1), True),  # depth dilation, one workgroup per CU
     (2, "bf16", 3, 2, 128, 128, (1, 17, 15), (1, 3, 3), 2, 1, 1, False),    # stride 2, whole-box variant
+    (2, "bf16", 1, 2, 192, 64, (1, 9, 10), (1, 3, 3), 1, 1, 1, True),       # three 64-channel box chunks
+    (3, "f16", 1, 1, 256, 128, (3, 5, 6), (3, 3, 3), 1, 1, 1, True),        # two 128-channel chunks, 3D
+    (2, "bf16", 2, 4, 128, 128, (1, 14, 14), (1, 3, 3), 1, 2, 2, True),     # dilation 2: two 64-channel chunks
 ]
 
 
