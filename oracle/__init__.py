@@ -1,4 +1,4 @@
-"""Plain CPU oracle for grouped / depthwise convolution forward.
+"""Plain CPU oracle for grouped / depthwise convolution forward and backward data.
 
 TEST INFRASTRUCTURE.  Only the test suite, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package.  The product path
@@ -12,6 +12,7 @@ ctypes and marshals numpy arrays:
 
 * ``conv_fwd``        -- every output element plus its error scale
 * ``conv_fwd_points`` -- selected output elements (full-size spot checks)
+* ``conv_bwd_data``   -- backward data: the gradient w.r.t. x from dy and w
 * ``out_extent``      -- output length along one axis
 
 Arrays use the oracle's layouts: x ``[N][D][H][W][G][Cpg]``,
@@ -70,6 +71,8 @@ def bind(path: str):
     lib.gref_conv_fwd_points.argtypes = [i64, i64, i64, i64, p64, p64, p64, p64, p64,
                                          pd, pd, pd, p64, i64, pd, pd]
     lib.gref_conv_fwd_points.restype = ctypes.c_int
+    lib.gref_conv_bwd_data.argtypes = [i64, i64, i64, i64, p64, p64, p64, p64, p64, pd, pd, pd, pd]
+    lib.gref_conv_bwd_data.restype = ctypes.c_int
     lib.gref_num_threads.argtypes = []
     lib.gref_num_threads.restype = ctypes.c_int
     return lib
@@ -158,6 +161,45 @@ def conv_fwd_points(x, w, bias, groups, stride, pad, dil, flat_idx):
     if rc != 0:
         raise ValueError("oracle rejected the problem or an index")
     return yp, sp
+
+
+def conv_bwd_data(dy, w, groups, in_spatial, stride, pad, dil, lib=None):
+    """Backward data (the gradient w.r.t. x), fp64.  Returns (dx, scale), both N,[D,]H,W,C.
+
+    dy is N[Do]HoWoK, w K[Z]YXCpg; in_spatial gives the input extents ((H, W) or
+    (D, H, W)), which a strided forward does not determine from dy.
+    """
+    lib = lib or _load()
+    dy = np.ascontiguousarray(dy, dtype=np.float64)
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    spatial3 = dy.ndim == 5
+    if dy.ndim == 4:
+        dy = dy[:, None]
+    if w.ndim == 4:
+        w = w[:, None]
+    if dy.ndim != 5 or w.ndim != 5:
+        raise ValueError("dy must be N[Do]HoWoK and w K[Z]YXCpg")
+    N, K = dy.shape[0], dy.shape[4]
+    G = int(groups)
+    Cpg = w.shape[4]
+    if G <= 0 or K % G or w.shape[0] != K:
+        raise ValueError("inconsistent channels")
+    C = G * Cpg
+    in_ = _triple(in_spatial, 1)
+    d = dict(in_=in_, filt=_triple(w.shape[1:4], 1), stride=_triple(stride, 1),
+             pad=_triple(pad, 0), dil=_triple(dil, 1))
+    outs = _outs(d, lib)
+    if tuple(outs) != tuple(dy.shape[1:4]):
+        raise ValueError("dy extents %r do not match the forward output %r" % (dy.shape[1:4], tuple(outs)))
+    dx = np.empty((N, in_[0], in_[1], in_[2], C), dtype=np.float64)
+    s = np.empty_like(dx)
+    rc = lib.gref_conv_bwd_data(N, G, C, K, in_, d["filt"], d["stride"], d["pad"], d["dil"],
+                                _dptr(dy), _dptr(w), _dptr(dx), _dptr(s))
+    if rc != 0:
+        raise ValueError("oracle rejected the problem")
+    if not spatial3:
+        dx, s = dx[:, 0], s[:, 0]
+    return dx, s
 
 
 def num_threads() -> int:

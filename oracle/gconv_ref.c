@@ -1,5 +1,6 @@
 /*
- * gconv_ref.c -- plain CPU oracle for grouped / depthwise convolution forward.
+ * gconv_ref.c -- plain CPU oracle for grouped / depthwise convolution forward
+ * and backward data.
  *
  * TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the
  * benchmark's CPU-baseline leg may load or call this library.  The product
@@ -172,6 +173,82 @@ int gref_conv_fwd_points(int64_t N, int64_t G, int64_t C, int64_t K,
         int64_t n = e;
         one_output(G, Cpg, Kpg, in, filt, stride, pad, dil, x, w, bias,
                    n, od, oh, ow, g, k, &y_out[i], &s_out[i]);
+    }
+    return 0;
+}
+
+/*
+ * Backward data: the gradient of a loss with respect to x, given its
+ * gradient dy with respect to y and the weights w (the backward-data variant
+ * the CK grouped_conv tile-engine README lists next to forward, and whose
+ * runner takes dY and W in the Python examples README, Runner argument
+ * contract).  It is the adjoint of the forward map above: every forward term
+ * x[n,id,ih,iw,g,c] * w[g,k,z,y,x,c] feeds y[n,od,oh,ow,g,k] with
+ * id = od*stride - pad + z*dil (and likewise in h, w), so
+ *
+ *   dx[n,id,ih,iw,g,c] = sum over (z, y, x, k) with od = (id + pad - z*dil) / stride
+ *                        an integer in [0, Do) (likewise oh, ow) of
+ *                        dy[n,od,oh,ow,g,k] * w[g,k,z,y,x,c].
+ *
+ * Layouts: dy [N][Do][Ho][Wo][G][Kpg], w [G][Kpg][Z][Y][X][Cpg],
+ * dx [N][D][H][W][G][Cpg]; in[] gives (D, H, W), which a strided forward does
+ * not determine from dy.  scale receives sum |dy*w| over the terms summed.
+ * Returns 0, or -1 on inconsistent sizes.
+ */
+int gref_conv_bwd_data(int64_t N, int64_t G, int64_t C, int64_t K,
+                       const int64_t in[3], const int64_t filt[3],
+                       const int64_t stride[3], const int64_t pad[3],
+                       const int64_t dil[3],
+                       const double *dy, const double *w, double *dx, double *scale)
+{
+    if (N <= 0 || G <= 0 || C <= 0 || K <= 0 || C % G != 0 || K % G != 0)
+        return -1;
+    const int64_t Cpg = C / G, Kpg = K / G;
+    int64_t out[3];
+    for (int a = 0; a < 3; ++a) {
+        out[a] = gref_out_extent(in[a], filt[a], stride[a], pad[a], dil[a]);
+        if (out[a] <= 0) return -1;
+    }
+    const int64_t D = in[0], H = in[1], W = in[2];
+    const int64_t Z = filt[0], Y = filt[1], X = filt[2];
+    const int64_t Do = out[0], Ho = out[1], Wo = out[2];
+    const int64_t rows = N * D * H;
+
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < rows; ++r) {
+        const int64_t ih = r % H;
+        const int64_t id = (r / H) % D;
+        const int64_t n = r / (H * D);
+        for (int64_t iw = 0; iw < W; ++iw)
+            for (int64_t g = 0; g < G; ++g)
+                for (int64_t c = 0; c < Cpg; ++c) {
+                    double acc = 0.0, s = 0.0;
+                    for (int64_t z = 0; z < Z; ++z) {
+                        const int64_t td = id + pad[0] - z * dil[0];
+                        if (td < 0 || td % stride[0] != 0 || td / stride[0] >= Do) continue;
+                        const int64_t od = td / stride[0];
+                        for (int64_t yy = 0; yy < Y; ++yy) {
+                            const int64_t th = ih + pad[1] - yy * dil[1];
+                            if (th < 0 || th % stride[1] != 0 || th / stride[1] >= Ho) continue;
+                            const int64_t oh = th / stride[1];
+                            for (int64_t xx = 0; xx < X; ++xx) {
+                                const int64_t tw = iw + pad[2] - xx * dil[2];
+                                if (tw < 0 || tw % stride[2] != 0 || tw / stride[2] >= Wo) continue;
+                                const int64_t ow = tw / stride[2];
+                                for (int64_t k = 0; k < Kpg; ++k) {
+                                    const int64_t yi = ((((n * Do + od) * Ho + oh) * Wo + ow) * G + g) * Kpg + k;
+                                    const int64_t wi = ((((g * Kpg + k) * Z + z) * Y + yy) * X + xx) * Cpg + c;
+                                    const double t = dy[yi] * w[wi];
+                                    acc += t;
+                                    s += fabs(t);
+                                }
+                            }
+                        }
+                    }
+                    const int64_t xi = ((((n * D + id) * H + ih) * W + iw) * G + g) * Cpg + c;
+                    dx[xi] = acc;
+                    scale[xi] = s;
+                }
     }
     return 0;
 }
