@@ -172,6 +172,55 @@ int run(const gconv_desc *d, int path, const void *x, const void *w, const void 
     return GCONV_OK;
 }
 
+// Backward data at stride 1 is a forward convolution of dy (the input, with
+// C' = K channels) with the flipped, C/K-exchanged weights (K' = C) under
+// padding dil (k - 1) - pad, which must not be negative.
+bool bwd_as_forward(const gconv_desc *d)
+{
+    for (int a = 0; a < 3; ++a)
+        if (d->stride[a] != 1 || d->dil[a] * (d->filt[a] - 1) - d->pad[a] < 0) return false;
+    return true;
+}
+
+gconv_desc bwd_forward_desc(const gconv_desc *d, const int64_t out[3])
+{
+    gconv_desc t = *d;
+    t.C = d->K;
+    t.K = d->C;
+    for (int a = 0; a < 3; ++a) {
+        t.in[a] = out[a];
+        t.stride[a] = 1;
+        t.pad[a] = d->dil[a] * (d->filt[a] - 1) - d->pad[a];
+    }
+    return t;
+}
+
+size_t weight_bytes(const gconv_desc *d)
+{
+    return (size_t)d->K * (size_t)d->filt[0] * (size_t)d->filt[1] * (size_t)d->filt[2] *
+           (size_t)(d->C / d->G) * (size_t)elem_size(d->dtype);
+}
+
+int run_bwd_data(const gconv_desc *d, const void *dy, const void *w, void *dx, void *ws,
+                 size_t ws_bytes, bool direct, void *stream)
+{
+    int64_t out[3];
+    int rc = check_desc(d, out);
+    if (rc != GCONV_OK) return rc;
+    if (!dy || !w || !dx) return GCONV_ERR_NULL_PTR;
+    const uintptr_t es = (uintptr_t)elem_size(d->dtype);
+    if (!aligned(dy, es) || !aligned(w, es) || !aligned(dx, es)) return GCONV_ERR_MISALIGNED;
+    const Problem p = to_problem(d, out);
+    hipStream_t s = (hipStream_t)stream;
+    if (!direct && bwd_as_forward(d) && ws && ws_bytes >= weight_bytes(d) && aligned(ws, 16)) {
+        if (bwd::launch_flip(p, w, ws, s) != hipSuccess) return GCONV_ERR_LAUNCH;
+        const gconv_desc t = bwd_forward_desc(d, out);
+        return run(&t, GCONV_PATH_AUTO, dy, ws, nullptr, dx, stream);
+    }
+    if (bwd::launch_direct(p, dy, w, dx, s) != hipSuccess) return GCONV_ERR_LAUNCH;
+    return GCONV_OK;
+}
+
 }  // namespace
 }  // namespace gconv
 
@@ -241,6 +290,28 @@ GCONV_API int gconv_fwd_timed(const gconv_desc *d, int path, const void *x, cons
                               void *ev_stop)
 {
     return run(d, path, x, w, bias, y, stream, ev_start, ev_stop);
+}
+
+GCONV_API int gconv_bwd_data_workspace(const gconv_desc *d, size_t *bytes)
+{
+    if (!bytes) return GCONV_ERR_NULL_PTR;
+    int64_t out[3];
+    int rc = check_desc(d, out);
+    if (rc != GCONV_OK) return rc;
+    *bytes = bwd_as_forward(d) ? weight_bytes(d) : 0;
+    return GCONV_OK;
+}
+
+GCONV_API int gconv_bwd_data(const gconv_desc *d, const void *dy, const void *w, void *dx,
+                             void *workspace, size_t workspace_bytes, void *stream)
+{
+    return run_bwd_data(d, dy, w, dx, workspace, workspace_bytes, false, stream);
+}
+
+GCONV_API int gconv_bwd_data_direct(const gconv_desc *d, const void *dy, const void *w, void *dx,
+                                    void *stream)
+{
+    return run_bwd_data(d, dy, w, dx, nullptr, 0, true, stream);
 }
 
 GCONV_API const char *gconv_status_str(int status)

@@ -86,6 +86,13 @@ gconv_plan plan(const Problem &p);
 hipError_t launch(const Problem &p, const Args &a, hipStream_t s);
 }
 
+// Backward data (k_bwd_data.hip).  `p` is the forward problem (its x extents
+// are dx's, its y extents dy's).
+namespace bwd {
+hipError_t launch_direct(const Problem &p, const void *dy, const void *w, void *dx, hipStream_t s);
+hipError_t launch_flip(const Problem &p, const void *w, void *wt, hipStream_t s);
+}
+
 inline int elem_size(int dtype) { return dtype == GCONV_F32 ? 4 : 2; }
 
 }  // namespace gconv

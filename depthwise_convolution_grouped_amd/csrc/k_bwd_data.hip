@@ -1,0 +1,146 @@
+// Backward data: dx, the gradient with respect to x, from dy and w.  It is
+// the second of the three grouped-convolution variants the CK grouped_conv
+// tile-engine README lists (forward, backward-data, backward-weight); the
+// CK Python examples README's runner for it takes dY and W (Runner argument
+// contract).  Layouts are the forward ones: dy [N][Do][Ho][Wo][G][Kpg],
+// w [G][Kpg][Z][Y][X][Cpg], dx [N][D][H][W][G][Cpg].
+//
+//   dx[n,i,g,c] = sum over taps t and k with o = (i + pad - t dil) / stride an
+//                 integer in [0, out) of dy[n,o,g,k] w[g,k,t,c]   (per axis)
+//
+// Two kernels live here:
+//   - a direct kernel for every shape: L consecutive threads own one dx
+//     element, walk the taps whose output coordinate is integral and in
+//     range, and split the Kpg output channels of the group between them
+//     (partial sums joined by lane exchanges), fp32 accumulation;
+//   - the weight transform of the stride-1 route: at stride 1, dx is the
+//     forward convolution of dy with the weights flipped in space and with
+//     C and K exchanged (wt[g][c][Z-1-z][Y-1-y][X-1-x][k] = w[g][k][z][y][x][c])
+//     under padding dil (k - 1) - pad, so the host runs this transform into
+//     a caller workspace and then the forward dispatcher.
+#include "device_common.h"
+#include "gconv_internal.h"
+
+namespace gconv {
+namespace bwd {
+namespace {
+
+constexpr int kBlock = 256;
+
+template <typename T, int L>
+__global__ __launch_bounds__(kBlock) void direct_kernel(Problem p, const T *__restrict__ dy,
+                                                        const T *__restrict__ w, T *__restrict__ dx,
+                                                        int total)
+{
+    const int tid = blockIdx.x * kBlock + threadIdx.x;
+    const int e = tid / L, part = tid - (tid / L) * L;
+    float acc = 0.f;
+    if (e < total) {
+        int r = e;
+        const int c = r % p.Cpg;  r /= p.Cpg;
+        const int g = r % p.G;    r /= p.G;
+        const int iw = r % p.W;   r /= p.W;
+        const int ih = r % p.H;   r /= p.H;
+        const int id = r % p.D;   r /= p.D;
+        const int n = r;
+        const int K = p.G * p.Kpg;
+        for (int z = 0; z < p.Z; ++z) {
+            const int td = id + p.pd - z * p.dd;
+            if (td < 0 || td % p.sd != 0 || td / p.sd >= p.Do) continue;
+            const int od = td / p.sd;
+            for (int yy = 0; yy < p.Y; ++yy) {
+                const int th = ih + p.ph - yy * p.dh;
+                if (th < 0 || th % p.sh != 0 || th / p.sh >= p.Ho) continue;
+                const int oh = th / p.sh;
+                for (int xx = 0; xx < p.X; ++xx) {
+                    const int tw = iw + p.pw - xx * p.dw;
+                    if (tw < 0 || tw % p.sw != 0 || tw / p.sw >= p.Wo) continue;
+                    const int ow = tw / p.sw;
+                    const T *dyp = dy + ((((n * p.Do + od) * p.Ho + oh) * p.Wo + ow) * K + g * p.Kpg);
+                    const T *wp = w + (((g * p.Kpg * p.Z + z) * p.Y + yy) * p.X + xx) * p.Cpg + c;
+                    const int kstep = p.Z * p.Y * p.X * p.Cpg;    // w elements between output channels
+                    for (int k = part; k < p.Kpg; k += L) acc = fmaf(to_f32(dyp[k]), to_f32(wp[k * kstep]), acc);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int m = L / 2; m >= 1; m /= 2) acc += __shfl_xor(acc, m);
+    if (e < total && part == 0) dx[e] = from_f32<T>(acc);
+}
+
+// wt[g][c][z][y][x][k] = w[g][k][Z-1-z][Y-1-y][X-1-x][c]; a copy of element
+// bits, one thread per element of wt
+template <typename U>
+__global__ __launch_bounds__(kBlock) void flip_kernel(Problem p, const U *__restrict__ w, U *__restrict__ wt,
+                                                      int total)
+{
+    const int f = blockIdx.x * kBlock + threadIdx.x;
+    if (f >= total) return;
+    int r = f;
+    const int k = r % p.Kpg;  r /= p.Kpg;
+    const int xx = r % p.X;   r /= p.X;
+    const int yy = r % p.Y;   r /= p.Y;
+    const int z = r % p.Z;    r /= p.Z;
+    const int c = r % p.Cpg;  r /= p.Cpg;
+    const int g = r;
+    const int src = ((((g * p.Kpg + k) * p.Z + (p.Z - 1 - z)) * p.Y + (p.Y - 1 - yy)) * p.X + (p.X - 1 - xx)) *
+                        p.Cpg + c;
+    wt[f] = w[src];
+}
+
+int lanes_for(const Problem &p, long long elems)
+{
+    int L = 1;
+    while (L < 16 && elems * L < 256LL * kBlock && 2 * L <= p.Kpg) L *= 2;
+    return L;
+}
+
+template <typename T, int L>
+hipError_t go2(const Problem &p, const void *dy, const void *w, void *dx, hipStream_t s)
+{
+    const long long elems = (long long)p.N * p.D * p.H * p.W * p.G * p.Cpg;
+    const int blocks = (int)((elems * L + kBlock - 1) / kBlock);
+    Args a{};
+    return enqueue(direct_kernel<T, L>, dim3(blocks), dim3(kBlock), 0, s, a, p, (const T *)dy,
+                   (const T *)w, (T *)dx, (int)elems);
+}
+
+template <typename T>
+hipError_t go(const Problem &p, const void *dy, const void *w, void *dx, hipStream_t s)
+{
+    const long long elems = (long long)p.N * p.D * p.H * p.W * p.G * p.Cpg;
+    switch (lanes_for(p, elems)) {
+    case 1: return go2<T, 1>(p, dy, w, dx, s);
+    case 2: return go2<T, 2>(p, dy, w, dx, s);
+    case 4: return go2<T, 4>(p, dy, w, dx, s);
+    case 8: return go2<T, 8>(p, dy, w, dx, s);
+    default: return go2<T, 16>(p, dy, w, dx, s);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_direct(const Problem &p, const void *dy, const void *w, void *dx, hipStream_t s)
+{
+    switch (p.dtype) {
+    case GCONV_F32: return go<float>(p, dy, w, dx, s);
+    case GCONV_F16: return go<_Float16>(p, dy, w, dx, s);
+    default: return go<__bf16>(p, dy, w, dx, s);
+    }
+}
+
+hipError_t launch_flip(const Problem &p, const void *w, void *wt, hipStream_t s)
+{
+    const long long total = (long long)p.G * p.Kpg * p.taps() * p.Cpg;
+    const int blocks = (int)((total + kBlock - 1) / kBlock);
+    Args a{};
+    if (elem_size(p.dtype) == 4)
+        return enqueue(flip_kernel<uint32_t>, dim3(blocks), dim3(kBlock), 0, s, a, p, (const uint32_t *)w,
+                       (uint32_t *)wt, (int)total);
+    return enqueue(flip_kernel<uint16_t>, dim3(blocks), dim3(kBlock), 0, s, a, p, (const uint16_t *)w,
+                   (uint16_t *)wt, (int)total);
+}
+
+}  // namespace bwd
+}  // namespace gconv

@@ -45,6 +45,7 @@ PATHS = {"generic": 0, "depthwise": 1, "smallg_mfma": 2, "igemm_mfma": 3, "ighal
 
 EXPORTS = ("gconv_validate", "gconv_out_dims", "gconv_select_path", "gconv_path_supported",
            "gconv_get_plan", "gconv_fwd", "gconv_fwd_path", "gconv_fwd_timed",
+           "gconv_bwd_data_workspace", "gconv_bwd_data", "gconv_bwd_data_direct",
            "gconv_status_str", "gconv_path_name", "gconv_abi_version")
 
 
@@ -100,6 +101,9 @@ def lib():
     L.gconv_fwd.argtypes = [pd, vp, vp, vp, vp, vp]
     L.gconv_fwd_path.argtypes = [pd, ctypes.c_int, vp, vp, vp, vp, vp]
     L.gconv_fwd_timed.argtypes = [pd, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp]
+    L.gconv_bwd_data_workspace.argtypes = [pd, ctypes.POINTER(ctypes.c_size_t)]
+    L.gconv_bwd_data.argtypes = [pd, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.gconv_bwd_data_direct.argtypes = [pd, vp, vp, vp, vp]
     L.gconv_status_str.argtypes = [ctypes.c_int]
     L.gconv_status_str.restype = ctypes.c_char_p
     L.gconv_path_name.argtypes = [ctypes.c_int]
@@ -107,6 +111,7 @@ def lib():
     L.gconv_abi_version.argtypes = []
     for name in ("gconv_validate", "gconv_out_dims", "gconv_select_path", "gconv_path_supported",
                  "gconv_get_plan", "gconv_fwd", "gconv_fwd_path", "gconv_fwd_timed",
+                 "gconv_bwd_data_workspace", "gconv_bwd_data", "gconv_bwd_data_direct",
                  "gconv_abi_version"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -186,6 +191,26 @@ def gconv_fwd_timed(d: gconv_desc, path: int, x: int, w: int, bias: Optional[int
                                  stream or None, ev_start or None, ev_stop or None)
 
 
+def gconv_bwd_data_workspace(d: gconv_desc) -> int:
+    """Workspace bytes gconv_bwd_data can use for the forward descriptor d."""
+    n = ctypes.c_size_t()
+    rc = lib().gconv_bwd_data_workspace(ctypes.byref(d), ctypes.byref(n))
+    if rc != GCONV_OK:
+        raise GconvError(rc, "gconv_bwd_data_workspace")
+    return int(n.value)
+
+
+def gconv_bwd_data(d: gconv_desc, dy: int, w: int, dx: int, workspace: Optional[int],
+                   workspace_bytes: int, stream: int = 0) -> int:
+    """Raw call with device addresses (ints); returns the status code."""
+    return lib().gconv_bwd_data(ctypes.byref(d), dy, w, dx, workspace or None, int(workspace_bytes),
+                                stream or None)
+
+
+def gconv_bwd_data_direct(d: gconv_desc, dy: int, w: int, dx: int, stream: int = 0) -> int:
+    return lib().gconv_bwd_data_direct(ctypes.byref(d), dy, w, dx, stream or None)
+
+
 def gconv_status_str(status: int) -> str:
     try:
         return lib().gconv_status_str(int(status)).decode()
@@ -242,4 +267,50 @@ def conv_fwd(x, w, bias=None, groups: int = 1, stride=None, pad=None, dil=None,
                         bias.data_ptr() if bias is not None else None, out.data_ptr(), s)
     if rc != GCONV_OK:
         raise GconvError(rc, "gconv_fwd")
+    return out
+
+
+def conv_bwd_data(dy, w, groups: int, in_spatial, stride=None, pad=None, dil=None, out=None,
+                  direct: bool = False, workspace=None, stream=None):
+    """Backward data on PyTorch device tensors: dx (N[D]HWC) from dy (N[Do]HoWoK) and w (K[Z]YXCpg).
+
+    in_spatial is dx's (H, W) or (D, H, W).  A workspace of
+    gconv_bwd_data_workspace bytes is allocated here unless one is passed
+    (a uint8 device tensor) or `direct` asks for the direct kernel.
+    """
+    import torch
+    nd = dy.dim() - 2
+    if nd not in (2, 3) or w.dim() != dy.dim():
+        raise ValueError("dy must be N[Do]HoWoK and w K[Z]YXCpg")
+    if not (dy.is_contiguous() and w.is_contiguous()):
+        raise ValueError("dy and w must be contiguous")
+    if w.dtype != dy.dtype:
+        raise TypeError("dy and w must share one dtype")
+    stride = stride or (1,) * nd
+    pad = pad or (0,) * nd
+    dil = dil or (1,) * nd
+    N, K = dy.shape[0], dy.shape[-1]
+    C = w.shape[-1] * groups
+    d = make_desc(nd, _torch_dtype_code(dy), N, groups, C, K, tuple(in_spatial),
+                  tuple(w.shape[1:-1]), stride, pad, dil)
+    o = gconv_out_dims(d)
+    if tuple(dy.shape[1:-1]) != (o if nd == 3 else o[1:]):
+        raise ValueError("dy's extents %r are not the forward output %r" % (tuple(dy.shape[1:-1]), o))
+    xshape = (N,) + tuple(in_spatial) + (C,)
+    if out is None:
+        out = torch.empty(xshape, dtype=dy.dtype, device=dy.device)
+    elif tuple(out.shape) != xshape or not out.is_contiguous() or out.dtype != dy.dtype:
+        raise ValueError("out must be a contiguous %s tensor of shape %s" % (dy.dtype, xshape))
+    s = stream if stream is not None else torch.cuda.current_stream(dy.device).cuda_stream
+    if direct:
+        rc = gconv_bwd_data_direct(d, dy.data_ptr(), w.data_ptr(), out.data_ptr(), s)
+    else:
+        need = gconv_bwd_data_workspace(d)
+        if workspace is None and need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dy.device)
+        ws_ptr = workspace.data_ptr() if workspace is not None else None
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        rc = gconv_bwd_data(d, dy.data_ptr(), w.data_ptr(), out.data_ptr(), ws_ptr, ws_bytes, s)
+    if rc != GCONV_OK:
+        raise GconvError(rc, "gconv_bwd_data")
     return out

@@ -215,6 +215,11 @@ def make_tensors(p: Problem, seed: int, x_dist=("normal", 1.0), w_dist=None,
                    to_storage(b, p.dtype) if b is not None else None)
 
 
+def make_array(shape, dtype: str, seed: int, dist=("normal", 1.0)) -> np.ndarray:
+    """A seeded storage array of any shape (e.g. an output gradient dy for backward data)."""
+    return to_storage(_draw(np.random.default_rng(seed), tuple(shape), dist), dtype)
+
+
 def workload_tensors(wl: Workload) -> Tensors:
     return make_tensors(wl.problem, wl.seed, wl.x_dist, wl.w_dist, wl.b_dist)
 

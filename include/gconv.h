@@ -154,6 +154,41 @@ int gconv_fwd_timed(const gconv_desc *d, int path, const void *x, const void *w,
                     const void *bias, void *y, void *stream, void *ev_start,
                     void *ev_stop);
 
+/* ---- Backward data ----------------------------------------------------
+ *
+ * dx, the gradient with respect to x, from dy (the gradient with respect to
+ * y) and w: the backward-data variant the CK grouped_conv tile-engine README
+ * lists next to forward (introduction), whose runner takes dY and W (CK
+ * Python examples README, Runner argument contract).  d is the FORWARD
+ * problem's descriptor: d->in gives dx's extents, the forward output extents
+ * (gconv_out_dims) dy's.  Layouts: dy [N][Do][Ho][Wo][G][Kpg],
+ * w [G][Kpg][Z][Y][X][Cpg], dx [N][D][H][W][G][Cpg], all device pointers
+ * aligned to the element size, dtype as d->dtype, fp32 accumulation, no bias.
+ *
+ *   dx[n,i,g,c] = sum over taps t and k with o = (i + pad - t*dil) / stride
+ *                 an integer in [0, out) of dy[n,o,g,k] * w[g,k,t,c]   (per axis)
+ */
+
+/* Bytes of device workspace gconv_bwd_data can use for d (0 when it has no
+ * use for any): at stride 1 with dil*(k-1) >= pad on every axis it is the
+ * size of w, and the call becomes a weight transform plus one forward
+ * launch on the fastest forward path. */
+int gconv_bwd_data_workspace(const gconv_desc *d, size_t *bytes);
+
+/* Backward data, asynchronous on `stream`.  `workspace` (device memory the
+ * caller owns, 16-byte aligned, may be NULL) of `workspace_bytes`: when it
+ * holds gconv_bwd_data_workspace bytes, two kernels run (the weight
+ * transform into the workspace, then the forward kernel); otherwise one
+ * direct kernel runs.  The workspace may be reused once the stream has
+ * passed the call.  Deterministic from run to run.  Status codes as for
+ * gconv_fwd. */
+int gconv_bwd_data(const gconv_desc *d, const void *dy, const void *w, void *dx,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* Backward data on the direct kernel alone (any shape, one launch). */
+int gconv_bwd_data_direct(const gconv_desc *d, const void *dy, const void *w, void *dx,
+                          void *stream);
+
 /* Static strings; never NULL. */
 const char *gconv_status_str(int status);
 const char *gconv_path_name(int path);

@@ -209,3 +209,27 @@ def test_status_strings():
         assert isinstance(G.gconv_status_str(s), str) and G.gconv_status_str(s)
     assert G.gconv_path_name(G.GCONV_PATH_AUTO) == "auto"
     assert [G.gconv_path_name(i) for i in range(G.GCONV_NUM_PATHS)] == list(G.PATHS)
+
+
+def test_bwd_data_workspace_sizes():
+    # stride 1 with dil (k - 1) >= pad: the transform route needs a copy of w
+    d = G.make_desc(2, "bf16", 2, 4, 64, 32, (9, 9), (3, 3), (1, 1), (1, 1), (1, 1))
+    assert G.gconv_bwd_data_workspace(d) == 32 * 3 * 3 * 16 * 2
+    d = G.make_desc(3, "f32", 1, 2, 4, 6, (5, 6, 7), (3, 1, 3), (1, 1, 1), (1, 0, 2), (1, 1, 1))
+    assert G.gconv_bwd_data_workspace(d) == 6 * 3 * 1 * 3 * 2 * 4
+    # a stride above 1, or a pad beyond the dilated filter, has no use for one
+    d = G.make_desc(2, "f16", 1, 1, 8, 8, (9, 9), (3, 3), (2, 2), (1, 1), (1, 1))
+    assert G.gconv_bwd_data_workspace(d) == 0
+    d = G.make_desc(2, "f16", 1, 1, 8, 8, (9, 9), (3, 3), (1, 1), (3, 3), (1, 1))
+    assert G.gconv_bwd_data_workspace(d) == 0
+
+
+def test_bwd_data_validates_before_any_launch():
+    bad = G.make_desc(2, "f16", 1, 3, 8, 8, (9, 9), (3, 3), (1, 1), (1, 1), (1, 1))   # C % G != 0
+    with pytest.raises(G.GconvError):
+        G.gconv_bwd_data_workspace(bad)
+    assert G.gconv_bwd_data(bad, 16, 16, 16, None, 0) == G.GCONV_ERR_BAD_DESC
+    ok = G.make_desc(2, "f16", 1, 1, 8, 8, (9, 9), (3, 3), (1, 1), (1, 1), (1, 1))
+    assert G.gconv_bwd_data(ok, 0, 16, 16, None, 0) == G.GCONV_ERR_NULL_PTR
+    assert G.gconv_bwd_data_direct(ok, 16, 16, 0) == G.GCONV_ERR_NULL_PTR
+    assert G.gconv_bwd_data(ok, 17, 16, 16, None, 0) == G.GCONV_ERR_MISALIGNED
