@@ -147,6 +147,127 @@ def cpu_baseline(names, max_seconds: float):
     }
 
 
+def bwd_problem(p):
+    """The workload's problem without bias (backward data has none)."""
+    return inputs.Problem(p.ndim, p.dtype, p.N, p.G, p.C, p.K, p.spatial, p.filt, p.stride, p.pad,
+                          p.dil, False)
+
+
+def cpu_baseline_bwd(names, max_seconds: float):
+    """The oracle's backward data on this host's cores, on the first images of the workload."""
+    import oracle
+    elapsed, total_bytes, runs = 0.0, 0, 0
+    p = bwd_problem(inputs.WORKLOADS[names[0]].problem)
+    t = inputs.make_tensors(p, 4100)
+    w = inputs.storage_to_f64(t.w, p.dtype)
+    o = metrics.out_spatial(p)
+    dshape = (p.N,) + (o if p.ndim == 3 else o[1:]) + (p.K,)
+    dy = inputs.storage_to_f64(inputs.make_array(dshape, p.dtype, 4105), p.dtype)
+    st, pd, dl = p.spatial_args()
+    in_sp = p.x_shape()[1:-1]
+    t0 = time.perf_counter()
+    oracle.conv_bwd_data(dy[:1], w, p.G, in_sp, st, pd, dl)
+    one = time.perf_counter() - t0
+    nimg = max(1, min(p.N, int(max_seconds / 3 / max(one, 1e-9))))
+    sub = inputs.Problem(p.ndim, p.dtype, nimg, p.G, p.C, p.K, p.spatial, p.filt, p.stride, p.pad, p.dil, False)
+    while runs < 1 or elapsed < max_seconds:
+        t0 = time.perf_counter()
+        oracle.conv_bwd_data(dy[:nimg], w, p.G, in_sp, st, pd, dl)
+        elapsed += time.perf_counter() - t0
+        total_bytes += metrics.total_bytes(sub)
+        runs += 1
+    return {"value": total_bytes / elapsed / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "%s backward data, first %d of %d images, %d pass(es), fp64, %.1f s"
+                      % (names[0], nimg, p.N, runs, elapsed)}
+
+
+def bench_bwd_data(a, G, torch):
+    """Backward data (gconv_bwd_data) on the first workload of the set: the same
+    rotating-buffer protocol, timed with events on the launch stream around
+    each call (the stride-1 route is two kernels: weight transform + forward)."""
+    names, _ = WORKLOAD_SETS[a.workload]
+    name = names[0]
+    p = bwd_problem(inputs.WORKLOADS[name].problem)
+    dev = torch.device("cuda", 0)
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[p.dtype]
+    d = G.desc_from_problem(p)
+    o = G.gconv_out_dims(d)
+    dshape = (p.N,) + (o if p.ndim == 3 else o[1:]) + (p.K,)
+    per_set = metrics.io_bytes(p)["x"] + metrics.io_bytes(p)["y"]
+    R = 1 if a.hot else min(64, max(2, -(-ROTATE_BYTES // per_set)))
+    dy0 = torch.randn(dshape, device=dev, generator=torch.Generator(device=dev).manual_seed(7)).to(tdt)
+    dys = [dy0] + [dy0.clone() for _ in range(R - 1)]
+    dxs = [torch.empty(p.x_shape(), dtype=tdt, device=dev) for _ in range(R)]
+    w = (torch.randn(p.w_shape(), device=dev, generator=torch.Generator(device=dev).manual_seed(8))
+         / (p.Cpg * p.filt[0] * p.filt[1] * p.filt[2]) ** 0.5).to(tdt)
+    need = G.gconv_bwd_data_workspace(d)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+
+    def call(i):
+        rc = G.gconv_bwd_data(d, dys[i % R].data_ptr(), w.data_ptr(), dxs[i % R].data_ptr(),
+                              ws.data_ptr(), need, sptr)
+        if rc != 0:
+            raise G.GconvError(rc, "gconv_bwd_data(%s)" % name)
+
+    for i in range(a.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(a.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for k in range(a.steps):
+        evs[k][0].record(stream)
+        call(k)
+        evs[k][1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / a.steps
+    ds = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    avg_ms = sum(ds) / len(ds)
+    r = metrics.rates(p, avg_ms * 1e-3)
+    ai = metrics.flops(p) / metrics.total_bytes(p)
+    peak_tf = metrics.PEAK_TFLOPS["f32_vector"] if p.dtype == "f32" else metrics.PEAK_TFLOPS[p.dtype]
+    if ai < peak_tf * 1e12 / (metrics.PEAK_HBM_GBS * 1e9):
+        roof = {"bound": "hbm", "achieved": r["gbs"], "peak": metrics.PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": r["frac_hbm"]}
+    else:
+        roof = {"bound": "alu" if p.dtype == "f32" else "mfma", "achieved": r["tflops"], "peak": peak_tf,
+                "unit": "TFLOP/s", "frac": r["frac_compute"]}
+    route = ("weight transform + forward %s" % G.gconv_path_name(G.gconv_select_path(
+        G.make_desc(p.ndim, p.dtype, p.N, p.G, p.K, p.C, o if p.ndim == 3 else o[1:],
+                    p.filt if p.ndim == 3 else p.filt[1:], (1,) * p.ndim,
+                    tuple(p.dil[i] * (p.filt[i] - 1) - p.pad[i] for i in range(3 - p.ndim, 3)),
+                    p.spatial_args()[2])))) if need else "direct"
+    roof.update({"traffic": None, "kernel": "bwd_data (%s)" % route, "workload": name,
+                 "algorithmic_bytes": metrics.total_bytes(p), "algorithmic_flop": metrics.flops(p),
+                 "us_per_launch": avg_ms * 1e3, "timed_launches": len(ds),
+                 "timing": "event pair around each gconv_bwd_data call on the launch stream"})
+    out = {
+        "metric": "grouped conv bwd_data TFLOP/s + HBM GB/s (% of MI355X peak), 1 GPU",
+        "value": metrics.total_bytes(p) / (ms_per_step * 1e-3) / 1e9,
+        "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": p.dtype,
+        "data": "synthetic (seeded; dy~N(0,1), w~N(0,1/fan_in)); inputs resident in HBM",
+        "config": {"workload": inputs.WORKLOADS[name].about + " (backward data, no bias)", "names": [name],
+                   "layout": "dy NHWGK, w GKYXC -> dx NHWGC",
+                   "cache": "hot (no rotation)" if a.hot else "rotating buffer sets >= 512 MB"},
+        "per_config": {name: {"route": route, "us_avg": avg_ms * 1e3, "us_median": ds[len(ds) // 2] * 1e3,
+                              "us_min": ds[0] * 1e3, "tflops": r["tflops"], "gbs": r["gbs"],
+                              "frac_hbm": r["frac_hbm"], "frac_compute": r["frac_compute"],
+                              "rotating_sets": R}},
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_bwd(names, a.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -164,6 +285,8 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run 3 plain device copies of MIB MiB (a reference kernel of "
                          "known size for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--op", default="fwd", choices=["fwd", "bwd_data"],
+                    help="bwd_data: time gconv_bwd_data (dx from dy and w) on the workload's shapes")
     a = ap.parse_args()
 
     if a.gpus != 1:
@@ -186,6 +309,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if a.op == "bwd_data":
+        return bench_bwd_data(a, G, torch)
 
     names, dominant = WORKLOAD_SETS[a.workload]
     path = G.GCONV_PATH_AUTO if a.path == "auto" else G.PATHS[a.path]

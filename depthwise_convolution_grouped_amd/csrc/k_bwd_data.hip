@@ -15,7 +15,8 @@
 //     (partial sums joined by lane exchanges), fp32 accumulation;
 //   - the weight transform of the stride-1 route: at stride 1, dx is the
 //     forward convolution of dy with the weights flipped in space and with
-//     C and K exchanged (wt[g][c][Z-1-z][Y-1-y][X-1-x][k] = w[g][k][z][y][x][c])
+//     C and K exchanged (wt[g][c][Z-1-z][Y-1-y][X-1-x][k] = w[g][k][z][y][x][c]:
+//     reversing the flat tap index reverses all three axes)
 //     under padding dil (k - 1) - pad, so the host runs this transform into
 //     a caller workspace and then the forward dispatcher.
 #include "device_common.h"
@@ -69,24 +70,33 @@ __global__ __launch_bounds__(kBlock) void direct_kernel(Problem p, const T *__re
     if (e < total && part == 0) dx[e] = from_f32<T>(acc);
 }
 
-// wt[g][c][z][y][x][k] = w[g][k][Z-1-z][Y-1-y][X-1-x][c]; a copy of element
-// bits, one thread per element of wt
+// wt[g][c][t][k] = w[g][k][T-1-t][c] (t the flat tap (z, y, x), so T-1-t
+// flips all three axes at once): for each (group, tap) a Kpg x Cpg matrix
+// transposed through LDS in 32 x 32 tiles, read along c and written along
+// k so both sides are coalesced; a copy of element bits
 template <typename U>
-__global__ __launch_bounds__(kBlock) void flip_kernel(Problem p, const U *__restrict__ w, U *__restrict__ wt,
-                                                      int total)
+__global__ __launch_bounds__(kBlock) void flip_kernel(Problem p, const U *__restrict__ w, U *__restrict__ wt)
 {
-    const int f = blockIdx.x * kBlock + threadIdx.x;
-    if (f >= total) return;
-    int r = f;
-    const int k = r % p.Kpg;  r /= p.Kpg;
-    const int xx = r % p.X;   r /= p.X;
-    const int yy = r % p.Y;   r /= p.Y;
-    const int z = r % p.Z;    r /= p.Z;
-    const int c = r % p.Cpg;  r /= p.Cpg;
-    const int g = r;
-    const int src = ((((g * p.Kpg + k) * p.Z + (p.Z - 1 - z)) * p.Y + (p.Y - 1 - yy)) * p.X + (p.X - 1 - xx)) *
-                        p.Cpg + c;
-    wt[f] = w[src];
+    __shared__ U tile[32][33];
+    const int T = p.Z * p.Y * p.X;
+    const int nct = (p.Cpg + 31) / 32;
+    const int gt = blockIdx.x / nct;            // g * T + t (destination tap t)
+    const int g = gt / T, t = gt - g * T;
+    const int c0 = (blockIdx.x - gt * nct) * 32, k0 = blockIdx.y * 32;
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 32 x 8 threads
+    const U *src = w + ((size_t)g * p.Kpg * T + (T - 1 - t)) * p.Cpg;   // + k * T * Cpg + c
+#pragma unroll
+    for (int j = 0; j < 32; j += 8) {
+        const int k = k0 + ty + j, c = c0 + tx;
+        if (k < p.Kpg && c < p.Cpg) tile[ty + j][tx] = src[(size_t)k * T * p.Cpg + c];
+    }
+    __syncthreads();
+    U *dst = wt + ((size_t)g * p.Cpg * T + t) * p.Kpg;                  // + c * T * Kpg + k
+#pragma unroll
+    for (int j = 0; j < 32; j += 8) {
+        const int c = c0 + ty + j, k = k0 + tx;
+        if (c < p.Cpg && k < p.Kpg) dst[(size_t)c * T * p.Kpg + k] = tile[tx][ty + j];
+    }
 }
 
 int lanes_for(const Problem &p, long long elems)
@@ -132,14 +142,12 @@ hipError_t launch_direct(const Problem &p, const void *dy, const void *w, void *
 
 hipError_t launch_flip(const Problem &p, const void *w, void *wt, hipStream_t s)
 {
-    const long long total = (long long)p.G * p.Kpg * p.taps() * p.Cpg;
-    const int blocks = (int)((total + kBlock - 1) / kBlock);
+    // x: (group, tap, 32-channel tile of c), y: 32-channel tile of k
+    const dim3 grid((unsigned)((long long)p.G * p.taps() * ((p.Cpg + 31) / 32)), (p.Kpg + 31) / 32, 1);
     Args a{};
     if (elem_size(p.dtype) == 4)
-        return enqueue(flip_kernel<uint32_t>, dim3(blocks), dim3(kBlock), 0, s, a, p, (const uint32_t *)w,
-                       (uint32_t *)wt, (int)total);
-    return enqueue(flip_kernel<uint16_t>, dim3(blocks), dim3(kBlock), 0, s, a, p, (const uint16_t *)w,
-                   (uint16_t *)wt, (int)total);
+        return enqueue(flip_kernel<uint32_t>, grid, dim3(kBlock), 0, s, a, p, (const uint32_t *)w, (uint32_t *)wt);
+    return enqueue(flip_kernel<uint16_t>, grid, dim3(kBlock), 0, s, a, p, (const uint16_t *)w, (uint16_t *)wt);
 }
 
 }  // namespace bwd
