@@ -8,11 +8,13 @@
 //   dx[n,i,g,c] = sum over taps t and k with o = (i + pad - t dil) / stride an
 //                 integer in [0, out) of dy[n,o,g,k] w[g,k,t,c]   (per axis)
 //
-// Two kernels live here:
+// Kernels here:
 //   - a direct kernel for every shape: L consecutive threads own one dx
 //     element, walk the taps whose output coordinate is integral and in
 //     range, and split the Kpg output channels of the group between them
-//     (partial sums joined by lane exchanges), fp32 accumulation;
+//     (partial sums joined by lane exchanges), fp32 accumulation; for
+//     depthwise problems with 16-byte aligned dy and dx, a channel-vector
+//     form of it;
 //   - the weight transform of the stride-1 route: at stride 1, dx is the
 //     forward convolution of dy with the weights flipped in space and with
 //     C and K exchanged (wt[g][c][Z-1-z][Y-1-y][X-1-x][k] = w[g][k][z][y][x][c]:
@@ -68,6 +70,74 @@ __global__ __launch_bounds__(kBlock) void direct_kernel(Problem p, const T *__re
 #pragma unroll
     for (int m = L / 2; m >= 1; m /= 2) acc += __shfl_xor(acc, m);
     if (e < total && part == 0) dx[e] = from_f32<T>(acc);
+}
+
+// Depthwise (Cpg = Kpg = 1, so group g is channel g): one thread owns VEC
+// consecutive channels (16 bytes) of one dx pixel.  The tap walk and its
+// index arithmetic are shared by the VEC channels, dy is read and dx written
+// as 16-byte vectors, and the whole weight tensor sits in LDS transposed to
+// [tap][channel], so the VEC weights of a tap are one 16-byte LDS read (a
+// gather from global memory would touch a different line per lane).
+constexpr int kDwLdsBytes = 32 * 1024;
+// S: the stride on every axis when it is 1 or 2 (the divisibility tests
+// and divisions become bit operations), 0 for any stride
+template <typename T, int S>
+__global__ __launch_bounds__(kBlock) void depthwise_kernel(Problem p, const T *__restrict__ dy,
+                                                           const T *__restrict__ w, T *__restrict__ dx,
+                                                           int total)
+{
+    constexpr int VEC = 16 / (int)sizeof(T);
+    extern __shared__ uint4 wl4[];
+    T *wl = reinterpret_cast<T *>(wl4);
+    const int T9 = p.Z * p.Y * p.X;
+    for (int i = threadIdx.x; i < p.G * T9; i += kBlock) {   // w[g][t] -> wl[t][g]
+        const int g = i / T9, t = i - g * T9;
+        wl[t * p.G + g] = w[i];
+    }
+    __syncthreads();
+    // grid-stride over (pixel, channel vector): a few blocks per CU, each
+    // staging the weights once
+    for (int e = blockIdx.x * kBlock + threadIdx.x; e < total; e += gridDim.x * kBlock) {
+        const int Cv = p.G / VEC;
+        int r = e;
+        const int cv = r % Cv;  r /= Cv;
+        const int iw = r % p.W; r /= p.W;
+        const int ih = r % p.H; r /= p.H;
+        const int id = r % p.D; r /= p.D;
+        const int n = r;
+        const int g0 = cv * VEC;
+        const int sd = S ? S : p.sd, sh = S ? S : p.sh, sw = S ? S : p.sw;
+        float acc[VEC];
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) acc[j] = 0.f;
+        for (int z = 0; z < p.Z; ++z) {
+            const int td = id + p.pd - z * p.dd;
+            if (td < 0 || td % sd != 0 || td / sd >= p.Do) continue;
+            const int od = td / sd;
+            for (int yy = 0; yy < p.Y; ++yy) {
+                const int th = ih + p.ph - yy * p.dh;
+                if (th < 0 || th % sh != 0 || th / sh >= p.Ho) continue;
+                const int oh = th / sh;
+                for (int xx = 0; xx < p.X; ++xx) {
+                    const int tw = iw + p.pw - xx * p.dw;
+                    if (tw < 0 || tw % sw != 0 || tw / sw >= p.Wo) continue;
+                    const int ow = tw / sw;
+                    const uint4 raw = *reinterpret_cast<const uint4 *>(
+                        dy + (((size_t)(n * p.Do + od) * p.Ho + oh) * p.Wo + ow) * p.G + g0);
+                    const T *dv = reinterpret_cast<const T *>(&raw);
+                    const int t = (z * p.Y + yy) * p.X + xx;
+                    const uint4 wraw = *reinterpret_cast<const uint4 *>(wl + t * p.G + g0);
+                    const T *wv = reinterpret_cast<const T *>(&wraw);
+#pragma unroll
+                    for (int j = 0; j < VEC; ++j) acc[j] = fmaf(to_f32(dv[j]), to_f32(wv[j]), acc[j]);
+                }
+            }
+        }
+        T o[VEC];
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) o[j] = from_f32<T>(acc[j]);
+        *reinterpret_cast<uint4 *>(dx + (size_t)e * VEC) = *reinterpret_cast<const uint4 *>(o);
+    }
 }
 
 // wt[g][c][t][k] = w[g][k][T-1-t][c] (t the flat tap (z, y, x), so T-1-t
@@ -131,8 +201,37 @@ hipError_t go(const Problem &p, const void *dy, const void *w, void *dx, hipStre
 
 }  // namespace
 
+template <typename T>
+hipError_t go_dw(const Problem &p, const void *dy, const void *w, void *dx, hipStream_t s)
+{
+    constexpr int VEC = 16 / (int)sizeof(T);
+    const long long total = (long long)p.N * p.D * p.H * p.W * (p.G / VEC);
+    Args a{};
+    const long long blocks = (total + kBlock - 1) / kBlock;
+    const dim3 grid((unsigned)(blocks < 2048 ? blocks : 2048));   // 8 per CU, grid-stride beyond
+    const bool same = p.sh == p.sw && (p.ndim == 2 || p.sd == p.sh);   // 2D: sd is 1 and unused
+    auto k = same && p.sh == 1 ? depthwise_kernel<T, 1> : same && p.sh == 2 ? depthwise_kernel<T, 2>
+                                                                             : depthwise_kernel<T, 0>;
+    const unsigned lds = (unsigned)(p.G * p.taps() * (int)sizeof(T));
+    return enqueue(k, grid, dim3(kBlock), lds, s, a, p, (const T *)dy, (const T *)w, (T *)dx, (int)total);
+}
+
+bool depthwise_ok(const Problem &p)
+{
+    return p.Cpg == 1 && p.Kpg == 1 && p.G % (16 / elem_size(p.dtype)) == 0 &&
+           (long long)p.G * p.taps() * elem_size(p.dtype) <= kDwLdsBytes;
+}
+
 hipError_t launch_direct(const Problem &p, const void *dy, const void *w, void *dx, hipStream_t s)
 {
+    const bool vec_ok = depthwise_ok(p) && ((uintptr_t)dy & 15) == 0 && ((uintptr_t)dx & 15) == 0;
+    if (vec_ok) {
+        switch (p.dtype) {
+        case GCONV_F32: return go_dw<float>(p, dy, w, dx, s);
+        case GCONV_F16: return go_dw<_Float16>(p, dy, w, dx, s);
+        default: return go_dw<__bf16>(p, dy, w, dx, s);
+        }
+    }
     switch (p.dtype) {
     case GCONV_F32: return go<float>(p, dy, w, dx, s);
     case GCONV_F16: return go<_Float16>(p, dy, w, dx, s);

@@ -68,6 +68,9 @@ CASES = [
     (2, "f16", 1, 1, 8, 8, (9, 9), (3, 3), 1, 3, 1),            # pad beyond the filter: direct only
     (2, "bf16", 1, 4, 32, 64, (12, 10), (1, 1), 1, 0, 1),       # 1x1
     (2, "f32", 3, 5, 15, 10, (7, 8), (3, 2), (2, 1), (1, 0), (1, 2)),   # mixed strides and dilations
+    (2, "f32", 2, 12, 12, 12, (11, 10), (3, 3), 2, 1, 2),       # depthwise fp32, channel vectors of 4
+    (3, "bf16", 1, 24, 24, 24, (5, 9, 8), (3, 3, 3), 2, 1, 1),  # depthwise 3D stride 2, vectors of 8
+    (2, "f16", 1, 20, 20, 20, (9, 9), (3, 3), 2, 1, 1),         # depthwise, C not a multiple of 8: scalar
 ]
 
 
