@@ -1,4 +1,4 @@
-"""Plain CPU oracle for grouped / depthwise convolution forward and backward data.
+"""Plain CPU oracle for grouped / depthwise convolution forward, backward data and backward weight.
 
 TEST INFRASTRUCTURE.  Only the test suite, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package.  The product path
@@ -13,6 +13,7 @@ ctypes and marshals numpy arrays:
 * ``conv_fwd``        -- every output element plus its error scale
 * ``conv_fwd_points`` -- selected output elements (full-size spot checks)
 * ``conv_bwd_data``   -- backward data: the gradient w.r.t. x from dy and w
+* ``conv_bwd_weight`` -- backward weight: the gradient w.r.t. w from x and dy
 * ``out_extent``      -- output length along one axis
 
 Arrays use the oracle's layouts: x ``[N][D][H][W][G][Cpg]``,
@@ -73,6 +74,8 @@ def bind(path: str):
     lib.gref_conv_fwd_points.restype = ctypes.c_int
     lib.gref_conv_bwd_data.argtypes = [i64, i64, i64, i64, p64, p64, p64, p64, p64, pd, pd, pd, pd]
     lib.gref_conv_bwd_data.restype = ctypes.c_int
+    lib.gref_conv_bwd_weight.argtypes = [i64, i64, i64, i64, p64, p64, p64, p64, p64, pd, pd, pd, pd]
+    lib.gref_conv_bwd_weight.restype = ctypes.c_int
     lib.gref_num_threads.argtypes = []
     lib.gref_num_threads.restype = ctypes.c_int
     return lib
@@ -200,6 +203,42 @@ def conv_bwd_data(dy, w, groups, in_spatial, stride, pad, dil, lib=None):
     if not spatial3:
         dx, s = dx[:, 0], s[:, 0]
     return dx, s
+
+
+def conv_bwd_weight(x, dy, groups, filt, stride, pad, dil, lib=None):
+    """Backward weight (the gradient w.r.t. w), fp64.  Returns (dw, scale), both K,[Z,]Y,X,Cpg.
+
+    x is N[D]HWC, dy N[Do]HoWoK; filt gives the filter extents ((Y, X) or (Z, Y, X)).
+    """
+    lib = lib or _load()
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    dy = np.ascontiguousarray(dy, dtype=np.float64)
+    spatial3 = x.ndim == 5
+    if x.ndim == 4:
+        x = x[:, None]
+    if dy.ndim == 4:
+        dy = dy[:, None]
+    if x.ndim != 5 or dy.ndim != 5:
+        raise ValueError("x must be N[D]HWC and dy N[Do]HoWoK")
+    N, C, K = x.shape[0], x.shape[4], dy.shape[4]
+    G = int(groups)
+    if G <= 0 or C % G or K % G or dy.shape[0] != N:
+        raise ValueError("inconsistent channels or batch")
+    d = dict(in_=_triple(x.shape[1:4], 1), filt=_triple(filt, 1), stride=_triple(stride, 1),
+             pad=_triple(pad, 0), dil=_triple(dil, 1))
+    outs = _outs(d, lib)
+    if tuple(outs) != tuple(dy.shape[1:4]):
+        raise ValueError("dy extents %r do not match the forward output %r" % (dy.shape[1:4], tuple(outs)))
+    f = d["filt"]
+    dw = np.empty((K, f[0], f[1], f[2], C // G), dtype=np.float64)
+    s = np.empty_like(dw)
+    rc = lib.gref_conv_bwd_weight(N, G, C, K, d["in_"], f, d["stride"], d["pad"], d["dil"],
+                                  _dptr(x), _dptr(dy), _dptr(dw), _dptr(s))
+    if rc != 0:
+        raise ValueError("oracle rejected the problem")
+    if not spatial3:
+        dw, s = dw[:, 0], s[:, 0]
+    return dw, s
 
 
 def num_threads() -> int:

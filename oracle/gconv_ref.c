@@ -1,6 +1,6 @@
 /*
- * gconv_ref.c -- plain CPU oracle for grouped / depthwise convolution forward
- * and backward data.
+ * gconv_ref.c -- plain CPU oracle for grouped / depthwise convolution forward,
+ * backward data and backward weight.
  *
  * TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the
  * benchmark's CPU-baseline leg may load or call this library.  The product
@@ -249,6 +249,74 @@ int gref_conv_bwd_data(int64_t N, int64_t G, int64_t C, int64_t K,
                     dx[xi] = acc;
                     scale[xi] = s;
                 }
+    }
+    return 0;
+}
+
+/*
+ * Backward weight: the gradient of a loss with respect to w, given x and dy
+ * (the third variant of the CK grouped_conv tile-engine README, introduction;
+ * its runner takes X and dY in the Python examples README, Runner argument
+ * contract).  Every forward term x[n,id,ih,iw,g,c] * w[g,k,z,y,x,c] feeds
+ * y[n,od,oh,ow,g,k], so
+ *
+ *   dw[g,k,z,y,x,c] = sum over n, od, oh, ow with id = od*stride - pad + z*dil
+ *                     (likewise ih, iw) inside the input of
+ *                     dy[n,od,oh,ow,g,k] * x[n,id,ih,iw,g,c].
+ *
+ * Layouts: x [N][D][H][W][G][Cpg], dy [N][Do][Ho][Wo][G][Kpg],
+ * dw [G][Kpg][Z][Y][X][Cpg].  scale receives sum |dy*x| over the terms
+ * summed.  Returns 0, or -1 on inconsistent sizes.
+ */
+int gref_conv_bwd_weight(int64_t N, int64_t G, int64_t C, int64_t K,
+                         const int64_t in[3], const int64_t filt[3],
+                         const int64_t stride[3], const int64_t pad[3],
+                         const int64_t dil[3],
+                         const double *x, const double *dy, double *dw, double *scale)
+{
+    if (N <= 0 || G <= 0 || C <= 0 || K <= 0 || C % G != 0 || K % G != 0)
+        return -1;
+    const int64_t Cpg = C / G, Kpg = K / G;
+    int64_t out[3];
+    for (int a = 0; a < 3; ++a) {
+        out[a] = gref_out_extent(in[a], filt[a], stride[a], pad[a], dil[a]);
+        if (out[a] <= 0) return -1;
+    }
+    const int64_t D = in[0], H = in[1], W = in[2];
+    const int64_t Z = filt[0], Y = filt[1], X = filt[2];
+    const int64_t Do = out[0], Ho = out[1], Wo = out[2];
+    const int64_t rows = G * Kpg;
+
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < rows; ++r) {
+        const int64_t g = r / Kpg, k = r % Kpg;
+        for (int64_t z = 0; z < Z; ++z)
+            for (int64_t yy = 0; yy < Y; ++yy)
+                for (int64_t xx = 0; xx < X; ++xx)
+                    for (int64_t c = 0; c < Cpg; ++c) {
+                        double acc = 0.0, s = 0.0;
+                        for (int64_t n = 0; n < N; ++n)
+                            for (int64_t od = 0; od < Do; ++od) {
+                                const int64_t id = od * stride[0] - pad[0] + z * dil[0];
+                                if (id < 0 || id >= D) continue;
+                                for (int64_t oh = 0; oh < Ho; ++oh) {
+                                    const int64_t ih = oh * stride[1] - pad[1] + yy * dil[1];
+                                    if (ih < 0 || ih >= H) continue;
+                                    for (int64_t ow = 0; ow < Wo; ++ow) {
+                                        const int64_t iw = ow * stride[2] - pad[2] + xx * dil[2];
+                                        if (iw < 0 || iw >= W) continue;
+                                        const int64_t yi = ((((n * Do + od) * Ho + oh) * Wo + ow) * G + g) * Kpg + k;
+                                        const int64_t xi = ((((n * D + id) * H + ih) * W + iw) * G + g) * Cpg + c;
+                                        const double t = dy[yi] * x[xi];
+                                        acc += t;
+                                        s += fabs(t);
+                                    }
+                                }
+                            }
+                        const int64_t wi = ((((g * Kpg + k) * Z + z) * Y + yy) * X + xx) * Cpg + c;
+                        dw[wi] = acc;
+                        scale[wi] = s;
+                    }
     }
     return 0;
 }
