@@ -137,8 +137,8 @@ MUTANTS = {
     "pad_sign": ("const int64_t tw = iw + pad[2] - xx * dil[2];", "const int64_t tw = iw - pad[2] - xx * dil[2];"),
     "flipped_taps": ("const int64_t td = id + pad[0] - z * dil[0];",
                      "const int64_t td = id + pad[0] - (Z - 1 - z) * dil[0];"),
-    "wrong_group_of_dy": ("const int64_t yi = ((((n * Do + od) * Ho + oh) * Wo + ow) * G + g) * Kpg + k;",
-                          "const int64_t yi = ((((n * Do + od) * Ho + oh) * Wo + ow) * G + (G - 1 - g)) * Kpg + k;"),
+    "wrong_group_of_dy": ("const double t = dy[yi] * w[wi];",
+                          "const double t = dy[yi + (G - 1 - 2 * g) * Kpg] * w[wi];"),
     "extent_bound_off_by_one": ("td / stride[0] >= Do) continue;", "td / stride[0] > Do) continue;"),
 }
 
