@@ -221,6 +221,31 @@ int run_bwd_data(const gconv_desc *d, const void *dy, const void *w, void *dx, v
     return GCONV_OK;
 }
 
+size_t bwd_weight_partials_bytes(const Problem &p, int nch)
+{
+    return nch > 1 ? (size_t)nch * (size_t)p.G * p.Kpg * p.taps() * p.Cpg * sizeof(float) : 0;
+}
+
+int run_bwd_weight(const gconv_desc *d, const void *x, const void *dy, void *dw, void *ws,
+                   size_t ws_bytes, void *stream)
+{
+    int64_t out[3];
+    int rc = check_desc(d, out);
+    if (rc != GCONV_OK) return rc;
+    if (!x || !dy || !dw) return GCONV_ERR_NULL_PTR;
+    const uintptr_t es = (uintptr_t)elem_size(d->dtype);
+    if (!aligned(x, es) || !aligned(dy, es) || !aligned(dw, es)) return GCONV_ERR_MISALIGNED;
+    const Problem p = to_problem(d, out);
+    int nch = bwdw::ideal_chunks(p);
+    const size_t per = bwd_weight_partials_bytes(p, 2) / 2;   // one chunk of partial sums
+    if (!ws || !aligned(ws, 4)) nch = 1;
+    else if ((size_t)nch * per > ws_bytes) nch = (int)(ws_bytes / per);
+    if (nch < 1) nch = 1;
+    if (bwdw::launch(p, x, dy, dw, (float *)ws, nch, (hipStream_t)stream) != hipSuccess)
+        return GCONV_ERR_LAUNCH;
+    return GCONV_OK;
+}
+
 }  // namespace
 }  // namespace gconv
 
@@ -312,6 +337,23 @@ GCONV_API int gconv_bwd_data_direct(const gconv_desc *d, const void *dy, const v
                                     void *stream)
 {
     return run_bwd_data(d, dy, w, dx, nullptr, 0, true, stream);
+}
+
+GCONV_API int gconv_bwd_weight_workspace(const gconv_desc *d, size_t *bytes)
+{
+    if (!bytes) return GCONV_ERR_NULL_PTR;
+    int64_t out[3];
+    int rc = check_desc(d, out);
+    if (rc != GCONV_OK) return rc;
+    const Problem p = to_problem(d, out);
+    *bytes = bwd_weight_partials_bytes(p, bwdw::ideal_chunks(p));
+    return GCONV_OK;
+}
+
+GCONV_API int gconv_bwd_weight(const gconv_desc *d, const void *x, const void *dy, void *dw,
+                               void *workspace, size_t workspace_bytes, void *stream)
+{
+    return run_bwd_weight(d, x, dy, dw, workspace, workspace_bytes, stream);
 }
 
 GCONV_API const char *gconv_status_str(int status)

@@ -93,6 +93,13 @@ hipError_t launch_direct(const Problem &p, const void *dy, const void *w, void *
 hipError_t launch_flip(const Problem &p, const void *w, void *wt, hipStream_t s);
 }
 
+// Backward weight (k_bwd_weight.hip).  `p` is the forward problem; ws holds
+// nch x (weight elements) fp32 partial sums when nch > 1.
+namespace bwdw {
+int ideal_chunks(const Problem &p);
+hipError_t launch(const Problem &p, const void *x, const void *dy, void *dw, float *ws, int nch, hipStream_t s);
+}
+
 inline int elem_size(int dtype) { return dtype == GCONV_F32 ? 4 : 2; }
 
 }  // namespace gconv

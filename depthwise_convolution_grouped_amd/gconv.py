@@ -46,6 +46,7 @@ PATHS = {"generic": 0, "depthwise": 1, "smallg_mfma": 2, "igemm_mfma": 3, "ighal
 EXPORTS = ("gconv_validate", "gconv_out_dims", "gconv_select_path", "gconv_path_supported",
            "gconv_get_plan", "gconv_fwd", "gconv_fwd_path", "gconv_fwd_timed",
            "gconv_bwd_data_workspace", "gconv_bwd_data", "gconv_bwd_data_direct",
+           "gconv_bwd_weight_workspace", "gconv_bwd_weight",
            "gconv_status_str", "gconv_path_name", "gconv_abi_version")
 
 
@@ -104,6 +105,8 @@ def lib():
     L.gconv_bwd_data_workspace.argtypes = [pd, ctypes.POINTER(ctypes.c_size_t)]
     L.gconv_bwd_data.argtypes = [pd, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.gconv_bwd_data_direct.argtypes = [pd, vp, vp, vp, vp]
+    L.gconv_bwd_weight_workspace.argtypes = [pd, ctypes.POINTER(ctypes.c_size_t)]
+    L.gconv_bwd_weight.argtypes = [pd, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.gconv_status_str.argtypes = [ctypes.c_int]
     L.gconv_status_str.restype = ctypes.c_char_p
     L.gconv_path_name.argtypes = [ctypes.c_int]
@@ -112,7 +115,7 @@ def lib():
     for name in ("gconv_validate", "gconv_out_dims", "gconv_select_path", "gconv_path_supported",
                  "gconv_get_plan", "gconv_fwd", "gconv_fwd_path", "gconv_fwd_timed",
                  "gconv_bwd_data_workspace", "gconv_bwd_data", "gconv_bwd_data_direct",
-                 "gconv_abi_version"):
+                 "gconv_bwd_weight_workspace", "gconv_bwd_weight", "gconv_abi_version"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -209,6 +212,22 @@ def gconv_bwd_data(d: gconv_desc, dy: int, w: int, dx: int, workspace: Optional[
 
 def gconv_bwd_data_direct(d: gconv_desc, dy: int, w: int, dx: int, stream: int = 0) -> int:
     return lib().gconv_bwd_data_direct(ctypes.byref(d), dy, w, dx, stream or None)
+
+
+def gconv_bwd_weight_workspace(d: gconv_desc) -> int:
+    """Partial-sum workspace bytes gconv_bwd_weight can use for the forward descriptor d."""
+    n = ctypes.c_size_t()
+    rc = lib().gconv_bwd_weight_workspace(ctypes.byref(d), ctypes.byref(n))
+    if rc != GCONV_OK:
+        raise GconvError(rc, "gconv_bwd_weight_workspace")
+    return int(n.value)
+
+
+def gconv_bwd_weight(d: gconv_desc, x: int, dy: int, dw: int, workspace: Optional[int],
+                     workspace_bytes: int, stream: int = 0) -> int:
+    """Raw call with device addresses (ints); returns the status code."""
+    return lib().gconv_bwd_weight(ctypes.byref(d), x, dy, dw, workspace or None, int(workspace_bytes),
+                                  stream or None)
 
 
 def gconv_status_str(status: int) -> str:
@@ -313,4 +332,48 @@ def conv_bwd_data(dy, w, groups: int, in_spatial, stride=None, pad=None, dil=Non
         rc = gconv_bwd_data(d, dy.data_ptr(), w.data_ptr(), out.data_ptr(), ws_ptr, ws_bytes, s)
     if rc != GCONV_OK:
         raise GconvError(rc, "gconv_bwd_data")
+    return out
+
+
+def conv_bwd_weight(x, dy, groups: int, filt, stride=None, pad=None, dil=None, out=None,
+                    workspace=None, use_workspace: bool = True, stream=None):
+    """Backward weight on PyTorch device tensors: dw (K[Z]YXCpg) from x (N[D]HWC) and dy (N[Do]HoWoK).
+
+    filt is (Y, X) or (Z, Y, X).  A workspace of gconv_bwd_weight_workspace
+    bytes is allocated here unless one is passed (a device tensor) or
+    use_workspace is False (one kernel, one chunk).
+    """
+    import torch
+    nd = x.dim() - 2
+    if nd not in (2, 3) or dy.dim() != x.dim():
+        raise ValueError("x must be N[D]HWC and dy N[Do]HoWoK")
+    if not (x.is_contiguous() and dy.is_contiguous()):
+        raise ValueError("x and dy must be contiguous")
+    if dy.dtype != x.dtype:
+        raise TypeError("x and dy must share one dtype")
+    stride = stride or (1,) * nd
+    pad = pad or (0,) * nd
+    dil = dil or (1,) * nd
+    N, C, K = x.shape[0], x.shape[-1], dy.shape[-1]
+    d = make_desc(nd, _torch_dtype_code(x), N, groups, C, K, tuple(x.shape[1:-1]), tuple(filt),
+                  stride, pad, dil)
+    o = gconv_out_dims(d)
+    if tuple(dy.shape[1:-1]) != (o if nd == 3 else o[1:]) or dy.shape[0] != N:
+        raise ValueError("dy's shape %r is not the forward output" % (tuple(dy.shape),))
+    wshape = (K,) + tuple(filt) + (C // groups,)
+    if out is None:
+        out = torch.empty(wshape, dtype=x.dtype, device=x.device)
+    elif tuple(out.shape) != wshape or not out.is_contiguous() or out.dtype != x.dtype:
+        raise ValueError("out must be a contiguous %s tensor of shape %s" % (x.dtype, wshape))
+    s = stream if stream is not None else torch.cuda.current_stream(x.device).cuda_stream
+    ws_ptr, ws_bytes = None, 0
+    if use_workspace:
+        need = gconv_bwd_weight_workspace(d)
+        if workspace is None and need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        if workspace is not None:
+            ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    rc = gconv_bwd_weight(d, x.data_ptr(), dy.data_ptr(), out.data_ptr(), ws_ptr, ws_bytes, s)
+    if rc != GCONV_OK:
+        raise GconvError(rc, "gconv_bwd_weight")
     return out

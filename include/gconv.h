@@ -189,6 +189,36 @@ int gconv_bwd_data(const gconv_desc *d, const void *dy, const void *w, void *dx,
 int gconv_bwd_data_direct(const gconv_desc *d, const void *dy, const void *w, void *dx,
                           void *stream);
 
+/* ---- Backward weight --------------------------------------------------
+ *
+ * dw, the gradient with respect to w, from x and dy: the backward-weight
+ * variant of the CK grouped_conv tile-engine README (introduction), whose
+ * runner takes X and dY (CK Python examples README, Runner argument
+ * contract).  d is the FORWARD problem's descriptor.  Layouts:
+ * x [N][D][H][W][G][Cpg], dy [N][Do][Ho][Wo][G][Kpg], dw [G][Kpg][Z][Y][X][Cpg],
+ * device pointers aligned to the element size, dtype as d->dtype, fp32
+ * accumulation, rounded once.
+ *
+ *   dw[g,k,t,c] = sum over output pixels o whose tap t reads an in-bounds
+ *                 input i = o*stride - pad + t*dil of dy[n,o,g,k] * x[n,i,g,c]
+ */
+
+/* Bytes of fp32 partial-sum workspace that lets gconv_bwd_weight split the
+ * reduction over enough chunks of output rows to fill the GPU (0 when one
+ * chunk already does). */
+int gconv_bwd_weight_workspace(const gconv_desc *d, size_t *bytes);
+
+/* Backward weight, asynchronous on `stream`.  `workspace` (device memory the
+ * caller owns, 4-byte aligned, may be NULL) of `workspace_bytes`: the
+ * reduction is split over as many chunks as it holds partial sums for (at
+ * most the gconv_bwd_weight_workspace amount), then the chunks are added in
+ * order (two kernels); with no room for two chunks one kernel sums each
+ * element alone.  No atomics: for a given workspace size the result is
+ * bitwise deterministic (the chunking, hence the summation order, depends on
+ * that size).  Status codes as for gconv_fwd. */
+int gconv_bwd_weight(const gconv_desc *d, const void *x, const void *dy, void *dw,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static strings; never NULL. */
 const char *gconv_status_str(int status);
 const char *gconv_path_name(int path);
