@@ -268,6 +268,89 @@ def bench_bwd_data(a, G, torch):
     return 0
 
 
+def bench_bwd_weight(a, G, torch):
+    """Backward weight (gconv_bwd_weight, full partial-sum workspace) on the first
+    workload of the set, timed like backward data (events around each call:
+    the two-stage reduction is two kernels)."""
+    names, _ = WORKLOAD_SETS[a.workload]
+    name = names[0]
+    p = bwd_problem(inputs.WORKLOADS[name].problem)
+    dev = torch.device("cuda", 0)
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[p.dtype]
+    d = G.desc_from_problem(p)
+    o = G.gconv_out_dims(d)
+    dshape = (p.N,) + (o if p.ndim == 3 else o[1:]) + (p.K,)
+    per_set = metrics.io_bytes(p)["x"] + metrics.io_bytes(p)["y"]
+    R = 1 if a.hot else min(64, max(2, -(-ROTATE_BYTES // per_set)))
+    gen = torch.Generator(device=dev)
+    x0 = torch.randn(p.x_shape(), device=dev, generator=gen.manual_seed(5)).to(tdt)
+    dy0 = torch.randn(dshape, device=dev, generator=gen.manual_seed(6)).to(tdt)
+    xs = [x0] + [x0.clone() for _ in range(R - 1)]
+    dys = [dy0] + [dy0.clone() for _ in range(R - 1)]
+    dw = torch.empty(p.w_shape(), dtype=tdt, device=dev)
+    need = G.gconv_bwd_weight_workspace(d)
+    ws = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+
+    def call(i):
+        rc = G.gconv_bwd_weight(d, xs[i % R].data_ptr(), dys[i % R].data_ptr(), dw.data_ptr(),
+                                ws.data_ptr(), need, sptr)
+        if rc != 0:
+            raise G.GconvError(rc, "gconv_bwd_weight(%s)" % name)
+
+    for i in range(a.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(a.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for k in range(a.steps):
+        evs[k][0].record(stream)
+        call(k)
+        evs[k][1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / a.steps
+    ds = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    avg_ms = sum(ds) / len(ds)
+    r = metrics.rates(p, avg_ms * 1e-3)
+    peak_tf = metrics.PEAK_TFLOPS["f32_vector"] if p.dtype == "f32" else metrics.PEAK_TFLOPS[p.dtype]
+    # the reduction runs on the vector ALUs (fp32 FMA) whatever the element type
+    alu_peak = metrics.PEAK_TFLOPS["f32_vector"]
+    ai = metrics.flops(p) / metrics.total_bytes(p)
+    if ai < alu_peak * 1e12 / (metrics.PEAK_HBM_GBS * 1e9):
+        roof = {"bound": "hbm", "achieved": r["gbs"], "peak": metrics.PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": r["frac_hbm"]}
+    else:
+        roof = {"bound": "alu", "achieved": r["tflops"], "peak": alu_peak, "unit": "TFLOP/s",
+                "frac": r["tflops"] / alu_peak}
+    route = "two-stage reduction (%d B of partial sums)" % need if need else "one-stage reduction"
+    roof.update({"traffic": None, "kernel": "bwd_weight (%s)" % route, "workload": name,
+                 "algorithmic_bytes": metrics.total_bytes(p), "algorithmic_flop": metrics.flops(p),
+                 "us_per_launch": avg_ms * 1e3, "timed_launches": len(ds),
+                 "timing": "event pair around each gconv_bwd_weight call on the launch stream"})
+    out = {
+        "metric": "grouped conv bwd_weight TFLOP/s + HBM GB/s (% of MI355X peak), 1 GPU",
+        "value": metrics.total_bytes(p) / (ms_per_step * 1e-3) / 1e9,
+        "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": p.dtype,
+        "data": "synthetic (seeded; x, dy ~ N(0,1)); inputs resident in HBM",
+        "config": {"workload": inputs.WORKLOADS[name].about + " (backward weight)", "names": [name],
+                   "layout": "x NHWGC, dy NHWGK -> dw GKYXC",
+                   "cache": "hot (no rotation)" if a.hot else "rotating buffer sets >= 512 MB"},
+        "per_config": {name: {"route": route, "us_avg": avg_ms * 1e3, "us_median": ds[len(ds) // 2] * 1e3,
+                              "us_min": ds[0] * 1e3, "tflops": r["tflops"], "gbs": r["gbs"],
+                              "frac_hbm": r["frac_hbm"], "frac_mfma_peak": r["tflops"] / peak_tf,
+                              "rotating_sets": R}},
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -285,8 +368,9 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run 3 plain device copies of MIB MiB (a reference kernel of "
                          "known size for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
-    ap.add_argument("--op", default="fwd", choices=["fwd", "bwd_data"],
-                    help="bwd_data: time gconv_bwd_data (dx from dy and w) on the workload's shapes")
+    ap.add_argument("--op", default="fwd", choices=["fwd", "bwd_data", "bwd_weight"],
+                    help="bwd_data: time gconv_bwd_data (dx from dy and w); bwd_weight: gconv_bwd_weight "
+                         "(dw from x and dy); both on the workload's shapes")
     a = ap.parse_args()
 
     if a.gpus != 1:
@@ -312,6 +396,8 @@ def main():
 
     if a.op == "bwd_data":
         return bench_bwd_data(a, G, torch)
+    if a.op == "bwd_weight":
+        return bench_bwd_weight(a, G, torch)
 
     names, dominant = WORKLOAD_SETS[a.workload]
     path = G.GCONV_PATH_AUTO if a.path == "auto" else G.PATHS[a.path]
