@@ -14,9 +14,11 @@
 //      over one chunk of output rows (n, od, oh) into an fp32 workspace
 //      [chunk][f]; consecutive threads take consecutive input channels c,
 //      so their x reads are contiguous and their dy reads shared;
-//   2. the chunks of each element are added in chunk order and rounded once.
+//   2. the chunks of each element are added in a fixed order (eight running
+//      sums over the chunks, then a fixed tree) and rounded once.
 // With one chunk (no workspace, or a problem with enough weight elements to
-// fill the chip) stage 1 writes dw directly.
+// fill the chip) stage 1 writes dw directly.  Depthwise 3x3 problems take a
+// channel-vector form of stage 1 (below).
 #include "device_common.h"
 #include "gconv_internal.h"
 
@@ -78,9 +80,125 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const float *__restrict_
 {
     const int f = blockIdx.x * kBlock + threadIdx.x;
     if (f >= welems) return;
-    float acc = 0.f;
-    for (int ch = 0; ch < nch; ++ch) acc += ws[(size_t)ch * welems + f];
-    dw[f] = from_f32<T>(acc);
+    // eight independent partial sums (loads in flight together), combined
+    // in a fixed order: deterministic
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int ch = 0;
+    for (; ch + 8 <= nch; ch += 8)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) a[u] += ws[(size_t)(ch + u) * welems + f];
+    for (; ch < nch; ++ch) a[0] += ws[(size_t)ch * welems + f];
+    dw[f] = from_f32<T>(((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7])));
+}
+
+// Depthwise 3x3 (Cpg = Kpg = 1, nine taps): workgroup (v, chunk) owns the
+// VEC channels of channel vector v over one chunk of output pixels.  Each
+// thread walks pixels tid, tid + 256, ... of the chunk with 16-byte loads of
+// dy and of the nine x pixels the taps read, keeping 9 x VEC fp32 sums;
+// the workgroup then adds its threads' sums tap by tap in a fixed LDS tree
+// and writes one partial per (tap, channel): [chunk][g][tap], or dw itself
+// when there is one chunk.
+constexpr int kDwTaps = 9;
+
+template <typename T, bool kFinal>
+__global__ __launch_bounds__(kBlock) void dw_partial_kernel(Problem p, const T *__restrict__ x,
+                                                            const T *__restrict__ dy, float *__restrict__ ws,
+                                                            T *__restrict__ dw, int ppc)
+{
+    constexpr int VEC = 16 / (int)sizeof(T);
+    __shared__ float red[VEC][kBlock];
+    const int v = blockIdx.x, ch = blockIdx.y, tid = threadIdx.x;
+    const int g0 = v * VEC;
+    const int M = p.N * p.Do * p.Ho * p.Wo;
+    const int m0 = ch * ppc;
+    const int m1 = m0 + ppc < M ? m0 + ppc : M;
+    float acc[kDwTaps][VEC];
+    int oz[kDwTaps], oy[kDwTaps], ox[kDwTaps];   // input offset of each tap (tap * dil - pad)
+#pragma unroll
+    for (int t = 0; t < kDwTaps; ++t) {
+        oz[t] = (t / (p.Y * p.X)) * p.dd - p.pd;
+        oy[t] = ((t / p.X) % p.Y) * p.dh - p.ph;
+        ox[t] = (t % p.X) * p.dw - p.pw;
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) acc[t][j] = 0.f;
+    }
+    for (int m = m0 + tid; m < m1; m += kBlock) {
+        int r = m;
+        const int ow = r % p.Wo; r /= p.Wo;
+        const int oh = r % p.Ho; r /= p.Ho;
+        const int od = r % p.Do; r /= p.Do;
+        const int n = r;
+        const uint4 draw = *reinterpret_cast<const uint4 *>(dy + (size_t)m * p.G + g0);
+        const T *dv = reinterpret_cast<const T *>(&draw);
+        float df[VEC];
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) df[j] = to_f32(dv[j]);
+#pragma unroll
+        for (int t = 0; t < kDwTaps; ++t) {
+            const int id = od * p.sd + oz[t];
+            const int ih = oh * p.sh + oy[t];
+            const int iw = ow * p.sw + ox[t];
+            if (id < 0 || id >= p.D || ih < 0 || ih >= p.H || iw < 0 || iw >= p.W) continue;
+            const uint4 xraw = *reinterpret_cast<const uint4 *>(
+                x + (((size_t)(n * p.D + id) * p.H + ih) * p.W + iw) * p.G + g0);
+            const T *xv = reinterpret_cast<const T *>(&xraw);
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) acc[t][j] = fmaf(df[j], to_f32(xv[j]), acc[t][j]);
+        }
+    }
+    const int welems = p.G * kDwTaps;
+#pragma unroll
+    for (int t = 0; t < kDwTaps; ++t) {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) red[j][tid] = acc[t][j];
+        __syncthreads();
+        for (int h = kBlock / 2; h > 0; h >>= 1) {
+            if (tid < h) {
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) red[j][tid] += red[j][tid + h];
+            }
+            __syncthreads();
+        }
+        if (tid < VEC) {
+            const int f = (g0 + tid) * kDwTaps + t;      // dw [g][k = 0][tap][c = 0]
+            if (kFinal) dw[f] = from_f32<T>(red[tid][0]);
+            else ws[(size_t)ch * welems + f] = red[tid][0];
+        }
+        __syncthreads();
+    }
+}
+
+bool dw_ok(const Problem &p)
+{
+    const int vec = 16 / elem_size(p.dtype);
+    return p.Cpg == 1 && p.Kpg == 1 && p.taps() == kDwTaps && p.G % vec == 0;
+}
+
+// chunks for the depthwise kernel: about four workgroups per CU in all, at
+// most `nch` (what the workspace holds) and at most 256 so stage 2 stays short
+template <typename T>
+hipError_t go_dw(const Problem &p, const void *x, const void *dy, void *dw, float *ws, int nch, hipStream_t s)
+{
+    constexpr int VEC = 16 / (int)sizeof(T);
+    const int nv = p.G / VEC;
+    const long long M = (long long)p.N * p.Do * p.Ho * p.Wo;
+    long long want = (1024 + nv - 1) / nv;
+    if (want > 256) want = 256;
+    if (want > nch) want = nch;
+    if (want > (M + kBlock - 1) / kBlock) want = (M + kBlock - 1) / kBlock;
+    if (want < 1) want = 1;
+    const int ppc = (int)((M + want - 1) / want);
+    const int chunks = (int)((M + ppc - 1) / ppc);
+    const int welems = p.G * kDwTaps;
+    Args a{};
+    if (chunks == 1)
+        return enqueue(dw_partial_kernel<T, true>, dim3(nv, 1), dim3(kBlock), 0, s, a, p, (const T *)x,
+                       (const T *)dy, (float *)nullptr, (T *)dw, ppc);
+    hipError_t e = enqueue(dw_partial_kernel<T, false>, dim3(nv, chunks), dim3(kBlock), 0, s, a, p, (const T *)x,
+                           (const T *)dy, ws, (T *)nullptr, ppc);
+    if (e != hipSuccess) return e;
+    return enqueue(reduce_kernel<T>, dim3((unsigned)((welems + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, a,
+                   (const float *)ws, (T *)dw, welems, chunks);
 }
 
 template <typename T>
@@ -118,6 +236,14 @@ int ideal_chunks(const Problem &p)
 
 hipError_t launch(const Problem &p, const void *x, const void *dy, void *dw, float *ws, int nch, hipStream_t s)
 {
+    const bool vec_ok = ((uintptr_t)x & 15) == 0 && ((uintptr_t)dy & 15) == 0;
+    if (dw_ok(p) && vec_ok) {
+        switch (p.dtype) {
+        case GCONV_F32: return go_dw<float>(p, x, dy, dw, ws, nch, s);
+        case GCONV_F16: return go_dw<_Float16>(p, x, dy, dw, ws, nch, s);
+        default: return go_dw<__bf16>(p, x, dy, dw, ws, nch, s);
+        }
+    }
     switch (p.dtype) {
     case GCONV_F32: return go<float>(p, x, dy, dw, ws, nch, s);
     case GCONV_F16: return go<_Float16>(p, x, dy, dw, ws, nch, s);
