@@ -14,8 +14,8 @@
 //      over one chunk of output rows (n, od, oh) into an fp32 workspace
 //      [chunk][f]; consecutive threads take consecutive input channels c,
 //      so their x reads are contiguous and their dy reads shared;
-//   2. the chunks of each element are added in a fixed order (eight running
-//      sums over the chunks, then a fixed tree) and rounded once.
+//   2. the chunks of each element are added in a fixed order (four waves
+//      with eight running sums each, then a fixed tree) and rounded once.
 // With one chunk (no workspace, or a problem with enough weight elements to
 // fill the chip) stage 1 writes dw directly.  Depthwise 3x3 problems take a
 // channel-vector form of stage 1 (below).
@@ -74,30 +74,46 @@ __global__ __launch_bounds__(kBlock) void partial_kernel(Problem p, const T *__r
     else ws[(size_t)ch * welems + f] = acc;
 }
 
+// Stage 2: a workgroup owns 64 weight elements; its four waves split their
+// chunks (wave q takes chunks q, q + 4, ...; eight running sums each, loads in
+// flight together), and the four wave sums are added in wave order through
+// LDS.  A fixed order throughout: deterministic.
+constexpr int kRedElems = 64;
+
 template <typename T>
 __global__ __launch_bounds__(kBlock) void reduce_kernel(const float *__restrict__ ws, T *__restrict__ dw,
                                                         int welems, int nch)
 {
-    const int f = blockIdx.x * kBlock + threadIdx.x;
-    if (f >= welems) return;
-    // eight independent partial sums (loads in flight together), combined
-    // in a fixed order: deterministic
+    __shared__ float part[kBlock / kRedElems][kRedElems];
+    const int l = threadIdx.x % kRedElems, q = threadIdx.x / kRedElems;
+    constexpr int NQ = kBlock / kRedElems;
+    const int f = blockIdx.x * kRedElems + l;
     float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    int ch = 0;
-    for (; ch + 8 <= nch; ch += 8)
+    if (f < welems) {
+        int ch = q;
+        for (; ch + 7 * NQ < nch; ch += 8 * NQ)
 #pragma unroll
-        for (int u = 0; u < 8; ++u) a[u] += ws[(size_t)(ch + u) * welems + f];
-    for (; ch < nch; ++ch) a[0] += ws[(size_t)ch * welems + f];
-    dw[f] = from_f32<T>(((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7])));
+            for (int u = 0; u < 8; ++u) a[u] += ws[(size_t)(ch + u * NQ) * welems + f];
+        for (; ch < nch; ch += NQ) a[0] += ws[(size_t)ch * welems + f];
+    }
+    part[q][l] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+    __syncthreads();
+    if (q == 0 && f < welems) {
+        float sum = part[0][l];
+#pragma unroll
+        for (int r = 1; r < NQ; ++r) sum += part[r][l];
+        dw[f] = from_f32<T>(sum);
+    }
 }
 
-// Depthwise 3x3 (Cpg = Kpg = 1, nine taps): workgroup (v, chunk) owns the
-// VEC channels of channel vector v over one chunk of output pixels.  Each
-// thread walks pixels tid, tid + 256, ... of the chunk with 16-byte loads of
-// dy and of the nine x pixels the taps read, keeping 9 x VEC fp32 sums;
-// the workgroup then adds its threads' sums tap by tap in a fixed LDS tree
-// and writes one partial per (tap, channel): [chunk][g][tap], or dw itself
-// when there is one chunk.
+// Depthwise 3x3 (Cpg = Kpg = 1, nine taps, at most 256 channel vectors of
+// 16 bytes): a workgroup owns every channel of one chunk of output pixels.
+// Lane `tid` takes channel vector v = tid % nv of pixel slot tid / nv, so
+// the lanes of a wave read whole pixels (all C channels, contiguous) of dy
+// and of the nine x pixels the taps read; each lane keeps 9 x VEC fp32 sums
+// over the pixels of its slot.  Per tap the slots' sums are added in slot
+// order through LDS and one partial per (tap, channel) is written:
+// [chunk][g][tap], or dw itself when there is one chunk.
 constexpr int kDwTaps = 9;
 
 template <typename T, bool kFinal>
@@ -106,8 +122,11 @@ __global__ __launch_bounds__(kBlock) void dw_partial_kernel(Problem p, const T *
                                                             T *__restrict__ dw, int ppc)
 {
     constexpr int VEC = 16 / (int)sizeof(T);
-    __shared__ float red[VEC][kBlock];
-    const int v = blockIdx.x, ch = blockIdx.y, tid = threadIdx.x;
+    __shared__ float red[kBlock * VEC];          // [slot][channel]
+    const int tid = threadIdx.x, ch = blockIdx.x;
+    const int nv = p.G / VEC, slots = kBlock / nv;
+    const int v = tid % nv, slot = tid / nv;
+    const bool active = slot < slots;
     const int g0 = v * VEC;
     const int M = p.N * p.Do * p.Ho * p.Wo;
     const int m0 = ch * ppc;
@@ -122,47 +141,56 @@ __global__ __launch_bounds__(kBlock) void dw_partial_kernel(Problem p, const T *
 #pragma unroll
         for (int j = 0; j < VEC; ++j) acc[t][j] = 0.f;
     }
-    for (int m = m0 + tid; m < m1; m += kBlock) {
-        int r = m;
-        const int ow = r % p.Wo; r /= p.Wo;
-        const int oh = r % p.Ho; r /= p.Ho;
-        const int od = r % p.Do; r /= p.Do;
-        const int n = r;
-        const uint4 draw = *reinterpret_cast<const uint4 *>(dy + (size_t)m * p.G + g0);
-        const T *dv = reinterpret_cast<const T *>(&draw);
-        float df[VEC];
+    if (active) {
+        for (int m = m0 + slot; m < m1; m += slots) {
+            int r = m;
+            const int ow = r % p.Wo; r /= p.Wo;
+            const int oh = r % p.Ho; r /= p.Ho;
+            const int od = r % p.Do; r /= p.Do;
+            const int n = r;
+            const uint4 draw = *reinterpret_cast<const uint4 *>(dy + (size_t)m * p.G + g0);
+            const T *dv = reinterpret_cast<const T *>(&draw);
+            float df[VEC];
 #pragma unroll
-        for (int j = 0; j < VEC; ++j) df[j] = to_f32(dv[j]);
+            for (int j = 0; j < VEC; ++j) df[j] = to_f32(dv[j]);
+            // all nine loads go out before any is used: a tap outside the
+            // input loads an in-bounds (clamped) pixel and its value is
+            // replaced by zero, instead of a branch around each load
+            uint4 xr[kDwTaps];
 #pragma unroll
-        for (int t = 0; t < kDwTaps; ++t) {
-            const int id = od * p.sd + oz[t];
-            const int ih = oh * p.sh + oy[t];
-            const int iw = ow * p.sw + ox[t];
-            if (id < 0 || id >= p.D || ih < 0 || ih >= p.H || iw < 0 || iw >= p.W) continue;
-            const uint4 xraw = *reinterpret_cast<const uint4 *>(
-                x + (((size_t)(n * p.D + id) * p.H + ih) * p.W + iw) * p.G + g0);
-            const T *xv = reinterpret_cast<const T *>(&xraw);
+            for (int t = 0; t < kDwTaps; ++t) {
+                const int id = od * p.sd + oz[t];
+                const int ih = oh * p.sh + oy[t];
+                const int iw = ow * p.sw + ox[t];
+                const int cd = id < 0 ? 0 : (id >= p.D ? p.D - 1 : id);
+                const int chh = ih < 0 ? 0 : (ih >= p.H ? p.H - 1 : ih);
+                const int cw = iw < 0 ? 0 : (iw >= p.W ? p.W - 1 : iw);
+                xr[t] = *reinterpret_cast<const uint4 *>(x + (((size_t)(n * p.D + cd) * p.H + chh) * p.W + cw) * p.G + g0);
+                const bool in = cd == id && chh == ih && cw == iw;
+                if (!in) xr[t] = make_uint4(0u, 0u, 0u, 0u);
+            }
 #pragma unroll
-            for (int j = 0; j < VEC; ++j) acc[t][j] = fmaf(df[j], to_f32(xv[j]), acc[t][j]);
+            for (int t = 0; t < kDwTaps; ++t) {
+                const T *xv = reinterpret_cast<const T *>(&xr[t]);
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) acc[t][j] = fmaf(df[j], to_f32(xv[j]), acc[t][j]);
+            }
         }
     }
     const int welems = p.G * kDwTaps;
 #pragma unroll
     for (int t = 0; t < kDwTaps; ++t) {
+        if (active) {
 #pragma unroll
-        for (int j = 0; j < VEC; ++j) red[j][tid] = acc[t][j];
-        __syncthreads();
-        for (int h = kBlock / 2; h > 0; h >>= 1) {
-            if (tid < h) {
-#pragma unroll
-                for (int j = 0; j < VEC; ++j) red[j][tid] += red[j][tid + h];
-            }
-            __syncthreads();
+            for (int j = 0; j < VEC; ++j) red[slot * p.G + g0 + j] = acc[t][j];
         }
-        if (tid < VEC) {
-            const int f = (g0 + tid) * kDwTaps + t;      // dw [g][k = 0][tap][c = 0]
-            if (kFinal) dw[f] = from_f32<T>(red[tid][0]);
-            else ws[(size_t)ch * welems + f] = red[tid][0];
+        __syncthreads();
+        for (int g = tid; g < p.G; g += kBlock) {
+            float sum = 0.f;
+            for (int q = 0; q < slots; ++q) sum += red[q * p.G + g];
+            const int f = g * kDwTaps + t;             // dw [g][k = 0][tap][c = 0]
+            if (kFinal) dw[f] = from_f32<T>(sum);
+            else ws[(size_t)ch * welems + f] = sum;
         }
         __syncthreads();
     }
@@ -171,34 +199,33 @@ __global__ __launch_bounds__(kBlock) void dw_partial_kernel(Problem p, const T *
 bool dw_ok(const Problem &p)
 {
     const int vec = 16 / elem_size(p.dtype);
-    return p.Cpg == 1 && p.Kpg == 1 && p.taps() == kDwTaps && p.G % vec == 0;
+    return p.Cpg == 1 && p.Kpg == 1 && p.taps() == kDwTaps && p.G % vec == 0 && p.G / vec <= kBlock;
 }
 
-// chunks for the depthwise kernel: about four workgroups per CU in all, at
-// most `nch` (what the workspace holds) and at most 256 so stage 2 stays short
+// chunks for the depthwise kernel: two workgroups per CU, at most
+// `nch` (what the workspace holds) and at most 512 so stage 2 stays short
 template <typename T>
 hipError_t go_dw(const Problem &p, const void *x, const void *dy, void *dw, float *ws, int nch, hipStream_t s)
 {
     constexpr int VEC = 16 / (int)sizeof(T);
-    const int nv = p.G / VEC;
+    const int slots = kBlock / (p.G / VEC);
     const long long M = (long long)p.N * p.Do * p.Ho * p.Wo;
-    long long want = (1024 + nv - 1) / nv;
-    if (want > 256) want = 256;
+    long long want = 512;
     if (want > nch) want = nch;
-    if (want > (M + kBlock - 1) / kBlock) want = (M + kBlock - 1) / kBlock;
+    if (want > (M + slots - 1) / slots) want = (M + slots - 1) / slots;
     if (want < 1) want = 1;
     const int ppc = (int)((M + want - 1) / want);
     const int chunks = (int)((M + ppc - 1) / ppc);
     const int welems = p.G * kDwTaps;
     Args a{};
     if (chunks == 1)
-        return enqueue(dw_partial_kernel<T, true>, dim3(nv, 1), dim3(kBlock), 0, s, a, p, (const T *)x,
+        return enqueue(dw_partial_kernel<T, true>, dim3(1), dim3(kBlock), 0, s, a, p, (const T *)x,
                        (const T *)dy, (float *)nullptr, (T *)dw, ppc);
-    hipError_t e = enqueue(dw_partial_kernel<T, false>, dim3(nv, chunks), dim3(kBlock), 0, s, a, p, (const T *)x,
+    hipError_t e = enqueue(dw_partial_kernel<T, false>, dim3(chunks), dim3(kBlock), 0, s, a, p, (const T *)x,
                            (const T *)dy, ws, (T *)nullptr, ppc);
     if (e != hipSuccess) return e;
-    return enqueue(reduce_kernel<T>, dim3((unsigned)((welems + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, a,
-                   (const float *)ws, (T *)dw, welems, chunks);
+    return enqueue(reduce_kernel<T>, dim3((unsigned)((welems + kRedElems - 1) / kRedElems)), dim3(kBlock), 0, s,
+                   a, (const float *)ws, (T *)dw, welems, chunks);
 }
 
 template <typename T>
@@ -216,16 +243,22 @@ hipError_t go(const Problem &p, const void *x, const void *dy, void *dw, float *
     hipError_t e = enqueue(partial_kernel<T, false>, grid, dim3(kBlock), 0, s, a, p, (const T *)x,
                            (const T *)dy, ws, (T *)nullptr, welems, rpc);
     if (e != hipSuccess) return e;
-    return enqueue(reduce_kernel<T>, dim3((unsigned)((welems + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, a,
-                   (const float *)ws, (T *)dw, welems, nch);
+    return enqueue(reduce_kernel<T>, dim3((unsigned)((welems + kRedElems - 1) / kRedElems)), dim3(kBlock), 0, s,
+                   a, (const float *)ws, (T *)dw, welems, nch);
 }
 
 }  // namespace
 
 // Chunks that fill the chip: about 256 K stage-1 threads, at most one chunk
-// per output row, at most 65535 (the grid's y extent).
+// per output row, at most 65535 (the grid's y extent); for the depthwise
+// kernel, up to 512 workgroups of one chunk each.
 int ideal_chunks(const Problem &p)
 {
+    if (dw_ok(p)) {   // the depthwise kernel: up to 512 workgroups, one chunk each
+        const long long slots = kBlock / (p.G / (16 / elem_size(p.dtype)));
+        const long long m = ((long long)p.N * p.Do * p.Ho * p.Wo + slots - 1) / slots;
+        return (int)(m < 512 ? (m < 1 ? 1 : m) : 512);
+    }
     const long long welems = (long long)p.G * p.Kpg * p.taps() * p.Cpg;
     const long long rows = (long long)p.N * p.Do * p.Ho;
     long long n = (262144 + welems - 1) / welems;
