@@ -40,7 +40,6 @@ namespace {
 
 constexpr int kBlock = 256;
 constexpr int kWaves = 4;
-constexpr int kMaxTiles = 14;         // M tiles (16 pixels) per item
 constexpr int kCUs = 256;              // MI355X compute units
 constexpr int kMaxLds = 160 * 1024;
 constexpr unsigned kOob = 0x80000000u;
