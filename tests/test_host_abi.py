@@ -233,3 +233,19 @@ def test_bwd_data_validates_before_any_launch():
     assert G.gconv_bwd_data(ok, 0, 16, 16, None, 0) == G.GCONV_ERR_NULL_PTR
     assert G.gconv_bwd_data_direct(ok, 16, 16, 0) == G.GCONV_ERR_NULL_PTR
     assert G.gconv_bwd_data(ok, 17, 16, 16, None, 0) == G.GCONV_ERR_MISALIGNED
+
+
+def test_bwd_weight_workspace_and_validation():
+    # depthwise 3x3 (channel-vector route): up to 512 chunks of G * 9 fp32 partial sums
+    d = G.make_desc(2, "f16", 2, 16, 16, 16, (13, 17), (3, 3), (1, 1), (1, 1), (1, 1))
+    n = G.gconv_bwd_weight_workspace(d)
+    assert n > 0 and n % (16 * 9 * 4) == 0 and n // (16 * 9 * 4) <= 512
+    # a problem whose weights alone fill the chip needs no partial sums
+    big = G.make_desc(2, "bf16", 64, 8, 1024, 1024, (14, 14), (3, 3), (1, 1), (1, 1), (1, 1))
+    assert G.gconv_bwd_weight_workspace(big) == 0
+    bad = G.make_desc(2, "f16", 1, 3, 8, 9, (9, 9), (3, 3), (1, 1), (1, 1), (1, 1))   # C % G != 0
+    with pytest.raises(G.GconvError):
+        G.gconv_bwd_weight_workspace(bad)
+    assert G.gconv_bwd_weight(bad, 16, 16, 16, None, 0) == G.GCONV_ERR_BAD_DESC
+    assert G.gconv_bwd_weight(d, 0, 16, 16, None, 0) == G.GCONV_ERR_NULL_PTR
+    assert G.gconv_bwd_weight(d, 16, 17, 16, None, 0) == G.GCONV_ERR_MISALIGNED
