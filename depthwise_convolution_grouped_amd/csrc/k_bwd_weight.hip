@@ -74,6 +74,86 @@ __global__ __launch_bounds__(kBlock) void partial_kernel(Problem p, const T *__r
     else ws[(size_t)ch * welems + f] = acc;
 }
 
+// Grouped, half types, Cpg % 8 == 0 and Kpg % 4 == 0: a register-tiled
+// stage 1.  Thread (chunk, tile) owns 4 output channels x 8 input channels
+// of one tap of one group; per output pixel it loads the 8 input channels
+// of x (16 bytes) and the 4 output channels of dy (8 bytes) and does 32
+// FMAs.  Consecutive threads take consecutive 8-channel vectors of x, so a
+// wave's x loads are contiguous runs.  Partial sums go to [chunk][f] as in
+// the plain kernel (or to dw with one chunk).
+template <typename T, bool kFinal>
+__global__ __launch_bounds__(kBlock) void tile_partial_kernel(Problem p, const T *__restrict__ x,
+                                                              const T *__restrict__ dy, float *__restrict__ ws,
+                                                              T *__restrict__ dw, int ntiles, int rows_per_chunk)
+{
+    const int tile = blockIdx.x * kBlock + threadIdx.x;
+    const int ch = blockIdx.y;
+    if (tile >= ntiles) return;
+    const int ncv = p.Cpg / 8, nkt = p.Kpg / 4;
+    int r = tile;
+    const int cv = r % ncv;  r /= ncv;
+    const int kt = r % nkt;  r /= nkt;
+    const int xx = r % p.X;  r /= p.X;
+    const int yy = r % p.Y;  r /= p.Y;
+    const int z = r % p.Z;   r /= p.Z;
+    const int g = r;
+    const int c0 = cv * 8, k0 = kt * 4;
+    const int C = p.G * p.Cpg, K = p.G * p.Kpg;
+    const int rows = p.N * p.Do * p.Ho;
+    const int r0 = ch * rows_per_chunk;
+    const int r1 = r0 + rows_per_chunk < rows ? r0 + rows_per_chunk : rows;
+    int ow_lo = 0, ow_hi = p.Wo;
+    {
+        const int off = xx * p.dw - p.pw;
+        if (off < 0) ow_lo = (-off + p.sw - 1) / p.sw;
+        const int lim = p.W - off;
+        const int hi = lim <= 0 ? 0 : (lim + p.sw - 1) / p.sw;
+        if (hi < ow_hi) ow_hi = hi;
+    }
+    float acc[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
+    for (int rr = r0; rr < r1; ++rr) {
+        const int oh = rr % p.Ho, t = rr / p.Ho;
+        const int od = t % p.Do, n = t / p.Do;
+        const int id = od * p.sd - p.pd + z * p.dd;
+        const int ih = oh * p.sh - p.ph + yy * p.dh;
+        if (id < 0 || id >= p.D || ih < 0 || ih >= p.H) continue;
+        const T *dyr = dy + ((size_t)((n * p.Do + od) * p.Ho + oh) * p.Wo) * K + g * p.Kpg + k0;
+        const T *xr = x + ((size_t)((n * p.D + id) * p.H + ih) * p.W) * C + g * p.Cpg + c0;
+        for (int ow = ow_lo; ow < ow_hi; ++ow) {
+            const int iw = ow * p.sw - p.pw + xx * p.dw;
+            const uint4 xv4 = *reinterpret_cast<const uint4 *>(xr + (size_t)iw * C);
+            const uint2 dv2 = *reinterpret_cast<const uint2 *>(dyr + (size_t)ow * K);
+            const T *xv = reinterpret_cast<const T *>(&xv4);
+            const T *dv = reinterpret_cast<const T *>(&dv2);
+            float xf[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) xf[j] = to_f32(xv[j]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float d = to_f32(dv[i]);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(d, xf[j], acc[i][j]);
+            }
+        }
+    }
+    const int T9 = p.Z * p.Y * p.X;
+    const int welems = p.G * p.Kpg * T9 * p.Cpg;
+    const int tap = (z * p.Y + yy) * p.X + xx;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int f0 = ((g * p.Kpg + k0 + i) * T9 + tap) * p.Cpg + c0;   // dw [g][k][tap][c]
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (kFinal) dw[f0 + j] = from_f32<T>(acc[i][j]);
+            else ws[(size_t)ch * welems + f0 + j] = acc[i][j];
+        }
+    }
+}
+
 // Stage 2: a workgroup owns 64 weight elements; its four waves split their
 // chunks (wave q takes chunks q, q + 4, ...; eight running sums each, loads in
 // flight together), and the four wave sums are added in wave order through
@@ -228,6 +308,11 @@ hipError_t go_dw(const Problem &p, const void *x, const void *dy, void *dw, floa
                    a, (const float *)ws, (T *)dw, welems, chunks);
 }
 
+bool tile_ok(const Problem &p)
+{
+    return p.dtype != GCONV_F32 && p.Cpg % 8 == 0 && p.Kpg % 4 == 0;
+}
+
 template <typename T>
 hipError_t go(const Problem &p, const void *x, const void *dy, void *dw, float *ws, int nch, hipStream_t s)
 {
@@ -237,6 +322,18 @@ hipError_t go(const Problem &p, const void *x, const void *dy, void *dw, float *
     nch = (rows + rpc - 1) / rpc;                  // no empty chunk
     const dim3 grid((unsigned)((welems + kBlock - 1) / kBlock), (unsigned)nch);
     Args a{};
+    if (tile_ok(p) && ((uintptr_t)x & 15) == 0 && ((uintptr_t)dy & 7) == 0) {
+        const int ntiles = welems / 32;
+        const dim3 tg((unsigned)((ntiles + kBlock - 1) / kBlock), (unsigned)nch);
+        if (nch == 1)
+            return enqueue(tile_partial_kernel<T, true>, tg, dim3(kBlock), 0, s, a, p, (const T *)x, (const T *)dy,
+                           (float *)nullptr, (T *)dw, ntiles, rpc);
+        hipError_t e = enqueue(tile_partial_kernel<T, false>, tg, dim3(kBlock), 0, s, a, p, (const T *)x,
+                               (const T *)dy, ws, (T *)nullptr, ntiles, rpc);
+        if (e != hipSuccess) return e;
+        return enqueue(reduce_kernel<T>, dim3((unsigned)((welems + kRedElems - 1) / kRedElems)), dim3(kBlock), 0,
+                       s, a, (const float *)ws, (T *)dw, welems, nch);
+    }
     if (nch == 1)
         return enqueue(partial_kernel<T, true>, grid, dim3(kBlock), 0, s, a, p, (const T *)x, (const T *)dy,
                        (float *)nullptr, (T *)dw, welems, rpc);
@@ -249,8 +346,9 @@ hipError_t go(const Problem &p, const void *x, const void *dy, void *dw, float *
 
 }  // namespace
 
-// Chunks that fill the chip: about 256 K stage-1 threads, at most one chunk
-// per output row, at most 65535 (the grid's y extent); for the depthwise
+// Chunks that fill the chip: about 256 K stage-1 threads (one per weight
+// element, or per 4 x 8 tile on the tiled route), at most one chunk per
+// output row, at most 65535 (the grid's y extent); for the depthwise
 // kernel, up to 512 workgroups of one chunk each.
 int ideal_chunks(const Problem &p)
 {
@@ -261,7 +359,8 @@ int ideal_chunks(const Problem &p)
     }
     const long long welems = (long long)p.G * p.Kpg * p.taps() * p.Cpg;
     const long long rows = (long long)p.N * p.Do * p.Ho;
-    long long n = (262144 + welems - 1) / welems;
+    const long long threads = tile_ok(p) ? welems / 32 : welems;   // stage-1 threads per chunk
+    long long n = (262144 + threads - 1) / threads;
     if (n > rows) n = rows;
     if (n > 65535) n = 65535;
     return n < 1 ? 1 : (int)n;
