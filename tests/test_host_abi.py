@@ -240,9 +240,13 @@ def test_bwd_weight_workspace_and_validation():
     d = G.make_desc(2, "f16", 2, 16, 16, 16, (13, 17), (3, 3), (1, 1), (1, 1), (1, 1))
     n = G.gconv_bwd_weight_workspace(d)
     assert n > 0 and n % (16 * 9 * 4) == 0 and n // (16 * 9 * 4) <= 512
-    # a problem whose weights alone fill the chip needs no partial sums
-    big = G.make_desc(2, "bf16", 64, 8, 1024, 1024, (14, 14), (3, 3), (1, 1), (1, 1), (1, 1))
+    # one thread per weight element (fp32): weights that alone fill the chip need no partial sums
+    big = G.make_desc(2, "f32", 64, 8, 1024, 1024, (14, 14), (3, 3), (1, 1), (1, 1), (1, 1))
     assert G.gconv_bwd_weight_workspace(big) == 0
+    # the 4 x 8 tiled route (bf16, Cpg % 8 == 0, Kpg % 4 == 0) has 32x fewer threads: it chunks
+    tiled = G.make_desc(2, "bf16", 64, 8, 1024, 1024, (14, 14), (3, 3), (1, 1), (1, 1), (1, 1))
+    wbytes = 1024 * 9 * 128 * 4
+    assert G.gconv_bwd_weight_workspace(tiled) == 8 * wbytes
     bad = G.make_desc(2, "f16", 1, 3, 8, 9, (9, 9), (3, 3), (1, 1), (1, 1), (1, 1))   # C % G != 0
     with pytest.raises(G.GconvError):
         G.gconv_bwd_weight_workspace(bad)
