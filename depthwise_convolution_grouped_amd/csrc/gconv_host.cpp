@@ -68,10 +68,34 @@ int check_desc(const gconv_desc *d, int64_t out[3])
     int64_t span = 0;
     for (int a = 0; a < 3; ++a)  // padded extent must also stay in int32
         span = span > d->in[a] + 2 * d->pad[a] ? span : d->in[a] + 2 * d->pad[a];
-    if (x_el >= kMaxElems || y_el >= kMaxElems || w_el >= kMaxElems || span >= kMaxElems ||
-        d->K >= kMaxElems || d->C >= kMaxElems || Kpg >= kMaxElems)
+    // x and y may exceed 2^31 elements as a batch: calls then split the batch
+    // into launches of whole images (every launch indexes in 32 bits), so
+    // only one image of each, and w, must stay below
+    const int64_t x_img = x_el / d->N, y_img = y_el / d->N;
+    if (x_img >= kMaxElems || y_img >= kMaxElems || w_el >= kMaxElems || span >= kMaxElems ||
+        d->K >= kMaxElems || d->C >= kMaxElems || Kpg >= kMaxElems || d->N >= kMaxElems || x_el >= INT64_MAX / 4 ||
+        y_el >= INT64_MAX / 4)
         return GCONV_ERR_TOO_LARGE;
     return GCONV_OK;
+}
+
+// Images per launch: the whole batch when x and y each have < 2^31
+// elements, else the most whole images that keep both below.
+int64_t images_per_launch(const gconv_desc *d, const int64_t out[3])
+{
+    const int64_t x_img = d->in[0] * d->in[1] * d->in[2] * d->C;
+    const int64_t y_img = out[0] * out[1] * out[2] * d->K;
+    const int64_t nx = (kMaxElems - 1) / x_img, ny = (kMaxElems - 1) / y_img;
+    const int64_t n = nx < ny ? nx : ny;
+    return n < d->N ? n : d->N;
+}
+
+// The descriptor of one launch: d with a batch of n images.
+gconv_desc with_batch(const gconv_desc *d, int64_t n)
+{
+    gconv_desc t = *d;
+    t.N = n;
+    return t;
 }
 
 Problem to_problem(const gconv_desc *d, const int64_t out[3])
@@ -142,6 +166,22 @@ int run(const gconv_desc *d, int path, const void *x, const void *w, const void 
     int rc = check_desc(d, out);
     if (rc != GCONV_OK) return rc;
     if (!x || !w || !y) return GCONV_ERR_NULL_PTR;
+    const int64_t nl = images_per_launch(d, out);
+    if (nl < d->N) {
+        // a batch of >= 2^31 elements: consecutive launches of nl whole images,
+        // the start event bound to the first and the stop event to the last
+        const size_t es = (size_t)elem_size(d->dtype);
+        const size_t x_img = (size_t)(d->in[0] * d->in[1] * d->in[2] * d->C) * es;
+        const size_t y_img = (size_t)(out[0] * out[1] * out[2] * d->K) * es;
+        for (int64_t n0 = 0; n0 < d->N; n0 += nl) {
+            const int64_t n = d->N - n0 < nl ? d->N - n0 : nl;
+            const gconv_desc t = with_batch(d, n);
+            rc = run(&t, path, (const char *)x + (size_t)n0 * x_img, w, bias, (char *)y + (size_t)n0 * y_img,
+                     stream, n0 == 0 ? ev_start : nullptr, n0 + n >= d->N ? ev_stop : nullptr);
+            if (rc != GCONV_OK) return rc;
+        }
+        return GCONV_OK;
+    }
     Problem p = to_problem(d, out);
     const uintptr_t es = (uintptr_t)elem_size(p.dtype);
     if (!aligned(x, es) || !aligned(w, es) || !aligned(y, es) || (bias && !aligned(bias, es)))
@@ -210,6 +250,20 @@ int run_bwd_data(const gconv_desc *d, const void *dy, const void *w, void *dx, v
     if (!dy || !w || !dx) return GCONV_ERR_NULL_PTR;
     const uintptr_t es = (uintptr_t)elem_size(d->dtype);
     if (!aligned(dy, es) || !aligned(w, es) || !aligned(dx, es)) return GCONV_ERR_MISALIGNED;
+    const int64_t nl = images_per_launch(d, out);
+    if (nl < d->N) {
+        // a batch of >= 2^31 elements: launches of nl whole images
+        const size_t x_img = (size_t)(d->in[0] * d->in[1] * d->in[2] * d->C) * es;
+        const size_t y_img = (size_t)(out[0] * out[1] * out[2] * d->K) * es;
+        for (int64_t n0 = 0; n0 < d->N; n0 += nl) {
+            const int64_t n = d->N - n0 < nl ? d->N - n0 : nl;
+            const gconv_desc t = with_batch(d, n);
+            rc = run_bwd_data(&t, (const char *)dy + (size_t)n0 * y_img, w, (char *)dx + (size_t)n0 * x_img, ws,
+                              ws_bytes, direct, stream);
+            if (rc != GCONV_OK) return rc;
+        }
+        return GCONV_OK;
+    }
     const Problem p = to_problem(d, out);
     hipStream_t s = (hipStream_t)stream;
     if (!direct && bwd_as_forward(d) && ws && ws_bytes >= weight_bytes(d) && aligned(ws, 16)) {
@@ -232,6 +286,8 @@ int run_bwd_weight(const gconv_desc *d, const void *x, const void *dy, void *dw,
     int64_t out[3];
     int rc = check_desc(d, out);
     if (rc != GCONV_OK) return rc;
+    // its reduction runs over the whole batch: no split into launches
+    if (images_per_launch(d, out) < d->N) return GCONV_ERR_TOO_LARGE;
     if (!x || !dy || !dw) return GCONV_ERR_NULL_PTR;
     const uintptr_t es = (uintptr_t)elem_size(d->dtype);
     if (!aligned(x, es) || !aligned(dy, es) || !aligned(dw, es)) return GCONV_ERR_MISALIGNED;
@@ -267,12 +323,14 @@ GCONV_API int gconv_out_dims(const gconv_desc *d, int64_t out[3])
     return GCONV_OK;
 }
 
+// Selection and plans describe one launch (the first, for a split batch).
 GCONV_API int gconv_select_path(const gconv_desc *d)
 {
     int64_t out[3];
     int rc = check_desc(d, out);
     if (rc != GCONV_OK) return rc;
-    return select(to_problem(d, out));
+    const gconv_desc t = with_batch(d, images_per_launch(d, out));
+    return select(to_problem(&t, out));
 }
 
 GCONV_API int gconv_path_supported(const gconv_desc *d, int path)
@@ -281,7 +339,8 @@ GCONV_API int gconv_path_supported(const gconv_desc *d, int path)
     int rc = check_desc(d, out);
     if (rc != GCONV_OK) return rc;
     if (path < 0 || path >= GCONV_NUM_PATHS) return GCONV_ERR_BAD_PATH;
-    return path_ok(to_problem(d, out), path) ? 1 : 0;
+    const gconv_desc t = with_batch(d, images_per_launch(d, out));
+    return path_ok(to_problem(&t, out), path) ? 1 : 0;
 }
 
 GCONV_API int gconv_get_plan(const gconv_desc *d, int path, gconv_plan *plan)
@@ -290,7 +349,8 @@ GCONV_API int gconv_get_plan(const gconv_desc *d, int path, gconv_plan *plan)
     int64_t out[3];
     int rc = check_desc(d, out);
     if (rc != GCONV_OK) return rc;
-    Problem p = to_problem(d, out);
+    const gconv_desc t = with_batch(d, images_per_launch(d, out));
+    Problem p = to_problem(&t, out);
     if (path == GCONV_PATH_AUTO) path = select(p);
     else if (path < 0 || path >= GCONV_NUM_PATHS) return GCONV_ERR_BAD_PATH;
     else if (!path_ok(p, path)) return GCONV_ERR_PATH_UNSUPPORTED;

@@ -64,7 +64,9 @@ typedef enum gconv_status {
                                        negative pad, 2D with depth entries set */
     GCONV_ERR_BAD_OUT_DIMS = -2,    /* an output extent would be <= 0 */
     GCONV_ERR_NULL_PTR = -3,        /* desc, x, w or y is NULL */
-    GCONV_ERR_TOO_LARGE = -4,       /* a tensor has >= 2^31 elements */
+    GCONV_ERR_TOO_LARGE = -4,       /* one image of x or y, or w, has >= 2^31 elements (a
+                                       larger batch is split into launches of whole images;
+                                       backward weight takes no split), or N >= 2^31 */
     GCONV_ERR_MISALIGNED = -5,      /* a pointer is not aligned as the path needs */
     GCONV_ERR_BAD_PATH = -6,        /* unknown path id */
     GCONV_ERR_PATH_UNSUPPORTED = -7,/* forced path cannot run this problem */
@@ -132,7 +134,13 @@ int gconv_get_plan(const gconv_desc *d, int path, gconv_plan *plan);
 /* Forward convolution, asynchronous on `stream` (a hipStream_t; NULL = the
  * null stream).  x, w, bias (NULL = no bias) and y are device pointers in the
  * layouts above, aligned to the element size.  Exactly one kernel is
- * launched; the caller synchronises the stream before reading y.  Results
+ * launched when x and y each have < 2^31 elements; a larger batch runs as
+ * consecutive launches of as many whole images as keep both below (every
+ * launch indexes in 32 bits), which gconv_select_path and gconv_get_plan
+ * describe.  The CK Python examples README's split_image option
+ * (Config-options harness) splits spatial dims for large tensors; here the
+ * batch is split instead, which needs no halo exchange between launches,
+ * and one image of >= 2^31 elements is rejected.  The caller synchronises the stream before reading y.  Results
  * are bitwise deterministic from run to run (no atomics). */
 int gconv_fwd(const gconv_desc *d, const void *x, const void *w,
               const void *bias, void *y, void *stream);

@@ -71,7 +71,8 @@ def test_valid_descriptor():
     (dict(filt=(3, 0)), G.GCONV_ERR_BAD_DESC),
     (dict(spatial=(2, 2), pad=(0, 0)), G.GCONV_ERR_BAD_OUT_DIMS),
     (dict(spatial=(5, 5), pad=(0, 0), dil=(3, 3)), G.GCONV_ERR_BAD_OUT_DIMS),
-    (dict(N=1 << 20, spatial=(1024, 1024)), G.GCONV_ERR_TOO_LARGE),
+    (dict(N=1 << 20, spatial=(1024, 1024)), G.GCONV_OK),           # split into launches of whole images
+    (dict(N=1, spatial=(65536, 65536)), G.GCONV_ERR_TOO_LARGE),    # one image of x has >= 2^31 elements
     (dict(N=1 << 40), G.GCONV_ERR_TOO_LARGE),
 ])
 def test_validation_errors(kw, status):
@@ -253,3 +254,15 @@ def test_bwd_weight_workspace_and_validation():
     assert G.gconv_bwd_weight(bad, 16, 16, 16, None, 0) == G.GCONV_ERR_BAD_DESC
     assert G.gconv_bwd_weight(d, 0, 16, 16, None, 0) == G.GCONV_ERR_NULL_PTR
     assert G.gconv_bwd_weight(d, 16, 17, 16, None, 0) == G.GCONV_ERR_MISALIGNED
+
+
+def test_large_batch_splits_into_whole_image_launches():
+    # a batch of x with >= 2^31 elements is valid; selection and plans describe one launch
+    d = G.make_desc(2, "f16", 33, 64, 64, 64, (1024, 1024), (3, 3), (1, 1), (1, 1), (1, 1))
+    assert G.gconv_validate(d) == G.GCONV_OK
+    assert G.gconv_select_path(d) == G.GCONV_PATH_DEPTHWISE
+    plan = G.gconv_get_plan(d)
+    small = G.make_desc(2, "f16", 31, 64, 64, 64, (1024, 1024), (3, 3), (1, 1), (1, 1), (1, 1))
+    assert plan == G.gconv_get_plan(small)        # (2^31 - 1) // 2^26 = 31 images per launch
+    # backward weight reduces over the whole batch: no split
+    assert G.gconv_bwd_weight(d, 16, 16, 16, None, 0) == G.GCONV_ERR_TOO_LARGE
