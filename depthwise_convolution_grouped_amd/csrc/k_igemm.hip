@@ -1,5 +1,5 @@
 // Implicit-GEMM grouped convolution on the matrix cores (fp16 / bf16, 2D and
-// 3D), for groups with many channels (Cpg % 32 == 0, Kpg % 64 == 0).
+// 3D), for groups with many channels (Cpg % 32 == 0, Kpg % 32 == 0).
 //
 // Per group g the convolution is a GEMM: M = output pixels (N * Do * Ho *
 // Wo), N = Kpg output channels, K = taps * Cpg.  The group is the grid's z
@@ -86,7 +86,8 @@ template <> struct Mfma<__bf16> {
     }
 };
 
-// BN: output channels per tile (64 or 128); KT: K per stage (32 or 64).
+// BN: output channels per tile (32, 64 or 128; each of the two waves along
+// N takes BN / 2); KT: K per stage (32 or 64).
 template <typename T, int BN, int KT>
 __global__ __launch_bounds__(kBlock) void kernel(Params q, const T *__restrict__ x,
                                                  const T *__restrict__ w,
@@ -263,13 +264,13 @@ struct Config {
 bool configure(const Problem &p, Config &c)
 {
     if (p.dtype != GCONV_F16 && p.dtype != GCONV_BF16) return false;
-    if (p.Cpg % 32 != 0 || p.Kpg % 64 != 0) return false;
+    if (p.Cpg % 32 != 0 || p.Kpg % 32 != 0) return false;
     const long long xb = (long long)p.N * p.D * p.H * p.W * p.C() * 2;
     const long long wb = (long long)p.K() * p.taps() * p.Cpg * 2;
     if (xb >= (1LL << 31) || wb >= (1LL << 31)) return false;
     const long long M = (long long)p.N * p.Do * p.Ho * p.Wo;
     if (M >= (1LL << 31)) return false;
-    c.BN = p.Kpg % 128 == 0 ? 128 : 64;
+    c.BN = p.Kpg % 128 == 0 ? 128 : (p.Kpg % 64 == 0 ? 64 : 32);
     c.KT = p.Cpg % 64 == 0 ? 64 : 32;
     c.mtiles = (int)((M + BM - 1) / BM);
     c.ntiles = p.Kpg / c.BN;
@@ -306,7 +307,8 @@ template <typename T>
 hipError_t go(const Problem &p, const Config &c, const Args &a, hipStream_t s)
 {
     if (c.BN == 128) return c.KT == 64 ? go3<T, 128, 64>(p, c, a, s) : go3<T, 128, 32>(p, c, a, s);
-    return c.KT == 64 ? go3<T, 64, 64>(p, c, a, s) : go3<T, 64, 32>(p, c, a, s);
+    if (c.BN == 64) return c.KT == 64 ? go3<T, 64, 64>(p, c, a, s) : go3<T, 64, 32>(p, c, a, s);
+    return c.KT == 64 ? go3<T, 32, 64>(p, c, a, s) : go3<T, 32, 32>(p, c, a, s);
 }
 
 }  // namespace

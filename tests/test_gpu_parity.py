@@ -329,3 +329,29 @@ def test_igemm_shapes(case, path):
     y = run_and_fetch(p, t, pid)
     r = U.check(y, ref, scale, p.dtype, "%s %r" % (path, IGEMM_CASES[case]))
     print("%s case %d max err/tol %.3f plan %s" % (path, case, r, G.gconv_get_plan(d, pid)))
+
+
+IGEMM_ONLY_CASES = [
+    # groups of 32 output channels: only the M-tiled implicit GEMM takes them (32-channel tiles)
+    (2, "bf16", 4, 8, 32, 32, (1, 28, 28), (1, 3, 3), 1, 1, 1, True),
+    (2, "f16", 2, 3, 64, 96, (1, 13, 11), (1, 3, 3), 2, 1, 1, False),      # Kpg = 96: three 32-channel tiles
+    (3, "bf16", 1, 2, 32, 32, (4, 6, 7), (3, 3, 3), 1, 1, (1, 2, 1), True),
+]
+
+
+@pytest.mark.parametrize("case", range(len(IGEMM_ONLY_CASES)))
+def test_igemm_32_channel_tiles(case):
+    nd, dt, N, Gr, Cpg, Kpg, sp, fl, s, pd, dl, bias = IGEMM_ONLY_CASES[case]
+    tr = lambda v: (v if isinstance(v, tuple) else (v, v, v))
+    st, pad, dil = tr(s), tr(pd), tr(dl)
+    if nd == 2:
+        st, pad, dil = (1, st[1], st[2]), (0, pad[1], pad[2]), (1, dil[1], dil[2])
+    p = inputs.Problem(nd, dt, N, Gr, Gr * Cpg, Gr * Kpg, sp, fl, st, pad, dil, bias)
+    d = G.desc_from_problem(p)
+    assert G.gconv_select_path(d) == G.GCONV_PATH_IGEMM
+    t = inputs.make_tensors(p, 7500 + case)
+    sa, pa, da = p.spatial_args()
+    ref, scale = oracle.conv_fwd(*U.oracle_inputs(p, t), p.G, sa, pa, da)
+    y = run_and_fetch(p, t, G.GCONV_PATH_IGEMM)
+    r = U.check(y, ref, scale, p.dtype, "igemm %r" % (IGEMM_ONLY_CASES[case],))
+    print("igemm 32-channel case %d max err/tol %.3f plan %s" % (case, r, G.gconv_get_plan(d)))
