@@ -217,7 +217,7 @@ struct Config {
 
 int pick_nmf(int nmf)
 {
-    const int opts[] = {5, 7, 9, 16};
+    const int opts[] = {5, 7, 9, 16, 28};
     for (int o : opts)
         if (nmf <= o) return o;
     return 0;
@@ -332,7 +332,8 @@ hipError_t go3(const Problem &p, const Config &c, const Args &a, hipStream_t s)
     case 5: return go4<T, 5, 4, CPGC>(p, c, a, s);
     case 7: return go4<T, 7, 2, CPGC>(p, c, a, s);
     case 9: return go4<T, 9, 2, CPGC>(p, c, a, s);
-    default: return go4<T, 16, 1, CPGC>(p, c, a, s);
+    case 16: return go4<T, 16, 1, CPGC>(p, c, a, s);
+    default: return go4<T, 28, 1, CPGC>(p, c, a, s);
     }
 }
 

@@ -256,6 +256,8 @@ def test_depthwise_shapes(case):
 SMALLG_CASES = [
     # ndim, dtype, N, G, Cpg, Kpg, spatial (D,H,W), filt (Z,Y,X), stride, pad, dil, bias
     (2, "bf16", 2, 32, 8, 8, (1, 13, 17), (1, 3, 3), 1, 1, 1, False),   # ResNeXt-like, ragged tiles
+    (3, "f16", 2, 32, 4, 2, (5, 9, 11), (3, 3, 3), 1, 1, 1, True),     # 27 x 4 K slices: the 28-fragment instance
+    (3, "bf16", 1, 16, 4, 2, (4, 7, 6), (3, 3, 3), 1, 1, 1, False),
     (2, "f16", 1, 8, 8, 8, (1, 9, 30), (1, 3, 3), 2, 1, 1, True),
     (2, "bf16", 1, 16, 4, 4, (1, 11, 11), (1, 3, 3), 1, 2, 2, True),     # dilation 2
     (2, "f16", 2, 4, 16, 16, (1, 7, 9), (1, 3, 3), 1, 1, 1, True),      # one group per tile
