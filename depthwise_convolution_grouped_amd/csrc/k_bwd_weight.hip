@@ -154,20 +154,21 @@ __global__ __launch_bounds__(kBlock) void tile_partial_kernel(Problem p, const T
     }
 }
 
-// Stage 2: a workgroup owns 64 weight elements; its four waves split their
-// chunks (wave q takes chunks q, q + 4, ...; eight running sums each, loads in
-// flight together), and the four wave sums are added in wave order through
-// LDS.  A fixed order throughout: deterministic.
-constexpr int kRedElems = 64;
-
-template <typename T>
+// Stage 2: a workgroup owns E weight elements; its kBlock / E lane groups
+// split their chunks (group q takes chunks q, q + kBlock / E, ...; eight
+// running sums each, loads in flight together), and the group sums are added
+// in group order through LDS.  A fixed order throughout: deterministic.  E is
+// 64 (whole 256-byte rows of the workspace per wave) unless the weight is
+// small, where 16 gives four times the workgroups and a quarter of the
+// dependent rounds per lane.
+template <typename T, int E>
 __global__ __launch_bounds__(kBlock) void reduce_kernel(const float *__restrict__ ws, T *__restrict__ dw,
                                                         int welems, int nch)
 {
-    __shared__ float part[kBlock / kRedElems][kRedElems];
-    const int l = threadIdx.x % kRedElems, q = threadIdx.x / kRedElems;
-    constexpr int NQ = kBlock / kRedElems;
-    const int f = blockIdx.x * kRedElems + l;
+    constexpr int NQ = kBlock / E;
+    __shared__ float part[NQ][E];
+    const int l = threadIdx.x % E, q = threadIdx.x / E;
+    const int f = blockIdx.x * E + l;
     float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (f < welems) {
         int ch = q;
@@ -186,6 +187,17 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const float *__restrict_
     }
 }
 
+template <typename T>
+hipError_t reduce(const float *ws, T *dw, int welems, int nch, hipStream_t s)
+{
+    Args a{};
+    if (welems < 8192)
+        return enqueue(reduce_kernel<T, 16>, dim3((unsigned)((welems + 15) / 16)), dim3(kBlock), 0, s, a, ws, dw,
+                       welems, nch);
+    return enqueue(reduce_kernel<T, 64>, dim3((unsigned)((welems + 63) / 64)), dim3(kBlock), 0, s, a, ws, dw,
+                   welems, nch);
+}
+
 // Depthwise 3x3 (Cpg = Kpg = 1, nine taps, at most 256 channel vectors of
 // 16 bytes): a workgroup owns every channel of one chunk of output pixels.
 // Lane `tid` takes channel vector v = tid % nv of pixel slot tid / nv, so
@@ -195,6 +207,10 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(const float *__restrict_
 // order through LDS and one partial per (tap, channel) is written:
 // [chunk][g][tap], or dw itself when there is one chunk.
 constexpr int kDwTaps = 9;
+constexpr int kDwPix = 2;   // pixels per lane per iteration
+
+// 16 zero bytes: the operand of a tap that falls outside the input
+__device__ __align__(16) uint4 kZero16 = {0u, 0u, 0u, 0u};
 
 template <typename T, bool kFinal>
 __global__ __launch_bounds__(kBlock) void dw_partial_kernel(Problem p, const T *__restrict__ x,
@@ -222,39 +238,53 @@ __global__ __launch_bounds__(kBlock) void dw_partial_kernel(Problem p, const T *
         for (int j = 0; j < VEC; ++j) acc[t][j] = 0.f;
     }
     if (active) {
-        for (int m = m0 + slot; m < m1; m += slots) {
-            int r = m;
-            const int ow = r % p.Wo; r /= p.Wo;
-            const int oh = r % p.Ho; r /= p.Ho;
-            const int od = r % p.Do; r /= p.Do;
-            const int n = r;
-            const uint4 draw = *reinterpret_cast<const uint4 *>(dy + (size_t)m * p.G + g0);
-            const T *dv = reinterpret_cast<const T *>(&draw);
-            float df[VEC];
+        // two pixels of the slot per iteration (m and m + slots), all twenty
+        // loads in flight before the first product.  A tap outside the input
+        // reads 16 zero bytes (kZero16) instead of its pixel, and past the
+        // chunk's end the second pixel's dy and x all read them: the choice
+        // is made on the address, so no loaded value is touched before the
+        // products (each tap's sum still runs over the slot's pixels in order)
+        const T *zero = reinterpret_cast<const T *>(&kZero16);
+        for (int m = m0 + slot; m < m1; m += 2 * slots) {
+            const bool two = m + slots < m1;
+            uint4 dr[kDwPix];
+            uint4 xr[kDwPix][kDwTaps];
 #pragma unroll
-            for (int j = 0; j < VEC; ++j) df[j] = to_f32(dv[j]);
-            // all nine loads go out before any is used: a tap outside the
-            // input loads an in-bounds (clamped) pixel and its value is
-            // replaced by zero, instead of a branch around each load
-            uint4 xr[kDwTaps];
+            for (int u = 0; u < kDwPix; ++u) {
+                const bool pad = u == 1 && !two;
+                const int mu = u == 1 ? m + slots : m;
+                int r = mu;
+                const int ow = r % p.Wo; r /= p.Wo;
+                const int oh = r % p.Ho; r /= p.Ho;
+                const int od = r % p.Do; r /= p.Do;
+                const int n = r;
+                dr[u] = *reinterpret_cast<const uint4 *>(pad ? zero : dy + (size_t)mu * p.G + g0);
 #pragma unroll
-            for (int t = 0; t < kDwTaps; ++t) {
-                const int id = od * p.sd + oz[t];
-                const int ih = oh * p.sh + oy[t];
-                const int iw = ow * p.sw + ox[t];
-                const int cd = id < 0 ? 0 : (id >= p.D ? p.D - 1 : id);
-                const int chh = ih < 0 ? 0 : (ih >= p.H ? p.H - 1 : ih);
-                const int cw = iw < 0 ? 0 : (iw >= p.W ? p.W - 1 : iw);
-                xr[t] = *reinterpret_cast<const uint4 *>(x + (((size_t)(n * p.D + cd) * p.H + chh) * p.W + cw) * p.G + g0);
-                const bool in = cd == id && chh == ih && cw == iw;
-                if (!in) xr[t] = make_uint4(0u, 0u, 0u, 0u);
+                for (int t = 0; t < kDwTaps; ++t) {
+                    const int id = od * p.sd + oz[t];
+                    const int ih = oh * p.sh + oy[t];
+                    const int iw = ow * p.sw + ox[t];
+                    const bool in = !pad && (unsigned)id < (unsigned)p.D && (unsigned)ih < (unsigned)p.H &&
+                                    (unsigned)iw < (unsigned)p.W;
+                    const T *src = in ? x + (((size_t)(n * p.D + id) * p.H + ih) * p.W + iw) * p.G + g0 : zero;
+                    xr[u][t] = *reinterpret_cast<const uint4 *>(src);
+                }
+            }
+            float df[kDwPix][VEC];
+#pragma unroll
+            for (int u = 0; u < kDwPix; ++u) {
+                const T *dv = reinterpret_cast<const T *>(&dr[u]);
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) df[u][j] = to_f32(dv[j]);
             }
 #pragma unroll
-            for (int t = 0; t < kDwTaps; ++t) {
-                const T *xv = reinterpret_cast<const T *>(&xr[t]);
+            for (int u = 0; u < kDwPix; ++u)
 #pragma unroll
-                for (int j = 0; j < VEC; ++j) acc[t][j] = fmaf(df[j], to_f32(xv[j]), acc[t][j]);
-            }
+                for (int t = 0; t < kDwTaps; ++t) {
+                    const T *xv = reinterpret_cast<const T *>(&xr[u][t]);
+#pragma unroll
+                    for (int j = 0; j < VEC; ++j) acc[t][j] = fmaf(df[u][j], to_f32(xv[j]), acc[t][j]);
+                }
         }
     }
     const int welems = p.G * kDwTaps;
@@ -304,8 +334,7 @@ hipError_t go_dw(const Problem &p, const void *x, const void *dy, void *dw, floa
     hipError_t e = enqueue(dw_partial_kernel<T, false>, dim3(chunks), dim3(kBlock), 0, s, a, p, (const T *)x,
                            (const T *)dy, ws, (T *)nullptr, ppc);
     if (e != hipSuccess) return e;
-    return enqueue(reduce_kernel<T>, dim3((unsigned)((welems + kRedElems - 1) / kRedElems)), dim3(kBlock), 0, s,
-                   a, (const float *)ws, (T *)dw, welems, chunks);
+    return reduce<T>(ws, (T *)dw, welems, chunks, s);
 }
 
 bool tile_ok(const Problem &p)
@@ -331,8 +360,7 @@ hipError_t go(const Problem &p, const void *x, const void *dy, void *dw, float *
         hipError_t e = enqueue(tile_partial_kernel<T, false>, tg, dim3(kBlock), 0, s, a, p, (const T *)x,
                                (const T *)dy, ws, (T *)nullptr, ntiles, rpc);
         if (e != hipSuccess) return e;
-        return enqueue(reduce_kernel<T>, dim3((unsigned)((welems + kRedElems - 1) / kRedElems)), dim3(kBlock), 0,
-                       s, a, (const float *)ws, (T *)dw, welems, nch);
+        return reduce<T>(ws, (T *)dw, welems, nch, s);
     }
     if (nch == 1)
         return enqueue(partial_kernel<T, true>, grid, dim3(kBlock), 0, s, a, p, (const T *)x, (const T *)dy,
@@ -340,8 +368,7 @@ hipError_t go(const Problem &p, const void *x, const void *dy, void *dw, float *
     hipError_t e = enqueue(partial_kernel<T, false>, grid, dim3(kBlock), 0, s, a, p, (const T *)x,
                            (const T *)dy, ws, (T *)nullptr, welems, rpc);
     if (e != hipSuccess) return e;
-    return enqueue(reduce_kernel<T>, dim3((unsigned)((welems + kRedElems - 1) / kRedElems)), dim3(kBlock), 0, s,
-                   a, (const float *)ws, (T *)dw, welems, nch);
+    return reduce<T>(ws, (T *)dw, welems, nch, s);
 }
 
 }  // namespace
