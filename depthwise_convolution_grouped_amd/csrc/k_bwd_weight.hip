@@ -28,6 +28,8 @@ namespace {
 
 constexpr int kBlock = 256;
 
+constexpr int kU = 8;        // output columns per step of the plain kernel
+
 template <typename T, bool kFinal>
 __global__ __launch_bounds__(kBlock) void partial_kernel(Problem p, const T *__restrict__ x,
                                                          const T *__restrict__ dy, float *__restrict__ ws,
@@ -65,13 +67,45 @@ __global__ __launch_bounds__(kBlock) void partial_kernel(Problem p, const T *__r
         if (id < 0 || id >= p.D || ih < 0 || ih >= p.H) continue;
         const T *dyr = dy + ((size_t)((n * p.Do + od) * p.Ho + oh) * p.Wo) * K + g * p.Kpg + k;
         const T *xr = x + ((size_t)((n * p.D + id) * p.H + ih) * p.W) * C + g * p.Cpg + c;
-        for (int ow = ow_lo; ow < ow_hi; ++ow) {
+        // kU columns per step, their loads issued before the first product
+        // (the sum still runs over ow in order)
+        int ow = ow_lo;
+        for (; ow + kU <= ow_hi; ow += kU) {
+            T dv[kU], xv[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int iw = (ow + u) * p.sw - p.pw + xx * p.dw;
+                dv[u] = dyr[(size_t)(ow + u) * K];
+                xv[u] = xr[(size_t)iw * C];
+            }
+#pragma unroll
+            for (int u = 0; u < kU; ++u) acc = fmaf(to_f32(dv[u]), to_f32(xv[u]), acc);
+        }
+        for (; ow < ow_hi; ++ow) {
             const int iw = ow * p.sw - p.pw + xx * p.dw;
             acc = fmaf(to_f32(dyr[(size_t)ow * K]), to_f32(xr[(size_t)iw * C]), acc);
         }
     }
     if (kFinal) dw[f] = from_f32<T>(acc);
     else ws[(size_t)ch * welems + f] = acc;
+}
+
+// acc[i][j] += dy channel i * x channel j over one pixel: 4 dy values (8
+// bytes) against 8 x values (16 bytes)
+template <typename T>
+__device__ __forceinline__ void tile_fma(float (&acc)[4][8], uint4 xv4, uint2 dv2)
+{
+    const T *xv = reinterpret_cast<const T *>(&xv4);
+    const T *dv = reinterpret_cast<const T *>(&dv2);
+    float xf[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xf[j] = to_f32(xv[j]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float d = to_f32(dv[i]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(d, xf[j], acc[i][j]);
+    }
 }
 
 // Grouped, half types, Cpg % 8 == 0 and Kpg % 4 == 0: a register-tiled
@@ -123,21 +157,12 @@ __global__ __launch_bounds__(kBlock) void tile_partial_kernel(Problem p, const T
         if (id < 0 || id >= p.D || ih < 0 || ih >= p.H) continue;
         const T *dyr = dy + ((size_t)((n * p.Do + od) * p.Ho + oh) * p.Wo) * K + g * p.Kpg + k0;
         const T *xr = x + ((size_t)((n * p.D + id) * p.H + ih) * p.W) * C + g * p.Cpg + c0;
+        // one column per step: four columns per step (their loads first)
+        // measured 14% slower on 8-channel groups, 7% faster on 128-channel
         for (int ow = ow_lo; ow < ow_hi; ++ow) {
             const int iw = ow * p.sw - p.pw + xx * p.dw;
-            const uint4 xv4 = *reinterpret_cast<const uint4 *>(xr + (size_t)iw * C);
-            const uint2 dv2 = *reinterpret_cast<const uint2 *>(dyr + (size_t)ow * K);
-            const T *xv = reinterpret_cast<const T *>(&xv4);
-            const T *dv = reinterpret_cast<const T *>(&dv2);
-            float xf[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) xf[j] = to_f32(xv[j]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float d = to_f32(dv[i]);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(d, xf[j], acc[i][j]);
-            }
+            tile_fma<T>(acc, *reinterpret_cast<const uint4 *>(xr + (size_t)iw * C),
+                        *reinterpret_cast<const uint2 *>(dyr + (size_t)ow * K));
         }
     }
     const int T9 = p.Z * p.Y * p.X;
