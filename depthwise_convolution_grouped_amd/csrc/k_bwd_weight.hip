@@ -233,6 +233,7 @@ hipError_t reduce(const float *ws, T *dw, int welems, int nch, hipStream_t s)
 // [chunk][g][tap], or dw itself when there is one chunk.
 constexpr int kDwTaps = 9;
 constexpr int kDwPix = 2;   // pixels per lane per iteration
+constexpr int kDwChunks = 512;   // two workgroups per CU (768, three per CU, measured slower)
 
 // 16 zero bytes: the operand of a tap that falls outside the input
 __device__ __align__(16) uint4 kZero16 = {0u, 0u, 0u, 0u};
@@ -338,14 +339,14 @@ bool dw_ok(const Problem &p)
 }
 
 // chunks for the depthwise kernel: two workgroups per CU, at most
-// `nch` (what the workspace holds) and at most 512 so stage 2 stays short
+// `nch` (what the workspace holds) and at most kDwChunks so stage 2 stays short
 template <typename T>
 hipError_t go_dw(const Problem &p, const void *x, const void *dy, void *dw, float *ws, int nch, hipStream_t s)
 {
     constexpr int VEC = 16 / (int)sizeof(T);
     const int slots = kBlock / (p.G / VEC);
     const long long M = (long long)p.N * p.Do * p.Ho * p.Wo;
-    long long want = 512;
+    long long want = kDwChunks;
     if (want > nch) want = nch;
     if (want > (M + slots - 1) / slots) want = (M + slots - 1) / slots;
     if (want < 1) want = 1;
@@ -401,13 +402,13 @@ hipError_t go(const Problem &p, const void *x, const void *dy, void *dw, float *
 // Chunks that fill the chip: about 256 K stage-1 threads (one per weight
 // element, or per 4 x 8 tile on the tiled route), at most one chunk per
 // output row, at most 65535 (the grid's y extent); for the depthwise
-// kernel, up to 512 workgroups of one chunk each.
+// kernel, up to kDwChunks workgroups of one chunk each.
 int ideal_chunks(const Problem &p)
 {
-    if (dw_ok(p)) {   // the depthwise kernel: up to 512 workgroups, one chunk each
+    if (dw_ok(p)) {   // the depthwise kernel: up to kDwChunks workgroups, one chunk each
         const long long slots = kBlock / (p.G / (16 / elem_size(p.dtype)));
         const long long m = ((long long)p.N * p.Do * p.Ho * p.Wo + slots - 1) / slots;
-        return (int)(m < 512 ? (m < 1 ? 1 : m) : 512);
+        return (int)(m < kDwChunks ? (m < 1 ? 1 : m) : kDwChunks);
     }
     const long long welems = (long long)p.G * p.Kpg * p.taps() * p.Cpg;
     const long long rows = (long long)p.N * p.Do * p.Ho;
