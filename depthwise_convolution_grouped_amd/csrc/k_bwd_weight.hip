@@ -240,7 +240,7 @@ hipError_t reduce(const float *ws, T *dw, int welems, int nch, hipStream_t s)
 // order through LDS and one partial per (tap, channel) is written:
 // [chunk][g][tap], or dw itself when there is one chunk.
 constexpr int kDwTaps = 9;
-constexpr int kDwPix = 2;   // pixels per lane per iteration
+constexpr int kDwPix = 2;   // pixels per lane per iteration (3 measured slower)
 constexpr int kDwChunks = 512;   // two workgroups per CU (768, three per CU, measured slower)
 
 // 16 zero bytes: the operand of a tap that falls outside the input
@@ -272,21 +272,20 @@ __global__ __launch_bounds__(kBlock) void dw_partial_kernel(Problem p, const T *
         for (int j = 0; j < VEC; ++j) acc[t][j] = 0.f;
     }
     if (active) {
-        // two pixels of the slot per iteration (m and m + slots), all twenty
-        // loads in flight before the first product.  A tap outside the input
-        // reads 16 zero bytes (kZero16) instead of its pixel, and past the
-        // chunk's end the second pixel's dy and x all read them: the choice
+        // kDwPix pixels of the slot per iteration (m, m + slots, ...), all
+        // their loads in flight before the first product.  A tap outside the
+        // input reads 16 zero bytes (kZero16) instead of its pixel, and a
+        // pixel past the chunk's end reads them for dy and every x: the choice
         // is made on the address, so no loaded value is touched before the
         // products (each tap's sum still runs over the slot's pixels in order)
         const T *zero = reinterpret_cast<const T *>(&kZero16);
-        for (int m = m0 + slot; m < m1; m += 2 * slots) {
-            const bool two = m + slots < m1;
+        for (int m = m0 + slot; m < m1; m += kDwPix * slots) {
             uint4 dr[kDwPix];
             uint4 xr[kDwPix][kDwTaps];
 #pragma unroll
             for (int u = 0; u < kDwPix; ++u) {
-                const bool pad = u == 1 && !two;
-                const int mu = u == 1 ? m + slots : m;
+                const int mu = m + u * slots;
+                const bool pad = mu >= m1;
                 int r = mu;
                 const int ow = r % p.Wo; r /= p.Wo;
                 const int oh = r % p.Ho; r /= p.Ho;
