@@ -79,14 +79,20 @@ int check_desc(const gconv_desc *d, int64_t out[3])
     return GCONV_OK;
 }
 
-// Images per launch: the whole batch when x and y each have < 2^31
-// elements, else the most whole images that keep both below.
+// Images per launch: the whole batch when x and y each span < 2^31 bytes,
+// else the most whole images that keep both below (at least one).  The
+// vector paths address a launch's tensors with 32-bit byte offsets, so a
+// byte limit keeps every launch on the path the dispatcher would pick for
+// its shape; the generic path indexes elements in 32 bits, which a launch
+// of one image below 2^31 elements also satisfies.
 int64_t images_per_launch(const gconv_desc *d, const int64_t out[3])
 {
-    const int64_t x_img = d->in[0] * d->in[1] * d->in[2] * d->C;
-    const int64_t y_img = out[0] * out[1] * out[2] * d->K;
-    const int64_t nx = (kMaxElems - 1) / x_img, ny = (kMaxElems - 1) / y_img;
-    const int64_t n = nx < ny ? nx : ny;
+    const int64_t es = elem_size(d->dtype);
+    const int64_t x_img = d->in[0] * d->in[1] * d->in[2] * d->C * es;
+    const int64_t y_img = out[0] * out[1] * out[2] * d->K * es;
+    const int64_t nx = kMaxElems / x_img, ny = kMaxElems / y_img;
+    int64_t n = nx < ny ? nx : ny;
+    if (n < 1) n = 1;
     return n < d->N ? n : d->N;
 }
 
@@ -287,7 +293,9 @@ int run_bwd_weight(const gconv_desc *d, const void *x, const void *dy, void *dw,
     int rc = check_desc(d, out);
     if (rc != GCONV_OK) return rc;
     // its reduction runs over the whole batch: no split into launches
-    if (images_per_launch(d, out) < d->N) return GCONV_ERR_TOO_LARGE;
+    const int64_t x_all = d->N * d->in[0] * d->in[1] * d->in[2] * d->C;
+    const int64_t y_all = d->N * out[0] * out[1] * out[2] * d->K;
+    if (x_all >= kMaxElems || y_all >= kMaxElems) return GCONV_ERR_TOO_LARGE;
     if (!x || !dy || !dw) return GCONV_ERR_NULL_PTR;
     const uintptr_t es = (uintptr_t)elem_size(d->dtype);
     if (!aligned(x, es) || !aligned(dy, es) || !aligned(dw, es)) return GCONV_ERR_MISALIGNED;

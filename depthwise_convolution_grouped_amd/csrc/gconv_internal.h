@@ -4,6 +4,8 @@
 
 #include <stdint.h>
 
+#include <atomic>
+
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -49,6 +51,21 @@ hipError_t enqueue(void (*k)(KP...), dim3 grid, dim3 block, unsigned lds, hipStr
 {
     void *argv[] = {(void *)&args...};
     return hipExtLaunchKernel((const void *)k, grid, block, argv, lds, s, a.ev_start, a.ev_stop, 0);
+}
+
+// Raises kernel `k`'s dynamic LDS limit to `bytes` on the current device,
+// once per device and kernel instance (`done` holds one bit per device, so
+// concurrent callers at worst repeat the idempotent attribute call).
+inline hipError_t allow_lds(const void *k, std::atomic<unsigned long long> &done, unsigned bytes)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const unsigned long long bit = dev >= 0 && dev < 64 ? 1ull << dev : 0ull;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+    return e;
 }
 
 // Per-path hooks.  `supported` and `plan` are pure host functions (no HIP

@@ -606,11 +606,9 @@ hipError_t go3(const Problem &p, const Config &c, const Args &a, hipStream_t s)
     q.x_bytes = (unsigned)((long long)p.N * p.D * p.H * p.W * p.C() * 2);
     q.w_bytes = (unsigned)((long long)p.K() * p.taps() * p.Cpg * 2);
     auto k = kernel<T, NTW, TPW>;
-    static bool lds_set = false;
-    if (!lds_set) {
-        (void)hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
-        lds_set = true;
-    }
+    static std::atomic<unsigned long long> lds_set{0};
+    const hipError_t e = allow_lds((const void *)k, lds_set, kMaxLds);
+    if (e != hipSuccess) return e;
     return enqueue(k, dim3(c.grid), dim3(kBlock), c.lds, s, a, q, (const T *)a.x, (const T *)a.w,
                    (const T *)a.bias, (T *)a.y);
 }

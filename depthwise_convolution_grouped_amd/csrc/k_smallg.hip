@@ -316,10 +316,10 @@ hipError_t go4(const Problem &p, const Config &c, const Args &a, hipStream_t s)
     q.img_bytes = (unsigned)((long long)p.D * p.H * p.W * p.C() * 2);
     const int blocks = c.ntw * c.nth * c.ntd * c.nslab * p.N;
     auto k = kernel<T, NMF, NTW, CPGC>;
-    static bool lds_set = false;      // one attribute call per kernel instance
-    if (c.lds > 64 * 1024 && !lds_set) {
-        hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsTile);
-        lds_set = true;
+    static std::atomic<unsigned long long> lds_set{0};   // one attribute call per kernel instance and device
+    if (c.lds > 64 * 1024) {
+        const hipError_t e = allow_lds((const void *)k, lds_set, kLdsTile);
+        if (e != hipSuccess) return e;
     }
     return enqueue(k, dim3(blocks), dim3(kBlock), c.lds, s, a, q, (const T *)a.x,
                    (const T *)a.w, (const T *)a.bias, (T *)a.y);

@@ -27,6 +27,8 @@ namespace gconv {
 namespace smallg {
 namespace {
 
+constexpr unsigned kRingMaxLds = 160 * 1024;   // the dynamic LDS limit every ring instance is raised to
+
 struct RingParams {
     Div dCpg, dKpg;
     int D, H, W, Do, Ho, Wo, C, K, Cpg, Kpg, GN, NT;
@@ -275,8 +277,12 @@ hipError_t ring_go(const Problem &p, const RingConfig &c, const Args &a, hipStre
     q.oimg_bytes = (unsigned)((long long)p.Ho * p.Wo * p.K() * 2);
     const int blocks = c.blocks;
     auto k = ring_kernel<T, S, R, CH8, NTW, CPGC, DZ>;
-    if (c.lds > 64 * 1024)
-        (void)hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, c.lds);
+    static std::atomic<unsigned long long> lds_set{0};
+    if (c.lds > 64 * 1024) {
+        // the limit is raised to the largest LDS any configuration of this instance uses
+        const hipError_t e = allow_lds((const void *)k, lds_set, kRingMaxLds);
+        if (e != hipSuccess) return e;
+    }
     return enqueue(k, dim3(blocks), dim3(kBlock), c.lds, s, a, q,
                    (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y);
 }

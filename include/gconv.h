@@ -32,9 +32,24 @@
  * and the result is rounded once (to nearest even) to the element type.
  *
  * Ownership: the caller allocates, owns and frees every buffer (device memory
- * for x, w, bias, y).  The library never allocates, frees or keeps a pointer
- * after a call returns, needs no workspace and holds no mutable global state;
- * calls from several host threads are safe.  y must not overlap x, w or bias.
+ * for x, w, bias, y, and the optional workspaces of the backward calls).  The
+ * library never allocates, frees or keeps a pointer after a call returns.
+ * The forward calls need no workspace; gconv_bwd_data and gconv_bwd_weight
+ * take an optional caller-owned workspace (sized by their *_workspace
+ * queries) that they may overwrite until the stream has passed the call.  The
+ * only global state is a per-device record of which kernels had their LDS
+ * limit raised (set once, atomically), so calls from several host threads are
+ * safe.  Outputs must not overlap inputs or workspaces.
+ *
+ * Non-finite inputs: the small-group path (GCONV_PATH_SMALLG) merges several
+ * groups into one block-diagonal matrix-core tile (the CK grouped-conv Python
+ * examples README's num_groups_to_merge option, Config-options harness), whose
+ * off-diagonal weights are zero.  An Inf or NaN in one group's input then
+ * makes the outputs of the other groups merged into the same tile NaN
+ * (0 * Inf), where the definition keeps them finite; the outputs of groups in
+ * other tiles, and every output when all inputs are finite, are unaffected.
+ * gconv_fwd_path with GCONV_PATH_GENERIC computes each group alone and keeps
+ * non-finite values inside their own group.
  *
  * Errors: every function returns GCONV_OK (0) or a negative gconv_status.
  * Validation errors are detected on the host before anything is launched.
@@ -42,6 +57,7 @@
 #ifndef GCONV_H
 #define GCONV_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -111,10 +127,19 @@ typedef struct gconv_plan {
 } gconv_plan;
 
 /* Checks the descriptor alone (no pointers, no HIP call).  Returns GCONV_OK,
- * GCONV_ERR_BAD_DESC, GCONV_ERR_BAD_OUT_DIMS or GCONV_ERR_TOO_LARGE. */
+ * GCONV_ERR_BAD_DESC, GCONV_ERR_BAD_OUT_DIMS or GCONV_ERR_TOO_LARGE.  The
+ * checks are those of rocm-libraries PR 10064 (Technical Details: C % G == 0
+ * and K % G == 0 before a grouped problem is accepted), of the TileOPs PR
+ * 1568 review (summary: the grouped ops validate the expected weight shape,
+ * which here follows from the descriptor) and positive extents, strides and
+ * dilations for the problem fields of the CK grouped_conv tile-engine README
+ * (Problem Registry). */
 int gconv_validate(const gconv_desc *d);
 
-/* Writes (Do, Ho, Wo) to out[0..2] (Do = 1 in 2D) after validating d. */
+/* Writes (Do, Ho, Wo) to out[0..2] (Do = 1 in 2D) after validating d: the
+ * dilation-aware extent formula above, which the TileOPs PR 1568 review
+ * (summary) says the grouped kernels keep and whose 3D case gives the
+ * review's 802,816 outputs ("The 50x is a baseline artifact"). */
 int gconv_out_dims(const gconv_desc *d, int64_t out[3]);
 
 /* Path gconv_fwd would take for d (a gconv_path >= 0), or a negative status.
@@ -124,11 +149,17 @@ int gconv_out_dims(const gconv_desc *d, int64_t out[3]);
  * Python examples README (Config-options harness, num_groups_to_merge). */
 int gconv_select_path(const gconv_desc *d);
 
-/* 1 if `path` can run d, 0 if not, or a negative status. */
+/* 1 if `path` can run d, 0 if not, or a negative status.  The counterpart of
+ * the legality rules of the CK grouped_conv tile-engine README (How It Works,
+ * Kernel Enumeration: the kernel pool holds only the configurations those
+ * rules accept), applied here per problem. */
 int gconv_path_supported(const gconv_desc *d, int path);
 
 /* Fills *plan with the launch shape of `path` (GCONV_PATH_AUTO: the selected
- * one) for d. */
+ * one) for d: the grid, with the group on the grid's z axis for the
+ * per-group implicit GEMM (rocm-libraries PR 10064, Technical Details: one
+ * grid slice per group), and the groups merged per tile (CK grouped-conv
+ * Python examples README, num_groups_to_merge). */
 int gconv_get_plan(const gconv_desc *d, int path, gconv_plan *plan);
 
 /* Forward convolution, asynchronous on `stream` (a hipStream_t; NULL = the
@@ -227,11 +258,14 @@ int gconv_bwd_weight_workspace(const gconv_desc *d, size_t *bytes);
 int gconv_bwd_weight(const gconv_desc *d, const void *x, const void *dy, void *dw,
                      void *workspace, size_t workspace_bytes, void *stream);
 
-/* Static strings; never NULL. */
+/* Static strings; never NULL.  A status string names why a call failed; the
+ * CK grouped_conv tile-engine README records a failed launch as a result of
+ * its own rather than a latency (Output CSV Schema: latency_ms=N/A). */
 const char *gconv_status_str(int status);
 const char *gconv_path_name(int path);
 
-/* GCONV_ABI_VERSION of the built library. */
+/* GCONV_ABI_VERSION of the built library (this header's layout of
+ * gconv_desc and gconv_plan and the entry points above). */
 int gconv_abi_version(void);
 
 #ifdef __cplusplus

@@ -357,3 +357,42 @@ def test_igemm_32_channel_tiles(case):
     y = run_and_fetch(p, t, G.GCONV_PATH_IGEMM)
     r = U.check(y, ref, scale, p.dtype, "igemm %r" % (IGEMM_ONLY_CASES[case],))
     print("igemm 32-channel case %d max err/tol %.3f plan %s" % (case, r, G.gconv_get_plan(d)))
+
+
+@pytest.mark.parametrize("name,N", [("grouped2d_resnext_bf16", 1), ("grouped3d_f16_n1", 1)])
+def test_nonfinite_input_stays_in_its_merged_tile(name, N):
+    """One Inf in one group's input.  The generic path keeps it inside that
+    group; the small-group path, whose block-diagonal tiles merge
+    groups_per_tile consecutive groups, may also turn the other groups of
+    that tile NaN (0 * Inf), and nothing else.  Every other output matches
+    the oracle."""
+    wl = inputs.WORKLOADS[name]
+    p = reduced(wl.problem, N)
+    t = inputs.workload_tensors(wl)
+    t = inputs.Tensors(t.x[:N].copy(), t.w, t.bias)
+    g_bad, c_bad = 5, p.Cpg - 1
+    pos = (0,) + tuple(s // 2 for s in t.x.shape[1:-1])
+    inf = inputs.to_storage(np.array([np.inf], dtype=np.float32), p.dtype)[0]
+    t.x[pos + (g_bad * p.Cpg + c_bad,)] = inf
+    st, pd, dl = p.spatial_args()
+    xo, wo, bo = U.oracle_inputs(p, t)
+    ref, scale = oracle.conv_fwd(xo, wo, bo, p.G, st, pd, dl)
+    ref_bad = ~np.isfinite(ref)
+    assert ref_bad.any()
+    grp = np.arange(p.K) // p.Kpg
+    d = G.desc_from_problem(p)
+    for path in (G.GCONV_PATH_GENERIC, G.GCONV_PATH_SMALLG):
+        assert G.gconv_path_supported(d, path) == 1
+        y = run_and_fetch(p, t, path)
+        gpt = G.gconv_get_plan(d, path)["groups_per_tile"] if path == G.GCONV_PATH_SMALLG else 1
+        tile = (grp // gpt) == (g_bad // gpt)
+        pix_bad = ref_bad.any(axis=-1, keepdims=True)       # pixels whose window reads the Inf
+        may_differ = pix_bad & tile                         # outputs the tile merge may turn NaN
+        assert not np.isfinite(y[ref_bad]).any(), "non-finite outputs of the Inf's group must stay non-finite"
+        keep = ~ref_bad & ~may_differ
+        U.check(y[keep], ref[keep], scale[keep], p.dtype, "%s path %d finite outputs" % (name, path))
+        if path == G.GCONV_PATH_GENERIC:
+            assert np.isfinite(y[~ref_bad]).all()
+        print("%s path=%s groups_per_tile=%d NaN outside the Inf's group: %d of %d allowed"
+              % (name, G.gconv_path_name(path), gpt, int((~np.isfinite(y) & ~ref_bad).sum()),
+                 int((may_differ & ~ref_bad).sum())))

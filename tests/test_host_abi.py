@@ -263,6 +263,101 @@ def test_large_batch_splits_into_whole_image_launches():
     assert G.gconv_select_path(d) == G.GCONV_PATH_DEPTHWISE
     plan = G.gconv_get_plan(d)
     small = G.make_desc(2, "f16", 31, 64, 64, 64, (1024, 1024), (3, 3), (1, 1), (1, 1), (1, 1))
-    assert plan == G.gconv_get_plan(small)        # (2^31 - 1) // 2^26 = 31 images per launch
+    assert plan == G.gconv_get_plan(small)        # (2^31 - 1) // 2^27 bytes = 15 images per launch
+    fifteen = G.make_desc(2, "f16", 15, 64, 64, 64, (1024, 1024), (3, 3), (1, 1), (1, 1), (1, 1))
+    assert plan == G.gconv_get_plan(fifteen)
     # backward weight reduces over the whole batch: no split
     assert G.gconv_bwd_weight(d, 16, 16, 16, None, 0) == G.GCONV_ERR_TOO_LARGE
+
+
+# ---- the header as a plain C / C++ consumer sees it ------------------------
+
+def _compiler(name):
+    import shutil
+    c = shutil.which(name)
+    if c is None:
+        pytest.skip("%s not available" % name)
+    return c
+
+
+@pytest.mark.parametrize("cc,flags,ext", [
+    ("gcc", ["-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic"], ".c"),
+    ("g++", ["-std=c++17", "-Wall", "-Wextra", "-Werror"], ".cpp"),
+])
+def test_header_compiles_alone(tmp_path, cc, flags, ext):
+    import subprocess
+    src = tmp_path / ("only_header" + ext)
+    src.write_text('#include "gconv.h"\nint gconv_probe_unused(void) { return GCONV_ABI_VERSION; }\n')
+    r = subprocess.run([_compiler(cc)] + flags + ["-I", os.path.dirname(HEADER), "-c", str(src),
+                        "-o", str(tmp_path / "o.o")], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_c_program_links_and_calls_host_functions(tmp_path):
+    """A C99 caller linked against libgconv.so validates, sizes and routes
+    every workload descriptor; the answers match the Python binding's."""
+    import subprocess
+    cc = _compiler("gcc")
+    names = sorted(inputs.WORKLOADS)
+    rows = []
+    for n in names:
+        d = G.desc_from_problem(inputs.WORKLOADS[n].problem)
+        rows.append("{%d, %d, %d, %d, %d, %d, {%s}, {%s}, {%s}, {%s}, {%s}}" % (
+            d.ndim, d.dtype, d.N, d.G, d.C, d.K,
+            ", ".join(str(v) for v in d.in_), ", ".join(str(v) for v in d.filt),
+            ", ".join(str(v) for v in d.stride), ", ".join(str(v) for v in d.pad),
+            ", ".join(str(v) for v in d.dil)))
+    prog = r'''
+#include <stdio.h>
+#include "gconv.h"
+static const gconv_desc descs[] = { %s };
+int main(void)
+{
+    unsigned i;
+    if (gconv_abi_version() != GCONV_ABI_VERSION) return 3;
+    for (i = 0; i < sizeof descs / sizeof descs[0]; ++i) {
+        int64_t out[3];
+        size_t ws = 0;
+        int v = gconv_validate(&descs[i]);
+        int o = gconv_out_dims(&descs[i], out);
+        int p = gconv_select_path(&descs[i]);
+        int b = gconv_bwd_weight_workspace(&descs[i], &ws);
+        if (v != GCONV_OK || o != GCONV_OK || p < 0 || b != GCONV_OK) return 4;
+        printf("%%d %%lld %%lld %%lld %%s %%lu\n", v, (long long)out[0], (long long)out[1],
+               (long long)out[2], gconv_path_name(p), (unsigned long)ws);
+    }
+    printf("%%s\n", gconv_status_str(GCONV_ERR_BAD_DESC));
+    return 0;
+}
+''' % ",\n    ".join(rows)
+    src = tmp_path / "caller.c"
+    src.write_text(prog)
+    exe = tmp_path / "caller"
+    libdir = os.path.dirname(G.LIB_PATH)
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER), str(src),
+                        "-L", libdir, "-lgconv", "-Wl,-rpath," + libdir, "-o", str(exe)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, (r.returncode, r.stderr)
+    lines = r.stdout.strip().splitlines()
+    assert len(lines) == len(names) + 1
+    for n, line in zip(names, lines):
+        d = G.desc_from_problem(inputs.WORKLOADS[n].problem)
+        v, o0, o1, o2, path, ws = line.split()
+        assert int(v) == G.GCONV_OK
+        assert (int(o0), int(o1), int(o2)) == G.gconv_out_dims(d)
+        assert path == G.gconv_path_name(G.gconv_select_path(d)) == EXPECTED_PATH[n]
+        assert int(ws) == G.gconv_bwd_weight_workspace(d)
+    assert lines[-1] == G.gconv_status_str(G.GCONV_ERR_BAD_DESC)
+
+
+def test_half_batch_between_2_30_and_2_31_elements_stays_on_the_mfma_path():
+    # x of 6000 large-group bf16 images: 1.2e9 elements (2.4 GB), over the
+    # 2^31-byte reach of one launch's buffer offsets, so the batch is split
+    # into launches that the halo implicit GEMM still takes
+    d = G.make_desc(2, "bf16", 6000, 8, 1024, 1024, (14, 14), (3, 3), (1, 1), (1, 1), (1, 1))
+    assert G.gconv_validate(d) == G.GCONV_OK
+    assert G.gconv_path_name(G.gconv_select_path(d)) == "ighalo_mfma"
+    one = G.make_desc(2, "bf16", 64, 8, 1024, 1024, (14, 14), (3, 3), (1, 1), (1, 1), (1, 1))
+    assert G.gconv_select_path(one) == G.gconv_select_path(d)
