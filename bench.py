@@ -1,23 +1,28 @@
 #!/usr/bin/env python3
 """Benchmark of the grouped / depthwise conv forward HIP library on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--op fwd]
 
-A step is one pass of the hot path over one batch of the workload: the
-default workload is the MobileNetV2-style depthwise fp16 case (N=32, C=144,
-56x56, 3x3, pad 1, bias) in its stride-1 form and its stride-2 form, i.e. two
-gconv_fwd calls per step (each one kernel launch).  Inputs are seeded
-synthetic tensors already resident in HBM.  To keep the 256 MB Infinity Cache
-from serving repeated reads, every call takes the next of R rotating input /
-output buffer sets, R chosen so the sets span >= 512 MB.
+A step is one pass of the hot path over one batch of every workload in the
+set: by default all eight workloads (small fp32 grouped; MobileNetV2-style
+depthwise fp16 at stride 1 and 2; ResNeXt-style bf16; 3D grouped fp16 at N=1
+and N=8; large-group bf16 with dilation 1 and 2), i.e. eight gconv_fwd calls
+per step, each one kernel launch.  Inputs are seeded synthetic tensors
+already resident in HBM.  To keep the 256 MB Infinity Cache from serving
+repeated reads, every call takes the next of R rotating input / output
+buffer sets of its workload, R chosen so the sets span >= 512 MB.
 
 Prints ONE JSON line: whole-step algorithmic HBM throughput (GB/s) as
-`value`, TFLOP/s and fractions of the MI355X peaks per call, a `roofline`
-object for the dominant kernel (its average duration from a pair of HIP
-events that the library binds to each of its kernel dispatches inside the
-timed region, on the launch stream),
-and a `cpu_baseline` object (the CPU oracle, timed on this host's cores on
-the same workload).
+`value`; per workload, the kernel's average duration from a pair of HIP
+events that the library binds to its dispatch (on the launch stream, every
+S-th timed step), TFLOP/s, GB/s, both fractions of the MI355X peaks and a
+roofline object; `roofline` for the dominant (longest) kernel; and a
+`cpu_baseline` object (the CPU oracle, timed on this host's cores on the
+first images of every workload).  `traffic` is the HBM bytes per launch from
+committed rocprofv3 counters (profiles/traffic.json), null once the kernel's
+sources have changed since they were taken.
+
+--op bwd_data / bwd_weight time the backward calls on one workload's shapes.
 """
 from __future__ import annotations
 
@@ -33,15 +38,15 @@ sys.path.insert(0, ROOT)
 
 from depthwise_convolution_grouped_amd import inputs, metrics  # noqa: E402
 
-WORKLOAD_SETS = {
-    # name -> (workload names run once each per step, dominant one)
-    "depthwise2d_f16": (["depthwise2d_f16", "depthwise2d_s2_f16"], "depthwise2d_f16"),
-}
+# name -> the workloads whose forward calls make up one step
+WORKLOAD_SETS = {"all": list(inputs.WORKLOADS),
+                 "depthwise2d_pair": ["depthwise2d_f16", "depthwise2d_s2_f16"]}
 for _n in inputs.WORKLOADS:
-    WORKLOAD_SETS.setdefault(_n, ([_n], _n))
+    WORKLOAD_SETS.setdefault(_n, [_n])
 
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 ROTATE_BYTES = 512 << 20
+LAUNCH_BOUND_BYTES = 8 << 20     # below this a problem's launch costs more than its HBM time
 
 
 def stored_traffic(workload: str, path_name: str):
@@ -102,14 +107,12 @@ class hip_runtime:
 
 
 def cpu_baseline(names, max_seconds: float):
-    """Time the CPU oracle on the workload (whole batches, repeated) on this host's cores."""
-    import numpy as np  # noqa: F401
+    """Time the CPU oracle on the first images of every workload of the step,
+    each given an equal share of `max_seconds`, on this host's cores."""
     import oracle
-    total_bytes = 0
-    elapsed = 0.0
-    runs = 0
-    per = []
-    data = []
+    total_bytes, elapsed = 0, 0.0
+    per, parts = {}, []
+    share = max_seconds / len(names)
     for n in names:
         wl = inputs.WORKLOADS[n]
         p = wl.problem
@@ -117,34 +120,37 @@ def cpu_baseline(names, max_seconds: float):
         x = inputs.storage_to_f64(t.x, p.dtype)
         w = inputs.storage_to_f64(t.w, p.dtype)
         b = inputs.storage_to_f64(t.bias, p.dtype) if t.bias is not None else None
-        data.append((p, x, w, b))
-    # bound the sample: shrink the batch if one pass would exceed the budget
-    t0 = time.perf_counter()
-    p, x, w, b = data[0]
-    st, pd, dl = p.spatial_args()
-    oracle.conv_fwd(x[:1], w, b, p.G, st, pd, dl)
-    one_image = time.perf_counter() - t0
-    nimg = max(1, min(data[0][0].N, int(max_seconds / 3 / max(one_image * len(data), 1e-9))))
-    while runs < 1 or elapsed < max_seconds:
-        for p, x, w, b in data:
-            st, pd, dl = p.spatial_args()
+        st, pd, dl = p.spatial_args()
+        done, secs, nb = 0, 0.0, 0
+        while done == 0 or secs < share:
+            # one image first, then as many as the remaining share allows,
+            # going round the batch again when it is done
+            i0 = done % p.N
+            k = 1 if done == 0 else max(1, min(p.N - i0, int((share - secs) / (secs / done))))
             t0 = time.perf_counter()
-            oracle.conv_fwd(x[:nimg], w, b, p.G, st, pd, dl)
-            dt = time.perf_counter() - t0
-            per.append(dt)
-            elapsed += dt
-            sub = inputs.Problem(p.ndim, p.dtype, nimg, p.G, p.C, p.K, p.spatial, p.filt,
-                                 p.stride, p.pad, p.dil, p.bias)
-            total_bytes += metrics.total_bytes(sub)
-        runs += 1
+            oracle.conv_fwd(x[i0:i0 + k], w, b, p.G, st, pd, dl)
+            secs += time.perf_counter() - t0
+            nb += metrics.total_bytes(_with_batch(p, k))
+            done += k
+        per[n] = {"gbs": nb / secs / 1e9, "images": done, "seconds": secs}
+        parts.append("%s %d images (batch %d)" % (n, done, p.N))
+        total_bytes += nb
+        elapsed += secs
     return {
         "value": total_bytes / elapsed / 1e9,
         "unit": "GB/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": "%s, first %d of %d images, %d pass(es), fp64 direct conv, %.1f s"
-                  % ("+".join(names), nimg, data[0][0].N, runs, elapsed),
+        "sample": "fp64 direct conv (the oracle), an equal time share per workload, images taken in "
+                  "batch order: %s; %.1f s in all"
+                  % (", ".join(parts), elapsed),
+        "per_config": per,
     }
+
+
+def _with_batch(p, n):
+    return inputs.Problem(p.ndim, p.dtype, n, p.G, p.C, p.K, p.spatial, p.filt, p.stride, p.pad,
+                          p.dil, p.bias)
 
 
 def bwd_problem(p):
@@ -153,41 +159,45 @@ def bwd_problem(p):
                           p.dil, False)
 
 
-def cpu_baseline_bwd(names, max_seconds: float):
-    """The oracle's backward data on this host's cores, on the first images of the workload."""
+def cpu_baseline_bwd(name, op: str, max_seconds: float):
+    """The oracle's backward data or backward weight on this host's cores, on
+    the first images of the workload (as many as fit in `max_seconds`)."""
     import oracle
-    elapsed, total_bytes, runs = 0.0, 0, 0
-    p = bwd_problem(inputs.WORKLOADS[names[0]].problem)
+    p = bwd_problem(inputs.WORKLOADS[name].problem)
     t = inputs.make_tensors(p, 4100)
+    x = inputs.storage_to_f64(t.x, p.dtype)
     w = inputs.storage_to_f64(t.w, p.dtype)
     o = metrics.out_spatial(p)
     dshape = (p.N,) + (o if p.ndim == 3 else o[1:]) + (p.K,)
     dy = inputs.storage_to_f64(inputs.make_array(dshape, p.dtype, 4105), p.dtype)
     st, pd, dl = p.spatial_args()
     in_sp = p.x_shape()[1:-1]
-    t0 = time.perf_counter()
-    oracle.conv_bwd_data(dy[:1], w, p.G, in_sp, st, pd, dl)
-    one = time.perf_counter() - t0
-    nimg = max(1, min(p.N, int(max_seconds / 3 / max(one, 1e-9))))
-    sub = inputs.Problem(p.ndim, p.dtype, nimg, p.G, p.C, p.K, p.spatial, p.filt, p.stride, p.pad, p.dil, False)
-    while runs < 1 or elapsed < max_seconds:
+
+    def run(k):
+        if op == "bwd_data":
+            oracle.conv_bwd_data(dy[:k], w, p.G, in_sp, st, pd, dl)
+        else:
+            oracle.conv_bwd_weight(x[:k], dy[:k], p.G, p.w_shape()[1:-1], st, pd, dl)
+
+    done, secs, nb = 0, 0.0, 0
+    while done < p.N and (done == 0 or secs < max_seconds):
+        k = 1 if done == 0 else max(1, min(p.N - done, int((max_seconds - secs) / (secs / done))))
         t0 = time.perf_counter()
-        oracle.conv_bwd_data(dy[:nimg], w, p.G, in_sp, st, pd, dl)
-        elapsed += time.perf_counter() - t0
-        total_bytes += metrics.total_bytes(sub)
-        runs += 1
-    return {"value": total_bytes / elapsed / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": "%s backward data, first %d of %d images, %d pass(es), fp64, %.1f s"
-                      % (names[0], nimg, p.N, runs, elapsed)}
+        run(k)
+        secs += time.perf_counter() - t0
+        nb += metrics.total_bytes(_with_batch(p, k))
+        done += k
+    what = "backward data" if op == "bwd_data" else "backward weight"
+    return {"value": nb / secs / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%s %s (the oracle, fp64) on the first %d of %d images, %.1f s"
+                      % (name, what, done, p.N, secs)}
 
 
 def bench_bwd_data(a, G, torch):
     """Backward data (gconv_bwd_data) on the first workload of the set: the same
     rotating-buffer protocol, timed with events on the launch stream around
     each call (the stride-1 route is two kernels: weight transform + forward)."""
-    names, _ = WORKLOAD_SETS[a.workload]
-    name = names[0]
+    name = WORKLOAD_SETS[a.workload][0]
     p = bwd_problem(inputs.WORKLOADS[name].problem)
     dev = torch.device("cuda", 0)
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[p.dtype]
@@ -242,7 +252,8 @@ def bench_bwd_data(a, G, torch):
                     p.filt if p.ndim == 3 else p.filt[1:], (1,) * p.ndim,
                     tuple(p.dil[i] * (p.filt[i] - 1) - p.pad[i] for i in range(3 - p.ndim, 3)),
                     p.spatial_args()[2])))) if need else "direct"
-    roof.update({"traffic": None, "kernel": "bwd_data (%s)" % route, "workload": name,
+    roof.update({"traffic": stored_traffic("bwd_data:" + name, "bwd_data"),
+                 "kernel": "bwd_data (%s)" % route, "workload": name,
                  "algorithmic_bytes": metrics.total_bytes(p), "algorithmic_flop": metrics.flops(p),
                  "us_per_launch": avg_ms * 1e3, "timed_launches": len(ds),
                  "timing": "event pair around each gconv_bwd_data call on the launch stream"})
@@ -263,7 +274,7 @@ def bench_bwd_data(a, G, torch):
         "cpu_baseline": None,
     }
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_bwd(names, a.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline_bwd(name, "bwd_data", a.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
 
@@ -272,8 +283,7 @@ def bench_bwd_weight(a, G, torch):
     """Backward weight (gconv_bwd_weight, full partial-sum workspace) on the first
     workload of the set, timed like backward data (events around each call:
     the two-stage reduction is two kernels)."""
-    names, _ = WORKLOAD_SETS[a.workload]
-    name = names[0]
+    name = WORKLOAD_SETS[a.workload][0]
     p = bwd_problem(inputs.WORKLOADS[name].problem)
     dev = torch.device("cuda", 0)
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[p.dtype]
@@ -327,7 +337,8 @@ def bench_bwd_weight(a, G, torch):
         roof = {"bound": "alu", "achieved": r["tflops"], "peak": alu_peak, "unit": "TFLOP/s",
                 "frac": r["tflops"] / alu_peak}
     route = "two-stage reduction (%d B of partial sums)" % need if need else "one-stage reduction"
-    roof.update({"traffic": None, "kernel": "bwd_weight (%s)" % route, "workload": name,
+    roof.update({"traffic": stored_traffic("bwd_weight:" + name, "bwd_weight"),
+                 "kernel": "bwd_weight (%s)" % route, "workload": name,
                  "algorithmic_bytes": metrics.total_bytes(p), "algorithmic_flop": metrics.flops(p),
                  "us_per_launch": avg_ms * 1e3, "timed_launches": len(ds),
                  "timing": "event pair around each gconv_bwd_weight call on the launch stream"})
@@ -347,59 +358,35 @@ def bench_bwd_weight(a, G, torch):
         "roofline": roof,
         "cpu_baseline": None,
     }
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_bwd(name, "bwd_weight", a.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="depthwise2d_f16", choices=sorted(WORKLOAD_SETS))
-    ap.add_argument("--path", default="auto", help="force a kernel path (auto|generic|depthwise|smallg_mfma|igemm_mfma|ighalo_mfma)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--event-every", type=int, default=4, metavar="S",
-                    help="bind an event pair to the dispatches of every S-th timed step (a dispatch-bound "
-                         "event pair costs about 25 us of host time, more than a step of GPU work)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="rough bound on the CPU oracle's timing sample")
-    ap.add_argument("--hot", action="store_true", help="no buffer rotation (cache-hot; labelled)")
-    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
-                    help="first run 3 plain device copies of MIB MiB (a reference kernel of "
-                         "known size for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
-    ap.add_argument("--op", default="fwd", choices=["fwd", "bwd_data", "bwd_weight"],
-                    help="bwd_data: time gconv_bwd_data (dx from dy and w); bwd_weight: gconv_bwd_weight "
-                         "(dw from x and dy); both on the workload's shapes")
-    a = ap.parse_args()
+def fwd_rooflines(p, us_avg, path_name, key):
+    """The roofline object of one forward config: HBM-bound below the ridge
+    point of its compute unit, else bound by that unit; launch-bound when the
+    whole problem moves less than 8 MB (the launch itself then dominates)."""
+    r = metrics.rates(p, us_avg * 1e-6)
+    ai = metrics.flops(p) / metrics.total_bytes(p)
+    # fp32 runs on the vector ALUs (256 FLOP/clk/CU x 256 CUs x 2.4 GHz =
+    # 157.3 TFLOP/s); half types on the matrix cores
+    peak_tf = metrics.PEAK_TFLOPS["f32_vector"] if p.dtype == "f32" else metrics.PEAK_TFLOPS[p.dtype]
+    ridge = peak_tf * 1e12 / (metrics.PEAK_HBM_GBS * 1e9)
+    if ai < ridge:
+        roof = {"bound": "hbm", "achieved": r["gbs"], "peak": metrics.PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": r["gbs"] / metrics.PEAK_HBM_GBS}
+    else:
+        roof = {"bound": "alu" if p.dtype == "f32" else "mfma", "achieved": r["tflops"],
+                "peak": peak_tf, "unit": "TFLOP/s", "frac": r["tflops"] / peak_tf}
+    roof["traffic"] = stored_traffic(key, path_name)
+    roof["launch_bound"] = metrics.total_bytes(p) < LAUNCH_BOUND_BYTES
+    return roof
 
-    if a.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(--gpus %d requested)" % a.gpus, file=sys.stderr)
-        return 2
 
-    import torch
-    from depthwise_convolution_grouped_amd import gconv as G
-    if not torch.cuda.is_available():
-        print("no GPU visible", file=sys.stderr)
-        return 2
-    G.lib()  # fail loudly if the HIP library is missing
-
-    if a.calibrate_copy:
-        nb = a.calibrate_copy << 20
-        src = torch.ones(nb // 4, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
-    if a.op == "bwd_data":
-        return bench_bwd_data(a, G, torch)
-    if a.op == "bwd_weight":
-        return bench_bwd_weight(a, G, torch)
-
-    names, dominant = WORKLOAD_SETS[a.workload]
+def bench_fwd(a, G, torch):
+    names = WORKLOAD_SETS[a.workload]
     path = G.GCONV_PATH_AUTO if a.path == "auto" else G.PATHS[a.path]
     dev = torch.device("cuda", 0)
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
@@ -436,31 +423,21 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
     counter = [0]
-
-    def launch(c):
-        i = counter[0] % c["R"]
-        rc = G.gconv_fwd_path(c["d"], c["path"], c["xs"][i].data_ptr(), c["w"].data_ptr(),
-                              c["b"].data_ptr() if c["b"] is not None else None,
-                              c["ys"][i].data_ptr(), sptr)
-        if rc != 0:
-            raise G.GconvError(rc, "gconv_fwd(%s)" % c["name"])
-
     hip = hip_runtime()
 
-    def launch_timed(c, e0, e1):
-        # a start/stop event pair (created beforehand) bound to this one kernel dispatch
+    def launch(c, e0=None, e1=None):
+        # e0/e1: a start/stop event pair (created beforehand) bound to this one dispatch
         i = counter[0] % c["R"]
         rc = G.gconv_fwd_timed(c["d"], c["path"], c["xs"][i].data_ptr(), c["w"].data_ptr(),
                                c["b"].data_ptr() if c["b"] is not None else None,
                                c["ys"][i].data_ptr(), sptr, e0, e1)
         if rc != 0:
-            raise G.GconvError(rc, "gconv_fwd_timed(%s)" % c["name"])
-        return e0, e1
+            raise G.GconvError(rc, "gconv_fwd(%s)" % c["name"])
 
     def step(events=None, k=0):
         for c in calls:
-            if events is not None and c["name"] in events:
-                launch_timed(c, *events[c["name"]][k])
+            if events is not None:
+                launch(c, *events[c["name"]][k])
             else:
                 launch(c)
         counter[0] += 1
@@ -496,44 +473,34 @@ def main():
     for c in calls:
         ds = sorted(hip.elapsed_ms(e0, e1) for e0, e1 in events[c["name"]])
         avg_ms = sum(ds) / len(ds)
-        med_ms = ds[len(ds) // 2]
         p = c["p"]
         r = metrics.rates(p, avg_ms * 1e-3)
+        name = G.gconv_path_name(c["path"])
+        roof = fwd_rooflines(p, avg_ms * 1e3, name, c["name"])
         per_config[c["name"]] = {
-            "path": G.gconv_path_name(c["path"]),
-            "us_avg": avg_ms * 1e3, "us_median": med_ms * 1e3, "us_min": ds[0] * 1e3,
+            "path": name,
+            "us_avg": avg_ms * 1e3, "us_median": ds[len(ds) // 2] * 1e3, "us_min": ds[0] * 1e3,
             "tflops": r["tflops"], "gbs": r["gbs"], "frac_hbm": r["frac_hbm"],
             "frac_compute": r["frac_compute"], "flop": metrics.flops(p),
             "bytes": metrics.total_bytes(p), "rotating_sets": c["R"],
             "grid": list(c["plan"]["grid"]), "block": c["plan"]["block"],
+            "roofline": roof,
         }
         step_bytes += metrics.total_bytes(p)
         step_flops += metrics.flops(p)
-
     hip.destroy_all()
-    dom = next(c for c in calls if c["name"] == dominant)
-    dp = dom["p"]
-    dom_cfg = per_config[dominant]
-    ai = metrics.flops(dp) / metrics.total_bytes(dp)
-    peak_tf = metrics.PEAK_TFLOPS["f32_vector"] if dp.dtype == "f32" else metrics.PEAK_TFLOPS[dp.dtype]
-    ridge = peak_tf * 1e12 / (metrics.PEAK_HBM_GBS * 1e9)
-    if ai < ridge:
-        roof = {"bound": "hbm", "achieved": dom_cfg["gbs"], "peak": metrics.PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": dom_cfg["gbs"] / metrics.PEAK_HBM_GBS}
-    else:
-        # fp32 runs on the vector ALUs (fp32 FMA, 256 FLOP/clk/CU x 256 CUs x
-        # 2.4 GHz = 157.3 TFLOP/s); half types on the matrix cores
-        roof = {"bound": "alu" if dp.dtype == "f32" else "mfma", "achieved": dom_cfg["tflops"],
-                "peak": peak_tf, "unit": "TFLOP/s", "frac": dom_cfg["tflops"] / peak_tf}
-    roof["traffic"] = stored_traffic(dominant, dom_cfg["path"])
-    roof["kernel"] = dom_cfg["path"]
-    roof["workload"] = dominant
-    roof["algorithmic_bytes"] = metrics.total_bytes(dp)
-    roof["algorithmic_flop"] = metrics.flops(dp)
-    roof["us_per_launch"] = dom_cfg["us_avg"]
-    roof["timed_launches"] = len(sampled)
-    roof["timing"] = "event pair bound to the dispatch (hipExtLaunchKernel) on every %d-th timed step" % every
 
+    # the dominant kernel: the config with the longest kernel time per step
+    dominant = max(per_config, key=lambda n: per_config[n]["us_avg"])
+    dom = per_config[dominant]
+    dp = inputs.WORKLOADS[dominant].problem
+    roof = dict(dom["roofline"])
+    roof.update({"kernel": dom["path"], "workload": dominant,
+                 "algorithmic_bytes": metrics.total_bytes(dp), "algorithmic_flop": metrics.flops(dp),
+                 "us_per_launch": dom["us_avg"], "timed_launches": len(sampled),
+                 "timing": "event pair bound to the dispatch (hipExtLaunchKernel) on every %d-th timed "
+                           "step, on the launch stream" % every})
+    dtypes = sorted({inputs.WORKLOADS[n].problem.dtype for n in names})
     out = {
         "metric": "grouped conv fwd TFLOP/s + HBM GB/s (% of MI355X peak) per config, 1 GPU",
         "value": step_bytes / (ms_per_step * 1e-3) / 1e9,
@@ -545,11 +512,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dp.dtype,
-        "data": "synthetic (seeded; x~N(0,1), w~N(0,1/fan_in), bias~U[-1,1]); inputs resident in HBM",
+        "dtype": "+".join(dtypes) + " (fp32 accumulate)" if len(dtypes) > 1 else dtypes[0],
+        "data": "synthetic (seeded; x~N(0,1) or U[-1,1], w~N(0,1/fan_in), bias~U[-1,1]); inputs resident in HBM",
         "config": {"workload": " + ".join(inputs.WORKLOADS[n].about for n in names),
                    "names": names, "layout": "NHWGC/GKYXC -> NHWGK",
-                   "cache": "hot (no rotation)" if a.hot else "rotating buffer sets >= 512 MB"},
+                   "step": "one gconv_fwd per listed workload (one kernel launch each)",
+                   "cache": "hot (no rotation)" if a.hot else "rotating buffer sets >= 512 MB per workload"},
         "tflops": step_flops / (ms_per_step * 1e-3) / 1e12,
         "frac_hbm_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / metrics.PEAK_HBM_GBS,
         "per_config": per_config,
@@ -560,6 +528,56 @@ def main():
         out["cpu_baseline"] = cpu_baseline(names, a.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="all", choices=sorted(WORKLOAD_SETS))
+    ap.add_argument("--path", default="auto", help="force a kernel path (auto|generic|depthwise|smallg_mfma|igemm_mfma|ighalo_mfma)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--event-every", type=int, default=4, metavar="S",
+                    help="bind an event pair to the dispatches of every S-th timed step (a dispatch-bound "
+                         "event pair costs about 25 us of host time)")
+    ap.add_argument("--cpu-seconds", type=float, default=16.0,
+                    help="rough bound on the CPU oracle's timing sample")
+    ap.add_argument("--hot", action="store_true", help="no buffer rotation (cache-hot; labelled)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="first run 3 plain device copies of MIB MiB (a reference kernel of "
+                         "known size for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--op", default="fwd", choices=["fwd", "bwd_data", "bwd_weight"],
+                    help="bwd_data: time gconv_bwd_data (dx from dy and w); bwd_weight: gconv_bwd_weight "
+                         "(dw from x and dy); both on the first workload of --workload")
+    a = ap.parse_args()
+
+    if a.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % a.gpus, file=sys.stderr)
+        return 2
+
+    import torch
+    from depthwise_convolution_grouped_amd import gconv as G
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 2
+    G.lib()  # fail loudly if the HIP library is missing
+
+    if a.calibrate_copy:
+        nb = a.calibrate_copy << 20
+        src = torch.ones(nb // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    if a.op == "bwd_data":
+        return bench_bwd_data(a, G, torch)
+    if a.op == "bwd_weight":
+        return bench_bwd_weight(a, G, torch)
+    return bench_fwd(a, G, torch)
 
 
 if __name__ == "__main__":

@@ -44,10 +44,16 @@ KERNEL_TAGS = {"generic": "generic", "depthwise": "depthwise", "smallg_mfma": "s
 
 
 def source_hash(path_name: str) -> str:
+    """Hash of the sources a path's kernels are built from.  The backward
+    routes run forward kernels too, so every kernel source counts for them."""
     h = hashlib.sha256()
     csrc = os.path.join(PKG, "csrc")
-    own = PATH_SOURCES[path_name]
-    for f in (own if isinstance(own, tuple) else (own,)) + SHARED:
+    if path_name in ("bwd_data", "bwd_weight"):
+        files = tuple(sorted(f for f in os.listdir(csrc) if f.endswith((".hip", ".h"))))
+    else:
+        own = PATH_SOURCES[path_name]
+        files = (own if isinstance(own, tuple) else (own,)) + SHARED
+    for f in files:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
