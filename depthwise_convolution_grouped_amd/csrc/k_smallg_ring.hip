@@ -9,7 +9,8 @@ namespace {
 template <typename T, int S, int R>
 hipError_t ring_go3(const Problem &p, const RingConfig &c, const Args &a, hipStream_t s)
 {
-    return c.CH8 == 1 ? ring_go4<T, S, R, 1, 4, 1>(p, c, a, s) : ring_go4<T, S, R, 2, 2, 1>(p, c, a, s);
+    return c.CH8 == 1 ? ring_go4<T, S, R, 1, 4, 1, kRingPF2d>(p, c, a, s)
+                      : ring_go4<T, S, R, 2, 2, 1, kRingPF2d>(p, c, a, s);
 }
 
 template <typename T>
@@ -59,8 +60,9 @@ bool ring_configure(const Problem &p, RingConfig &c)
     c.RS = (c.DZ * c.IW * c.CV + 63) / 64 * 64;
     c.NINS = c.RS / 64;
     if (c.NINS > 8 * kWaves) return false;
-    // NR = 4 ring rows, the zero slot, two staging rows of 16 padded pixels
-    c.lds = 4 * c.RS * 16 + 16 + 2 * 16 * (c.TPB * 2 * 16 + 16);
+    // PF + 1 ring rows, the zero slot, two staging rows of 16 padded pixels
+    const int nr = (is3 ? kRingPF3d : kRingPF2d) + 1;
+    c.lds = nr * c.RS * 16 + 16 + 2 * 16 * (c.TPB * 2 * 16 + 16);
     c.nmt = (p.Wo + 15) / 16;
     if (is3) {
         c.R = 7;                                           // short runs: 3D grids are small

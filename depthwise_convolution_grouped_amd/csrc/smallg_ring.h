@@ -28,6 +28,11 @@ namespace smallg {
 namespace {
 
 constexpr unsigned kRingMaxLds = 160 * 1024;   // the dynamic LDS limit every ring instance is raised to
+// Input rows in flight ahead of the arithmetic (the ring holds one more).
+// Measured on the ResNeXt-style and 3D N=8 workloads: 6 rows ahead (2D) and
+// all 8 of a 3D run's later rows issued up front time the same as 3 rows.
+constexpr int kRingPF2d = 3;
+constexpr int kRingPF3d = 3;
 
 struct RingParams {
     Div dCpg, dKpg;
@@ -40,7 +45,7 @@ struct RingParams {
     unsigned in_row, img_bytes, oimg_bytes;
 };
 
-template <typename T, int S, int R, int CH8, int NTW, int CPGC, int DZ>
+template <typename T, int S, int R, int CH8, int NTW, int CPGC, int DZ, int PF>
 __global__ __launch_bounds__(kBlock) void ring_kernel(RingParams q, const T *__restrict__ x,
                                                       const T *__restrict__ w,
                                                       const T *__restrict__ bias, T *__restrict__ y)
@@ -50,7 +55,7 @@ __global__ __launch_bounds__(kBlock) void ring_kernel(RingParams q, const T *__r
     constexpr int NSL = 3 * CH8;             // K slices of one input row
     constexpr int NSR = (NSL + 3) / 4;       // MFMAs per (input row, tile, window row)
     constexpr int NI = (R - 1) * S + 3;      // input rows of R output rows
-    constexpr int PF = 3;                    // rows in flight ahead of the arithmetic
+    static_assert(PF >= 1 && PF < NI, "rows in flight ahead of the arithmetic");
     constexpr int NR = PF + 1;               // ring rows
     constexpr int kMaxIns = 8;               // DMA instructions per wave per row
     constexpr int CVR = kWaves * NTW * CH8;  // 16-byte chunks per ring pixel (16 or 8)
@@ -204,10 +209,11 @@ __global__ __launch_bounds__(kBlock) void ring_kernel(RingParams q, const T *__r
         // the stores issued since remain: rows i+1 .. i+PF-1 and the stores
         // of steps i-PF .. i-1
         constexpr int later_rows = (i + PF - 1 < NI - 1 ? i + PF - 1 : NI - 1) - i;
-        constexpr int later_stores = (i - PF >= 0 ? stores_at(i - PF) : 0) +
-                                     (PF >= 2 && i - PF + 1 >= 0 ? stores_at(i - PF + 1) : 0) +
-                                     (PF >= 3 && i - PF + 2 >= 0 ? stores_at(i - PF + 2) : 0) +
-                                     (PF >= 4 && i - PF + 3 >= 0 ? stores_at(i - PF + 3) : 0);
+        constexpr int later_stores = [=]() constexpr {
+            int n = 0;
+            for (int k = i - PF; k < i; ++k) n += k >= 0 ? stores_at(k) : 0;
+            return n;
+        }();
         vm_wait(later_rows * nins + later_stores);
         __syncthreads();
         // the slot of row i + PF was last read at step i - 1: refill it
@@ -261,7 +267,7 @@ __global__ __launch_bounds__(kBlock) void ring_kernel(RingParams q, const T *__r
     __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
 }
 
-template <typename T, int S, int R, int CH8, int NTW, int CPGC, int DZ>
+template <typename T, int S, int R, int CH8, int NTW, int CPGC, int DZ, int PF>
 hipError_t ring_go(const Problem &p, const RingConfig &c, const Args &a, hipStream_t s)
 {
     RingParams q;
@@ -276,7 +282,7 @@ hipError_t ring_go(const Problem &p, const RingConfig &c, const Args &a, hipStre
     q.img_bytes = (unsigned)((long long)p.D * p.H * p.W * p.C() * 2);
     q.oimg_bytes = (unsigned)((long long)p.Ho * p.Wo * p.K() * 2);
     const int blocks = c.blocks;
-    auto k = ring_kernel<T, S, R, CH8, NTW, CPGC, DZ>;
+    auto k = ring_kernel<T, S, R, CH8, NTW, CPGC, DZ, PF>;
     static std::atomic<unsigned long long> lds_set{0};
     if (c.lds > 64 * 1024) {
         // the limit is raised to the largest LDS any configuration of this instance uses
@@ -287,14 +293,14 @@ hipError_t ring_go(const Problem &p, const RingConfig &c, const Args &a, hipStre
                    (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y);
 }
 
-template <typename T, int S, int R, int CH8, int NTW, int DZ>
+template <typename T, int S, int R, int CH8, int NTW, int DZ, int PF>
 hipError_t ring_go4(const Problem &p, const RingConfig &c, const Args &a, hipStream_t s)
 {
     switch (p.Cpg) {
-    case 1: return ring_go<T, S, R, CH8, NTW, 1, DZ>(p, c, a, s);
-    case 2: return ring_go<T, S, R, CH8, NTW, 2, DZ>(p, c, a, s);
-    case 4: return ring_go<T, S, R, CH8, NTW, 4, DZ>(p, c, a, s);
-    default: return ring_go<T, S, R, CH8, NTW, 8, DZ>(p, c, a, s);
+    case 1: return ring_go<T, S, R, CH8, NTW, 1, DZ, PF>(p, c, a, s);
+    case 2: return ring_go<T, S, R, CH8, NTW, 2, DZ, PF>(p, c, a, s);
+    case 4: return ring_go<T, S, R, CH8, NTW, 4, DZ, PF>(p, c, a, s);
+    default: return ring_go<T, S, R, CH8, NTW, 8, DZ, PF>(p, c, a, s);
     }
 }
 
