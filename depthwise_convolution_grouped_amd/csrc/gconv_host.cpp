@@ -19,7 +19,8 @@
 namespace gconv {
 namespace {
 
-constexpr int64_t kMaxElems = (int64_t)INT32_MAX;  // tensors must have < 2^31 elements
+constexpr int64_t kMaxElems = (int64_t)INT32_MAX;  // elements a launch may index in 32 bits
+constexpr int64_t kLim = (int64_t)INT32_MAX;       // bytes a launch's tensor may span (32-bit buffer offsets)
 
 // out = floor((in + 2 pad - dil (k - 1) - 1) / stride) + 1, or 0 if no window fits.
 int64_t out_extent(int64_t in, int64_t k, int64_t s, int64_t p, int64_t d)
@@ -35,6 +36,49 @@ int64_t sat_mul(int64_t a, int64_t b)
     if (a <= 0 || b <= 0) return a * b;
     if (a > cap / b) return cap;
     return a * b;
+}
+
+int64_t floor_div(int64_t a, int64_t b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
+int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
+int64_t max64(int64_t a, int64_t b) { return a > b ? a : b; }
+
+// The spatial axis a call too large for one launch per image is split
+// along: the outermost one (planes in 3D, rows in 2D), whose slices are
+// contiguous in every layout.
+int split_axis(const gconv_desc *d) { return d->ndim == 3 ? 0 : 1; }
+
+// Bytes of one slice along the split axis: inner extents x channels.
+int64_t slice_bytes(const gconv_desc *d, const int64_t ext[3], int64_t ch)
+{
+    int64_t b = ch * elem_size(d->dtype);
+    for (int a = split_axis(d) + 1; a < 3; ++a) b = sat_mul(b, ext[a]);
+    return b;
+}
+
+// Output slices per launch of a forward call split along the axis: the
+// most whose input window (with its halo) and output each span < 2^31 bytes.
+int64_t fwd_slices_per_launch(const gconv_desc *d, const int64_t out[3])
+{
+    const int a = split_axis(d);
+    const int64_t xs = slice_bytes(d, d->in, d->C), ys = slice_bytes(d, out, d->K);
+    const int64_t reach = d->dil[a] * (d->filt[a] - 1) + 1;     // input slices one output slice reads
+    const int64_t by_y = kLim / ys, in_fit = kLim / xs;
+    const int64_t by_x = in_fit < reach ? 0 : (in_fit - reach) / d->stride[a] + 1;
+    return min64(by_y, by_x);
+}
+
+// dx slices per launch of a backward-data call split along the axis: dx,
+// and the dy slices that reach it, each span < 2^31 bytes.
+int64_t bwd_slices_per_launch(const gconv_desc *d, const int64_t out[3])
+{
+    const int a = split_axis(d);
+    const int64_t xs = slice_bytes(d, d->in, d->C), ys = slice_bytes(d, out, d->K);
+    const int64_t reach = d->dil[a] * (d->filt[a] - 1);
+    const int64_t by_x = kLim / xs;
+    // n dx slices read at most floor((n - 1 + reach) / s) + 2 dy slices
+    const int64_t dy_fit = kLim / ys;
+    const int64_t by_y = dy_fit < 2 ? 0 : (dy_fit - 2) * d->stride[a] + 1 - reach;
+    return max64(0, min64(by_x, by_y));
 }
 
 int check_desc(const gconv_desc *d, int64_t out[3])
@@ -68,40 +112,31 @@ int check_desc(const gconv_desc *d, int64_t out[3])
     int64_t span = 0;
     for (int a = 0; a < 3; ++a)  // padded extent must also stay in int32
         span = span > d->in[a] + 2 * d->pad[a] ? span : d->in[a] + 2 * d->pad[a];
-    // x and y may exceed 2^31 elements as a batch: calls then split the batch
-    // into launches of whole images (every launch indexes in 32 bits), so
-    // only one image of each, and w, must stay below
-    const int64_t x_img = x_el / d->N, y_img = y_el / d->N;
-    if (x_img >= kMaxElems || y_img >= kMaxElems || w_el >= kMaxElems || span >= kMaxElems ||
-        d->K >= kMaxElems || d->C >= kMaxElems || Kpg >= kMaxElems || d->N >= kMaxElems || x_el >= INT64_MAX / 4 ||
-        y_el >= INT64_MAX / 4)
+    if (w_el >= kMaxElems || span >= kMaxElems || d->K >= kMaxElems || d->C >= kMaxElems ||
+        Kpg >= kMaxElems || d->N >= kMaxElems || x_el >= INT64_MAX / 4 || y_el >= INT64_MAX / 4)
+        return GCONV_ERR_TOO_LARGE;
+    // x and y may span more than a launch's 32-bit reach: calls then split
+    // the batch into launches of whole images, and an image too large for
+    // one launch into slices along the outermost spatial axis.  A slice
+    // window that alone exceeds the reach cannot be split further.
+    if (fwd_slices_per_launch(d, out) < 1 || bwd_slices_per_launch(d, out) < 1)
         return GCONV_ERR_TOO_LARGE;
     return GCONV_OK;
 }
 
 // Images per launch: the whole batch when x and y each span < 2^31 bytes,
-// else the most whole images that keep both below (at least one).  The
-// vector paths address a launch's tensors with 32-bit byte offsets, so a
-// byte limit keeps every launch on the path the dispatcher would pick for
-// its shape; the generic path indexes elements in 32 bits, which a launch
-// of one image below 2^31 elements also satisfies.
+// else the most whole images that keep both below; 0 when one image alone
+// does not fit (the image is then split into slices).  The vector paths
+// address a launch's tensors with 32-bit byte offsets, so a byte limit keeps
+// every launch on the path the dispatcher would pick for its shape.
 int64_t images_per_launch(const gconv_desc *d, const int64_t out[3])
 {
     const int64_t es = elem_size(d->dtype);
     const int64_t x_img = d->in[0] * d->in[1] * d->in[2] * d->C * es;
     const int64_t y_img = out[0] * out[1] * out[2] * d->K * es;
-    const int64_t nx = kMaxElems / x_img, ny = kMaxElems / y_img;
-    int64_t n = nx < ny ? nx : ny;
-    if (n < 1) n = 1;
+    const int64_t nx = kLim / x_img, ny = kLim / y_img;
+    const int64_t n = nx < ny ? nx : ny;
     return n < d->N ? n : d->N;
-}
-
-// The descriptor of one launch: d with a batch of n images.
-gconv_desc with_batch(const gconv_desc *d, int64_t n)
-{
-    gconv_desc t = *d;
-    t.N = n;
-    return t;
 }
 
 Problem to_problem(const gconv_desc *d, const int64_t out[3])
@@ -122,8 +157,132 @@ Problem to_problem(const gconv_desc *d, const int64_t out[3])
     return p;
 }
 
+// Sets a problem's input extent, leading pad and output extent along axis a.
+void set_axis(Problem &p, int a, int in, int pad, int out)
+{
+    if (a == 0) { p.D = in; p.pd = pad; p.Do = out; }
+    else { p.H = in; p.ph = pad; p.Ho = out; }
+}
+
+// One launch of a call: a problem whose tensors each span < 2^31 bytes and
+// the byte offsets of its input-side and output-side tensors (x and y for
+// forward, dy and dx for backward data) in the caller's buffers.  Its leading
+// pad along the split axis may differ from the trailing one (the window of
+// a slice can start inside the image); kernels take the leading pad and
+// the extents, never a symmetric pad.
+struct Piece {
+    Problem p;
+    size_t in_off, out_off;
+};
+
+// Calls f(piece, first, last) for the launches of a forward call: one
+// launch of the whole batch, else launches of whole images, else, image by
+// image, launches of output slices along the split axis whose input windows
+// (halo included) are taken from the image.  Stops at the first non-zero
+// status f returns.
+template <class F>
+int for_fwd_pieces(const gconv_desc *d, const int64_t out[3], F &&f)
+{
+    const size_t es = (size_t)elem_size(d->dtype);
+    const size_t x_img = (size_t)(d->in[0] * d->in[1] * d->in[2] * d->C) * es;
+    const size_t y_img = (size_t)(out[0] * out[1] * out[2] * d->K) * es;
+    const int64_t nl = images_per_launch(d, out);
+    if (nl >= 1) {
+        for (int64_t n0 = 0; n0 < d->N; n0 += nl) {
+            const int64_t n = d->N - n0 < nl ? d->N - n0 : nl;
+            Piece pc{to_problem(d, out), (size_t)n0 * x_img, (size_t)n0 * y_img};
+            pc.p.N = (int)n;
+            const int rc = f(pc, n0 == 0, n0 + n >= d->N);
+            if (rc != GCONV_OK) return rc;
+        }
+        return GCONV_OK;
+    }
+    const int a = split_axis(d);
+    const int64_t I = d->in[a], O = out[a], s = d->stride[a], pd = d->pad[a];
+    const int64_t reach = d->dil[a] * (d->filt[a] - 1) + 1;
+    const int64_t per = fwd_slices_per_launch(d, out);
+    const size_t xs = (size_t)slice_bytes(d, d->in, d->C), ys = (size_t)slice_bytes(d, out, d->K);
+    for (int64_t n = 0; n < d->N; ++n) {
+        for (int64_t o0 = 0; o0 < O; o0 += per) {
+            const int64_t o1 = min64(O, o0 + per);
+            const int64_t i_lo = o0 * s - pd, i_hi = (o1 - 1) * s - pd + reach;
+            int64_t lo = max64(i_lo, 0), hi = min64(i_hi, I);
+            // a window wholly inside the trailing padding keeps one real
+            // slice; its leading pad is then negative (generic kernel)
+            if (hi <= lo) {
+                lo = min64(lo, I - 1);
+                hi = lo + 1;
+            }
+            Piece pc{to_problem(d, out), (size_t)n * x_img + (size_t)lo * xs, (size_t)n * y_img + (size_t)o0 * ys};
+            pc.p.N = 1;
+            set_axis(pc.p, a, (int)(hi - lo), (int)(lo - i_lo), (int)(o1 - o0));
+            const int rc = f(pc, n == 0 && o0 == 0, n + 1 == d->N && o1 == O);
+            if (rc != GCONV_OK) return rc;
+        }
+    }
+    return GCONV_OK;
+}
+
+// The same for backward data: launches of whole images, else of dx slices
+// along the split axis with the dy slices that reach them.  In a piece's
+// problem the input extent is dx's and the output extent dy's.
+template <class F>
+int for_bwd_pieces(const gconv_desc *d, const int64_t out[3], F &&f)
+{
+    const size_t es = (size_t)elem_size(d->dtype);
+    const size_t x_img = (size_t)(d->in[0] * d->in[1] * d->in[2] * d->C) * es;
+    const size_t y_img = (size_t)(out[0] * out[1] * out[2] * d->K) * es;
+    const int64_t nl = images_per_launch(d, out);
+    if (nl >= 1) {
+        for (int64_t n0 = 0; n0 < d->N; n0 += nl) {
+            const int64_t n = d->N - n0 < nl ? d->N - n0 : nl;
+            Piece pc{to_problem(d, out), (size_t)n0 * y_img, (size_t)n0 * x_img};
+            pc.p.N = (int)n;
+            const int rc = f(pc, n0 == 0, n0 + n >= d->N);
+            if (rc != GCONV_OK) return rc;
+        }
+        return GCONV_OK;
+    }
+    const int a = split_axis(d);
+    const int64_t I = d->in[a], O = out[a], s = d->stride[a], pd = d->pad[a];
+    const int64_t reach = d->dil[a] * (d->filt[a] - 1);
+    const int64_t per = bwd_slices_per_launch(d, out);
+    const size_t xs = (size_t)slice_bytes(d, d->in, d->C), ys = (size_t)slice_bytes(d, out, d->K);
+    for (int64_t n = 0; n < d->N; ++n) {
+        for (int64_t i0 = 0; i0 < I; i0 += per) {
+            const int64_t i1 = min64(I, i0 + per);
+            // dy slices o with o s - pad + t dil in [i0, i1) for some tap t;
+            // taking the lower end rounded down keeps the leading pad
+            // pad + i0 - oa s >= dil (k - 1) >= 0 (extra slices add nothing)
+            int64_t oa = floor_div(i0 + pd - reach, s), ob = floor_div(i1 - 1 + pd, s);
+            oa = max64(0, min64(oa, O - 1));
+            ob = max64(oa, min64(ob, O - 1));
+            Piece pc{to_problem(d, out), (size_t)n * y_img + (size_t)oa * ys, (size_t)n * x_img + (size_t)i0 * xs};
+            pc.p.N = 1;
+            set_axis(pc.p, a, (int)(i1 - i0), (int)(pd + i0 - oa * s), (int)(ob - oa + 1));
+            const int rc = f(pc, n == 0 && i0 == 0, n + 1 == d->N && i1 == I);
+            if (rc != GCONV_OK) return rc;
+        }
+    }
+    return GCONV_OK;
+}
+
+// The first launch of a forward call (what selection and plans describe).
+Problem first_piece(const gconv_desc *d, const int64_t out[3])
+{
+    Problem first{};
+    for_fwd_pieces(d, out, [&](const Piece &pc, bool, bool) {
+        first = pc.p;
+        return 1;   // stop after the first
+    });
+    return first;
+}
+
 bool path_ok(const Problem &p, int path)
 {
+    // a slice whose window starts below the image (negative leading pad)
+    // runs on the generic kernel only
+    if (path != GCONV_PATH_GENERIC && (p.pd < 0 || p.ph < 0 || p.pw < 0)) return false;
     switch (path) {
     case GCONV_PATH_GENERIC: return generic::supported(p);
     case GCONV_PATH_DEPTHWISE: return depthwise::supported(p);
@@ -141,6 +300,7 @@ bool path_ok(const Problem &p, int path)
 // tile; everything else takes the generic kernel.
 int select(const Problem &p)
 {
+    if (p.pd < 0 || p.ph < 0 || p.pw < 0) return GCONV_PATH_GENERIC;
     if (depthwise::supported(p)) return GCONV_PATH_DEPTHWISE;
     if (p.dtype != GCONV_F32 && p.Cpg >= 32 && p.Kpg >= 32) {
         if (ighalo::supported(p)) return GCONV_PATH_IGHALO;
@@ -165,47 +325,21 @@ gconv_plan plan_of(const Problem &p, int path)
 
 bool aligned(const void *ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
 
-int run(const gconv_desc *d, int path, const void *x, const void *w, const void *bias,
-        void *y, void *stream, void *ev_start = nullptr, void *ev_stop = nullptr)
+// The path one launch takes (GCONV_PATH_AUTO: the dispatcher's pick, the
+// generic kernel for pointers the 16-byte vector paths cannot take), or a
+// negative status for a forced path that cannot run it.
+int launch_path(const Problem &p, int path, const void *x, const void *w, const void *bias, const void *y)
 {
-    int64_t out[3];
-    int rc = check_desc(d, out);
-    if (rc != GCONV_OK) return rc;
-    if (!x || !w || !y) return GCONV_ERR_NULL_PTR;
-    const int64_t nl = images_per_launch(d, out);
-    if (nl < d->N) {
-        // a batch of >= 2^31 elements: consecutive launches of nl whole images,
-        // the start event bound to the first and the stop event to the last
-        const size_t es = (size_t)elem_size(d->dtype);
-        const size_t x_img = (size_t)(d->in[0] * d->in[1] * d->in[2] * d->C) * es;
-        const size_t y_img = (size_t)(out[0] * out[1] * out[2] * d->K) * es;
-        for (int64_t n0 = 0; n0 < d->N; n0 += nl) {
-            const int64_t n = d->N - n0 < nl ? d->N - n0 : nl;
-            const gconv_desc t = with_batch(d, n);
-            rc = run(&t, path, (const char *)x + (size_t)n0 * x_img, w, bias, (char *)y + (size_t)n0 * y_img,
-                     stream, n0 == 0 ? ev_start : nullptr, n0 + n >= d->N ? ev_stop : nullptr);
-            if (rc != GCONV_OK) return rc;
-        }
-        return GCONV_OK;
-    }
-    Problem p = to_problem(d, out);
-    const uintptr_t es = (uintptr_t)elem_size(p.dtype);
-    if (!aligned(x, es) || !aligned(w, es) || !aligned(y, es) || (bias && !aligned(bias, es)))
-        return GCONV_ERR_MISALIGNED;
-    // The vector paths load and store 16-byte channel vectors; automatic
-    // dispatch falls back to the generic kernel for other pointers.
-    const bool vec_ok = aligned(x, 16) && aligned(w, 16) && aligned(y, 16) &&
-                        (!bias || aligned(bias, 16));
-    if (path == GCONV_PATH_AUTO) {
-        path = select(p);
-        if (!vec_ok) path = GCONV_PATH_GENERIC;
-    } else {
-        if (path < 0 || path >= GCONV_NUM_PATHS) return GCONV_ERR_BAD_PATH;
-        if (!path_ok(p, path)) return GCONV_ERR_PATH_UNSUPPORTED;
-        if (path != GCONV_PATH_GENERIC && !vec_ok) return GCONV_ERR_MISALIGNED;
-    }
-    Args a{x, w, bias, y, (hipEvent_t)ev_start, (hipEvent_t)ev_stop};
-    hipStream_t s = (hipStream_t)stream;
+    const bool vec_ok = aligned(x, 16) && aligned(w, 16) && aligned(y, 16) && (!bias || aligned(bias, 16));
+    if (path == GCONV_PATH_AUTO) return vec_ok ? select(p) : GCONV_PATH_GENERIC;
+    if (path < 0 || path >= GCONV_NUM_PATHS) return GCONV_ERR_BAD_PATH;
+    if (!path_ok(p, path)) return GCONV_ERR_PATH_UNSUPPORTED;
+    if (path != GCONV_PATH_GENERIC && !vec_ok) return GCONV_ERR_MISALIGNED;
+    return path;
+}
+
+int launch_problem(const Problem &p, int path, const Args &a, hipStream_t s)
+{
     hipError_t e;
     switch (path) {
     case GCONV_PATH_DEPTHWISE: e = depthwise::launch(p, a, s); break;
@@ -214,8 +348,35 @@ int run(const gconv_desc *d, int path, const void *x, const void *w, const void 
     case GCONV_PATH_IGHALO: e = ighalo::launch(p, a, s); break;
     default: e = generic::launch(p, a, s); break;
     }
-    if (e != hipSuccess) return GCONV_ERR_LAUNCH;
-    return GCONV_OK;
+    return e == hipSuccess ? GCONV_OK : GCONV_ERR_LAUNCH;
+}
+
+int run(const gconv_desc *d, int path, const void *x, const void *w, const void *bias,
+        void *y, void *stream, void *ev_start = nullptr, void *ev_stop = nullptr)
+{
+    int64_t out[3];
+    int rc = check_desc(d, out);
+    if (rc != GCONV_OK) return rc;
+    if (!x || !w || !y) return GCONV_ERR_NULL_PTR;
+    const uintptr_t es = (uintptr_t)elem_size(d->dtype);
+    if (!aligned(x, es) || !aligned(w, es) || !aligned(y, es) || (bias && !aligned(bias, es)))
+        return GCONV_ERR_MISALIGNED;
+    // every launch's path is settled before the first is enqueued, so a
+    // forced path that cannot take one of them launches nothing
+    rc = for_fwd_pieces(d, out, [&](const Piece &pc, bool, bool) {
+        const int pth = launch_path(pc.p, path, (const char *)x + pc.in_off, w, bias, (const char *)y + pc.out_off);
+        return pth < 0 ? pth : (int)GCONV_OK;
+    });
+    if (rc != GCONV_OK) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    return for_fwd_pieces(d, out, [&](const Piece &pc, bool first, bool last) {
+        const void *xp = (const char *)x + pc.in_off;
+        void *yp = (char *)y + pc.out_off;
+        const int pth = launch_path(pc.p, path, xp, w, bias, yp);
+        // the start event is bound to the first launch, the stop event to the last
+        Args a{xp, w, bias, yp, first ? (hipEvent_t)ev_start : nullptr, last ? (hipEvent_t)ev_stop : nullptr};
+        return launch_problem(pc.p, pth, a, s);
+    });
 }
 
 // Backward data at stride 1 is a forward convolution of dy (the input, with
@@ -228,17 +389,22 @@ bool bwd_as_forward(const gconv_desc *d)
     return true;
 }
 
-gconv_desc bwd_forward_desc(const gconv_desc *d, const int64_t out[3])
+// The forward problem that computes a backward-data piece at stride 1:
+// input dy (the piece's output extents, K channels), output dx (its input
+// extents, C channels), leading pad dil (k - 1) - pad per axis; false when a
+// pad would be negative.
+bool bwd_forward_problem(const Problem &q, Problem &t)
 {
-    gconv_desc t = *d;
-    t.C = d->K;
-    t.K = d->C;
-    for (int a = 0; a < 3; ++a) {
-        t.in[a] = out[a];
-        t.stride[a] = 1;
-        t.pad[a] = d->dil[a] * (d->filt[a] - 1) - d->pad[a];
-    }
-    return t;
+    t = q;
+    t.Cpg = q.Kpg;
+    t.Kpg = q.Cpg;
+    t.D = q.Do; t.H = q.Ho; t.W = q.Wo;
+    t.Do = q.D; t.Ho = q.H; t.Wo = q.W;
+    t.sd = t.sh = t.sw = 1;
+    t.pd = q.dd * (q.Z - 1) - q.pd;
+    t.ph = q.dh * (q.Y - 1) - q.ph;
+    t.pw = q.dw * (q.X - 1) - q.pw;
+    return q.sd == 1 && q.sh == 1 && q.sw == 1 && t.pd >= 0 && t.ph >= 0 && t.pw >= 0;
 }
 
 size_t weight_bytes(const gconv_desc *d)
@@ -256,29 +422,23 @@ int run_bwd_data(const gconv_desc *d, const void *dy, const void *w, void *dx, v
     if (!dy || !w || !dx) return GCONV_ERR_NULL_PTR;
     const uintptr_t es = (uintptr_t)elem_size(d->dtype);
     if (!aligned(dy, es) || !aligned(w, es) || !aligned(dx, es)) return GCONV_ERR_MISALIGNED;
-    const int64_t nl = images_per_launch(d, out);
-    if (nl < d->N) {
-        // a batch of >= 2^31 elements: launches of nl whole images
-        const size_t x_img = (size_t)(d->in[0] * d->in[1] * d->in[2] * d->C) * es;
-        const size_t y_img = (size_t)(out[0] * out[1] * out[2] * d->K) * es;
-        for (int64_t n0 = 0; n0 < d->N; n0 += nl) {
-            const int64_t n = d->N - n0 < nl ? d->N - n0 : nl;
-            const gconv_desc t = with_batch(d, n);
-            rc = run_bwd_data(&t, (const char *)dy + (size_t)n0 * y_img, w, (char *)dx + (size_t)n0 * x_img, ws,
-                              ws_bytes, direct, stream);
-            if (rc != GCONV_OK) return rc;
-        }
-        return GCONV_OK;
-    }
-    const Problem p = to_problem(d, out);
     hipStream_t s = (hipStream_t)stream;
-    if (!direct && bwd_as_forward(d) && ws && ws_bytes >= weight_bytes(d) && aligned(ws, 16)) {
-        if (bwd::launch_flip(p, w, ws, s) != hipSuccess) return GCONV_ERR_LAUNCH;
-        const gconv_desc t = bwd_forward_desc(d, out);
-        return run(&t, GCONV_PATH_AUTO, dy, ws, nullptr, dx, stream);
+    const bool route = !direct && bwd_as_forward(d) && ws && ws_bytes >= weight_bytes(d) && aligned(ws, 16);
+    if (route) {
+        Problem whole = to_problem(d, out);
+        if (bwd::launch_flip(whole, w, ws, s) != hipSuccess) return GCONV_ERR_LAUNCH;
     }
-    if (bwd::launch_direct(p, dy, w, dx, s) != hipSuccess) return GCONV_ERR_LAUNCH;
-    return GCONV_OK;
+    return for_bwd_pieces(d, out, [&](const Piece &pc, bool, bool) {
+        const void *dyp = (const char *)dy + pc.in_off;
+        void *dxp = (char *)dx + pc.out_off;
+        Problem t;
+        if (route && bwd_forward_problem(pc.p, t)) {
+            const int pth = launch_path(t, GCONV_PATH_AUTO, dyp, ws, nullptr, dxp);
+            Args a{dyp, ws, nullptr, dxp};
+            return launch_problem(t, pth, a, s);
+        }
+        return bwd::launch_direct(pc.p, dyp, w, dxp, s) == hipSuccess ? (int)GCONV_OK : (int)GCONV_ERR_LAUNCH;
+    });
 }
 
 size_t bwd_weight_partials_bytes(const Problem &p, int nch)
@@ -331,14 +491,14 @@ GCONV_API int gconv_out_dims(const gconv_desc *d, int64_t out[3])
     return GCONV_OK;
 }
 
-// Selection and plans describe one launch (the first, for a split batch).
+// Selection and plans describe one launch (the first, for a call split
+// into launches); support covers every launch of the call.
 GCONV_API int gconv_select_path(const gconv_desc *d)
 {
     int64_t out[3];
     int rc = check_desc(d, out);
     if (rc != GCONV_OK) return rc;
-    const gconv_desc t = with_batch(d, images_per_launch(d, out));
-    return select(to_problem(&t, out));
+    return select(first_piece(d, out));
 }
 
 GCONV_API int gconv_path_supported(const gconv_desc *d, int path)
@@ -347,8 +507,12 @@ GCONV_API int gconv_path_supported(const gconv_desc *d, int path)
     int rc = check_desc(d, out);
     if (rc != GCONV_OK) return rc;
     if (path < 0 || path >= GCONV_NUM_PATHS) return GCONV_ERR_BAD_PATH;
-    const gconv_desc t = with_batch(d, images_per_launch(d, out));
-    return path_ok(to_problem(&t, out), path) ? 1 : 0;
+    bool ok = true;
+    for_fwd_pieces(d, out, [&](const Piece &pc, bool, bool) {
+        ok = ok && path_ok(pc.p, path);
+        return ok ? (int)GCONV_OK : 1;
+    });
+    return ok ? 1 : 0;
 }
 
 GCONV_API int gconv_get_plan(const gconv_desc *d, int path, gconv_plan *plan)
@@ -357,8 +521,7 @@ GCONV_API int gconv_get_plan(const gconv_desc *d, int path, gconv_plan *plan)
     int64_t out[3];
     int rc = check_desc(d, out);
     if (rc != GCONV_OK) return rc;
-    const gconv_desc t = with_batch(d, images_per_launch(d, out));
-    Problem p = to_problem(&t, out);
+    const Problem p = first_piece(d, out);
     if (path == GCONV_PATH_AUTO) path = select(p);
     else if (path < 0 || path >= GCONV_NUM_PATHS) return GCONV_ERR_BAD_PATH;
     else if (!path_ok(p, path)) return GCONV_ERR_PATH_UNSUPPORTED;

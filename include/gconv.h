@@ -80,9 +80,11 @@ typedef enum gconv_status {
                                        negative pad, 2D with depth entries set */
     GCONV_ERR_BAD_OUT_DIMS = -2,    /* an output extent would be <= 0 */
     GCONV_ERR_NULL_PTR = -3,        /* desc, x, w or y is NULL */
-    GCONV_ERR_TOO_LARGE = -4,       /* one image of x or y, or w, has >= 2^31 elements (a
-                                       larger batch is split into launches of whole images;
-                                       backward weight takes no split), or N >= 2^31 */
+    GCONV_ERR_TOO_LARGE = -4,       /* w has >= 2^31 elements, N or an extent >= 2^31, or
+                                       one slice along the outermost spatial axis (a row
+                                       in 2D, a plane in 3D) of x or y, with the window it
+                                       needs, spans >= 2^31 bytes; backward weight: x or y
+                                       has >= 2^31 elements */
     GCONV_ERR_MISALIGNED = -5,      /* a pointer is not aligned as the path needs */
     GCONV_ERR_BAD_PATH = -6,        /* unknown path id */
     GCONV_ERR_PATH_UNSUPPORTED = -7,/* forced path cannot run this problem */
@@ -165,14 +167,17 @@ int gconv_get_plan(const gconv_desc *d, int path, gconv_plan *plan);
 /* Forward convolution, asynchronous on `stream` (a hipStream_t; NULL = the
  * null stream).  x, w, bias (NULL = no bias) and y are device pointers in the
  * layouts above, aligned to the element size.  Exactly one kernel is
- * launched when x and y each have < 2^31 elements; a larger batch runs as
- * consecutive launches of as many whole images as keep both below (every
- * launch indexes in 32 bits), which gconv_select_path and gconv_get_plan
- * describe.  The CK Python examples README's split_image option
- * (Config-options harness) splits spatial dims for large tensors; here the
- * batch is split instead, which needs no halo exchange between launches,
- * and one image of >= 2^31 elements is rejected.  The caller synchronises the stream before reading y.  Results
- * are bitwise deterministic from run to run (no atomics). */
+ * launched when x and y each span < 2^31 bytes (every launch addresses its
+ * tensors with 32-bit offsets).  Larger tensors are split, as the CK Python
+ * examples README's split_image option does for large tensors
+ * (Config-options harness): a batch into consecutive launches of as many
+ * whole images as fit, and an image that alone does not fit into launches
+ * of output slices along its outermost spatial axis (rows in 2D, planes in
+ * 3D), each reading the input slices its window covers, halo included, from
+ * the same x; no data is copied.  gconv_select_path and gconv_get_plan
+ * describe the first launch.  The caller synchronises the stream before
+ * reading y.  Results are bitwise deterministic from run to run (no
+ * atomics). */
 int gconv_fwd(const gconv_desc *d, const void *x, const void *w,
               const void *bias, void *y, void *stream);
 
@@ -185,10 +190,12 @@ int gconv_fwd_path(const gconv_desc *d, int path, const void *x, const void *w,
                    const void *bias, void *y, void *stream);
 
 /* As gconv_fwd_path, and binds two HIP events (hipEvent_t, either may be
- * NULL; created by the caller, with timing enabled) to the one kernel
- * dispatch: hipEventElapsedTime(start, stop) is then that kernel's execution
- * time, with no marker packets between the events and the kernel.  For
- * measurement; the result in y is the same as gconv_fwd_path's. */
+ * NULL; created by the caller, with timing enabled) to the kernel dispatch
+ * (the start event to the first and the stop event to the last launch of a
+ * split call): hipEventElapsedTime(start, stop) is then the kernels'
+ * execution time, with no marker packets between the events and the
+ * kernels.  For measurement; the result in y is the same as
+ * gconv_fwd_path's. */
 int gconv_fwd_timed(const gconv_desc *d, int path, const void *x, const void *w,
                     const void *bias, void *y, void *stream, void *ev_start,
                     void *ev_stop);
@@ -218,13 +225,16 @@ int gconv_bwd_data_workspace(const gconv_desc *d, size_t *bytes);
  * caller owns, 16-byte aligned, may be NULL) of `workspace_bytes`: when it
  * holds gconv_bwd_data_workspace bytes, two kernels run (the weight
  * transform into the workspace, then the forward kernel); otherwise one
- * direct kernel runs.  The workspace may be reused once the stream has
- * passed the call.  Deterministic from run to run.  Status codes as for
- * gconv_fwd. */
+ * direct kernel runs.  Tensors too large for one launch are split as in
+ * gconv_fwd: whole images, else slices of dx along the outermost spatial
+ * axis, each with the dy slices that reach it.  The workspace may be reused
+ * once the stream has passed the call.  Deterministic from run to run.
+ * Status codes as for gconv_fwd. */
 int gconv_bwd_data(const gconv_desc *d, const void *dy, const void *w, void *dx,
                    void *workspace, size_t workspace_bytes, void *stream);
 
-/* Backward data on the direct kernel alone (any shape, one launch). */
+/* Backward data on the direct kernel alone (any shape; one launch unless
+ * the tensors must be split as for gconv_bwd_data). */
 int gconv_bwd_data_direct(const gconv_desc *d, const void *dy, const void *w, void *dx,
                           void *stream);
 

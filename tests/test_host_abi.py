@@ -72,7 +72,8 @@ def test_valid_descriptor():
     (dict(spatial=(2, 2), pad=(0, 0)), G.GCONV_ERR_BAD_OUT_DIMS),
     (dict(spatial=(5, 5), pad=(0, 0), dil=(3, 3)), G.GCONV_ERR_BAD_OUT_DIMS),
     (dict(N=1 << 20, spatial=(1024, 1024)), G.GCONV_OK),           # split into launches of whole images
-    (dict(N=1, spatial=(65536, 65536)), G.GCONV_ERR_TOO_LARGE),    # one image of x has >= 2^31 elements
+    (dict(N=1, spatial=(65536, 65536)), G.GCONV_OK),               # one image of 2^35 elements: split into row slices
+    (dict(N=1, spatial=(4, 1 << 28)), G.GCONV_ERR_TOO_LARGE),      # one row of x spans 2^32 bytes: no slice fits
     (dict(N=1 << 40), G.GCONV_ERR_TOO_LARGE),
 ])
 def test_validation_errors(kw, status):
@@ -361,3 +362,18 @@ def test_half_batch_between_2_30_and_2_31_elements_stays_on_the_mfma_path():
     assert G.gconv_path_name(G.gconv_select_path(d)) == "ighalo_mfma"
     one = G.make_desc(2, "bf16", 64, 8, 1024, 1024, (14, 14), (3, 3), (1, 1), (1, 1), (1, 1))
     assert G.gconv_select_path(one) == G.gconv_select_path(d)
+
+
+def test_image_beyond_one_launch_is_split_into_slices():
+    # one fp16 depthwise image of 6000 x 6000 x 64 = 2.3 G elements (4.6 GB):
+    # launches of output row slices, each on the vector path it would take
+    big = G.make_desc(2, "f16", 1, 64, 64, 64, (6000, 6000), (3, 3), (1, 1), (1, 1), (1, 1))
+    assert G.gconv_validate(big) == G.GCONV_OK
+    assert G.gconv_path_name(G.gconv_select_path(big)) == "depthwise"
+    assert G.gconv_path_supported(big, G.GCONV_PATH_DEPTHWISE) == 1
+    # the same in 3D splits along the planes
+    big3 = G.make_desc(3, "bf16", 1, 8, 64, 64, (600, 240, 240), (3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1))
+    assert G.gconv_validate(big3) == G.GCONV_OK
+    assert G.gconv_select_path(big3) >= 0
+    # backward data accepts it as well (dx slices with the dy slices reaching them)
+    assert G.gconv_bwd_data_workspace(big) == 64 * 9 * 2
