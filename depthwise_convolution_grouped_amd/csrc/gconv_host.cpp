@@ -446,27 +446,74 @@ size_t bwd_weight_partials_bytes(const Problem &p, int nch)
     return nch > 1 ? (size_t)nch * (size_t)p.G * p.Kpg * p.taps() * p.Cpg * sizeof(float) : 0;
 }
 
+// Backward weight reduces over the whole batch.  A batch too large for one
+// launch runs stage 1 as launches of whole images, each writing its own
+// chunks of partial sums into the workspace (consecutive ranges, in batch
+// order), and one stage 2 adds them all in chunk order.  The launches'
+// chunk counts, and so the summation order, depend only on the descriptor
+// and the workspace size.
+struct BwdwPlan {
+    int64_t nl;        // images per launch
+    int64_t launches;
+    int per;           // chunks per launch (the last may use fewer)
+    int total;         // chunks in all (1: stage 1 writes dw itself)
+};
+
+int bwdw_plan(const gconv_desc *d, const int64_t out[3], size_t ws_bytes, bool have_ws, BwdwPlan &pl)
+{
+    pl.nl = images_per_launch(d, out);
+    if (pl.nl < 1) return GCONV_ERR_TOO_LARGE;           // one image beyond a launch: not split for this reduction
+    pl.launches = (d->N + pl.nl - 1) / pl.nl;
+    gconv_desc t = *d;
+    t.N = pl.nl;
+    const Problem p = to_problem(&t, out);
+    const size_t per_chunk = (size_t)p.G * p.Kpg * p.taps() * p.Cpg * sizeof(float);
+    const int64_t room = have_ws ? (int64_t)(ws_bytes / per_chunk) : 0;
+    int64_t want = bwdw::ideal_chunks(p);
+    if (pl.launches == 1) {
+        pl.per = (int)(room >= 2 ? min64(want, room) : 1);
+        pl.total = pl.per;
+        return GCONV_OK;
+    }
+    // every launch needs at least one chunk of its own in the workspace
+    if (room < pl.launches) return GCONV_ERR_TOO_LARGE;
+    pl.per = (int)max64(1, min64(want, room / pl.launches));
+    pl.total = (int)(pl.per * pl.launches);
+    return GCONV_OK;
+}
+
 int run_bwd_weight(const gconv_desc *d, const void *x, const void *dy, void *dw, void *ws,
                    size_t ws_bytes, void *stream)
 {
     int64_t out[3];
     int rc = check_desc(d, out);
     if (rc != GCONV_OK) return rc;
-    // its reduction runs over the whole batch: no split into launches
-    const int64_t x_all = d->N * d->in[0] * d->in[1] * d->in[2] * d->C;
-    const int64_t y_all = d->N * out[0] * out[1] * out[2] * d->K;
-    if (x_all >= kMaxElems || y_all >= kMaxElems) return GCONV_ERR_TOO_LARGE;
     if (!x || !dy || !dw) return GCONV_ERR_NULL_PTR;
     const uintptr_t es = (uintptr_t)elem_size(d->dtype);
     if (!aligned(x, es) || !aligned(dy, es) || !aligned(dw, es)) return GCONV_ERR_MISALIGNED;
-    const Problem p = to_problem(d, out);
-    int nch = bwdw::ideal_chunks(p);
-    const size_t per = bwd_weight_partials_bytes(p, 2) / 2;   // one chunk of partial sums
-    if (!ws || !aligned(ws, 4)) nch = 1;
-    else if ((size_t)nch * per > ws_bytes) nch = (int)(ws_bytes / per);
-    if (nch < 1) nch = 1;
-    if (bwdw::launch(p, x, dy, dw, (float *)ws, nch, (hipStream_t)stream) != hipSuccess)
-        return GCONV_ERR_LAUNCH;
+    const bool have_ws = ws && aligned(ws, 4);
+    BwdwPlan pl;
+    rc = bwdw_plan(d, out, ws_bytes, have_ws, pl);
+    if (rc != GCONV_OK) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    const size_t x_img = (size_t)(d->in[0] * d->in[1] * d->in[2] * d->C) * es;
+    const size_t y_img = (size_t)(out[0] * out[1] * out[2] * d->K) * es;
+    Problem whole = to_problem(d, out);
+    const size_t welems = (size_t)whole.G * whole.Kpg * whole.taps() * whole.Cpg;
+    int base = 0;
+    for (int64_t n0 = 0; n0 < d->N; n0 += pl.nl) {
+        gconv_desc t = *d;
+        t.N = d->N - n0 < pl.nl ? d->N - n0 : pl.nl;
+        const Problem p = to_problem(&t, out);
+        int used = 0;
+        const bool final_ = pl.total == 1;
+        if (bwdw::stage1(p, (const char *)x + (size_t)n0 * x_img, (const char *)dy + (size_t)n0 * y_img,
+                         final_ ? nullptr : (float *)ws + (size_t)base * welems, final_ ? dw : nullptr, pl.per,
+                         &used, s) != hipSuccess)
+            return GCONV_ERR_LAUNCH;
+        base += used;
+    }
+    if (pl.total > 1 && bwdw::stage2(whole, (const float *)ws, dw, base, s) != hipSuccess) return GCONV_ERR_LAUNCH;
     return GCONV_OK;
 }
 
@@ -576,8 +623,17 @@ GCONV_API int gconv_bwd_weight_workspace(const gconv_desc *d, size_t *bytes)
     int64_t out[3];
     int rc = check_desc(d, out);
     if (rc != GCONV_OK) return rc;
-    const Problem p = to_problem(d, out);
-    *bytes = bwd_weight_partials_bytes(p, bwdw::ideal_chunks(p));
+    const int64_t nl = images_per_launch(d, out);
+    if (nl < 1) return GCONV_ERR_TOO_LARGE;
+    gconv_desc t = *d;
+    t.N = nl;
+    const Problem p = to_problem(&t, out);
+    const int64_t launches = (d->N + nl - 1) / nl;
+    const int per = bwdw::ideal_chunks(p);
+    // one launch: the ideal chunks (none when one chunk fills the chip); a
+    // split batch: the ideal chunks of every launch
+    *bytes = launches == 1 ? bwd_weight_partials_bytes(p, per)
+                           : (size_t)launches * (size_t)per * (size_t)p.G * p.Kpg * p.taps() * p.Cpg * sizeof(float);
     return GCONV_OK;
 }
 

@@ -110,11 +110,28 @@ hipError_t launch_direct(const Problem &p, const void *dy, const void *w, void *
 hipError_t launch_flip(const Problem &p, const void *w, void *wt, hipStream_t s);
 }
 
-// Backward weight (k_bwd_weight.hip).  `p` is the forward problem; ws holds
-// nch x (weight elements) fp32 partial sums when nch > 1.
+// Backward weight (k_bwd_weight.hip).  `p` is the forward problem of one
+// launch.  stage1 picks the route (depthwise channel vectors, the MFMA
+// implicit GEMM, register tiles, plain) and writes the partial sums of at
+// most nch chunks to ws[chunk][f] (*used of them), or, with dw non-null and
+// nch == 1, dw itself; stage2 adds nch chunks in order and rounds once.
 namespace bwdw {
 int ideal_chunks(const Problem &p);
-hipError_t launch(const Problem &p, const void *x, const void *dy, void *dw, float *ws, int nch, hipStream_t s);
+hipError_t stage1(const Problem &p, const void *x, const void *dy, float *ws, void *dw, int nch, int *used,
+                  hipStream_t s);
+hipError_t stage2(const Problem &p, const float *ws, void *dw, int nch, hipStream_t s);
+}
+
+// Backward weight, stage 1 on the matrix cores (k_bwd_weight_mfma.hip):
+// half types whose groups merge into super-groups of 16-multiple channel
+// counts, windows of 1, 9, 25 or 27 taps.  stage1 writes the partial sums
+// of at most nch chunks of output pixels to ws[chunk][f] (*used of them),
+// or, with dw non-null and nch == 1, dw itself (rounded once).
+namespace bwdw_mfma {
+bool supported(const Problem &p);
+int chunks(const Problem &p);
+hipError_t stage1(const Problem &p, const void *x, const void *dy, float *ws, void *dw, int nch, int *used,
+                  hipStream_t s);
 }
 
 inline int elem_size(int dtype) { return dtype == GCONV_F32 ? 4 : 2; }

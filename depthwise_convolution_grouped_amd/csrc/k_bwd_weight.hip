@@ -345,10 +345,12 @@ bool dw_ok(const Problem &p)
     return p.Cpg == 1 && p.Kpg == 1 && p.taps() == kDwTaps && p.G % vec == 0 && p.G / vec <= kBlock;
 }
 
-// chunks for the depthwise kernel: two workgroups per CU, at most
-// `nch` (what the workspace holds) and at most kDwChunks so stage 2 stays short
+// Stage 1 of the depthwise kernel: two workgroups per CU, at most `nch`
+// chunks (what the workspace holds) and at most kDwChunks so stage 2 stays
+// short; one chunk writes dw directly when dw is given.
 template <typename T>
-hipError_t go_dw(const Problem &p, const void *x, const void *dy, void *dw, float *ws, int nch, hipStream_t s)
+hipError_t go_dw(const Problem &p, const void *x, const void *dy, void *dw, float *ws, int nch, int *used,
+                 hipStream_t s)
 {
     constexpr int VEC = 16 / (int)sizeof(T);
     const int slots = kBlock / (p.G / VEC);
@@ -359,15 +361,13 @@ hipError_t go_dw(const Problem &p, const void *x, const void *dy, void *dw, floa
     if (want < 1) want = 1;
     const int ppc = (int)((M + want - 1) / want);
     const int chunks = (int)((M + ppc - 1) / ppc);
-    const int welems = p.G * kDwTaps;
+    *used = chunks;
     Args a{};
-    if (chunks == 1)
+    if (chunks == 1 && dw)
         return enqueue(dw_partial_kernel<T, true>, dim3(1), dim3(kBlock), 0, s, a, p, (const T *)x,
                        (const T *)dy, (float *)nullptr, (T *)dw, ppc);
-    hipError_t e = enqueue(dw_partial_kernel<T, false>, dim3(chunks), dim3(kBlock), 0, s, a, p, (const T *)x,
-                           (const T *)dy, ws, (T *)nullptr, ppc);
-    if (e != hipSuccess) return e;
-    return reduce<T>(ws, (T *)dw, welems, chunks, s);
+    return enqueue(dw_partial_kernel<T, false>, dim3(chunks), dim3(kBlock), 0, s, a, p, (const T *)x,
+                   (const T *)dy, ws, (T *)nullptr, ppc);
 }
 
 bool tile_ok(const Problem &p)
@@ -375,41 +375,47 @@ bool tile_ok(const Problem &p)
     return p.dtype != GCONV_F32 && p.Cpg % 8 == 0 && p.Kpg % 4 == 0;
 }
 
+// Stage 1 of the register-tiled and plain kernels: chunks of output rows.
 template <typename T>
-hipError_t go(const Problem &p, const void *x, const void *dy, void *dw, float *ws, int nch, hipStream_t s)
+hipError_t go(const Problem &p, const void *x, const void *dy, void *dw, float *ws, int nch, int *used,
+              hipStream_t s)
 {
     const int welems = p.G * p.Kpg * p.taps() * p.Cpg;
     const int rows = p.N * p.Do * p.Ho;
     const int rpc = (rows + nch - 1) / nch;
     nch = (rows + rpc - 1) / rpc;                  // no empty chunk
+    *used = nch;
+    const bool final_ = nch == 1 && dw;
     const dim3 grid((unsigned)((welems + kBlock - 1) / kBlock), (unsigned)nch);
     Args a{};
     if (tile_ok(p) && ((uintptr_t)x & 15) == 0 && ((uintptr_t)dy & 7) == 0) {
         const int ntiles = welems / 32;
         const dim3 tg((unsigned)((ntiles + kBlock - 1) / kBlock), (unsigned)nch);
-        if (nch == 1)
+        if (final_)
             return enqueue(tile_partial_kernel<T, true>, tg, dim3(kBlock), 0, s, a, p, (const T *)x, (const T *)dy,
                            (float *)nullptr, (T *)dw, ntiles, rpc);
-        hipError_t e = enqueue(tile_partial_kernel<T, false>, tg, dim3(kBlock), 0, s, a, p, (const T *)x,
-                               (const T *)dy, ws, (T *)nullptr, ntiles, rpc);
-        if (e != hipSuccess) return e;
-        return reduce<T>(ws, (T *)dw, welems, nch, s);
+        return enqueue(tile_partial_kernel<T, false>, tg, dim3(kBlock), 0, s, a, p, (const T *)x,
+                       (const T *)dy, ws, (T *)nullptr, ntiles, rpc);
     }
-    if (nch == 1)
+    if (final_)
         return enqueue(partial_kernel<T, true>, grid, dim3(kBlock), 0, s, a, p, (const T *)x, (const T *)dy,
                        (float *)nullptr, (T *)dw, welems, rpc);
-    hipError_t e = enqueue(partial_kernel<T, false>, grid, dim3(kBlock), 0, s, a, p, (const T *)x,
-                           (const T *)dy, ws, (T *)nullptr, welems, rpc);
-    if (e != hipSuccess) return e;
-    return reduce<T>(ws, (T *)dw, welems, nch, s);
+    return enqueue(partial_kernel<T, false>, grid, dim3(kBlock), 0, s, a, p, (const T *)x,
+                   (const T *)dy, ws, (T *)nullptr, welems, rpc);
+}
+
+bool vec_aligned(const void *x, const void *dy)
+{
+    return ((uintptr_t)x & 15) == 0 && ((uintptr_t)dy & 15) == 0;
 }
 
 }  // namespace
 
-// Chunks that fill the chip: about 256 K stage-1 threads (one per weight
-// element, or per 4 x 8 tile on the tiled route), at most one chunk per
-// output row, at most 65535 (the grid's y extent); for the depthwise
-// kernel, up to kDwChunks workgroups of one chunk each.
+// Chunks that fill the chip: the MFMA route's own count; else about 256 K
+// stage-1 threads (one per weight element, or per 4 x 8 tile on the tiled
+// route), at most one chunk per output row, at most 65535 (the grid's y
+// extent); for the depthwise kernel, up to kDwChunks workgroups of one
+// chunk each.
 int ideal_chunks(const Problem &p)
 {
     if (dw_ok(p)) {   // the depthwise kernel: up to kDwChunks workgroups, one chunk each
@@ -417,6 +423,7 @@ int ideal_chunks(const Problem &p)
         const long long m = ((long long)p.N * p.Do * p.Ho * p.Wo + slots - 1) / slots;
         return (int)(m < kDwChunks ? (m < 1 ? 1 : m) : kDwChunks);
     }
+    if (bwdw_mfma::supported(p)) return bwdw_mfma::chunks(p);
     const long long welems = (long long)p.G * p.Kpg * p.taps() * p.Cpg;
     const long long rows = (long long)p.N * p.Do * p.Ho;
     const long long threads = tile_ok(p) ? welems / 32 : welems;   // stage-1 threads per chunk
@@ -426,20 +433,33 @@ int ideal_chunks(const Problem &p)
     return n < 1 ? 1 : (int)n;
 }
 
-hipError_t launch(const Problem &p, const void *x, const void *dy, void *dw, float *ws, int nch, hipStream_t s)
+hipError_t stage1(const Problem &p, const void *x, const void *dy, float *ws, void *dw, int nch, int *used,
+                  hipStream_t s)
 {
-    const bool vec_ok = ((uintptr_t)x & 15) == 0 && ((uintptr_t)dy & 15) == 0;
+    if (nch < 1) nch = 1;
+    const bool vec_ok = vec_aligned(x, dy);
     if (dw_ok(p) && vec_ok) {
         switch (p.dtype) {
-        case GCONV_F32: return go_dw<float>(p, x, dy, dw, ws, nch, s);
-        case GCONV_F16: return go_dw<_Float16>(p, x, dy, dw, ws, nch, s);
-        default: return go_dw<__bf16>(p, x, dy, dw, ws, nch, s);
+        case GCONV_F32: return go_dw<float>(p, x, dy, dw, ws, nch, used, s);
+        case GCONV_F16: return go_dw<_Float16>(p, x, dy, dw, ws, nch, used, s);
+        default: return go_dw<__bf16>(p, x, dy, dw, ws, nch, used, s);
         }
     }
+    if (vec_ok && bwdw_mfma::supported(p)) return bwdw_mfma::stage1(p, x, dy, ws, dw, nch, used, s);
     switch (p.dtype) {
-    case GCONV_F32: return go<float>(p, x, dy, dw, ws, nch, s);
-    case GCONV_F16: return go<_Float16>(p, x, dy, dw, ws, nch, s);
-    default: return go<__bf16>(p, x, dy, dw, ws, nch, s);
+    case GCONV_F32: return go<float>(p, x, dy, dw, ws, nch, used, s);
+    case GCONV_F16: return go<_Float16>(p, x, dy, dw, ws, nch, used, s);
+    default: return go<__bf16>(p, x, dy, dw, ws, nch, used, s);
+    }
+}
+
+hipError_t stage2(const Problem &p, const float *ws, void *dw, int nch, hipStream_t s)
+{
+    const int welems = p.G * p.Kpg * p.taps() * p.Cpg;
+    switch (p.dtype) {
+    case GCONV_F32: return reduce<float>(ws, (float *)dw, welems, nch, s);
+    case GCONV_F16: return reduce<_Float16>(ws, (_Float16 *)dw, welems, nch, s);
+    default: return reduce<__bf16>(ws, (__bf16 *)dw, welems, nch, s);
     }
 }
 

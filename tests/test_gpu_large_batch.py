@@ -69,3 +69,31 @@ def test_bwd_data_large_batch():
                                     (1, 1), (1, 1), (1, 1))
         return r[0], s[0]
     _sample_check(dx, ref, [0, 30, 31, 32], "bwd_data")
+
+
+def test_bwd_weight_large_batch_accumulates_every_launch():
+    """Backward weight on a batch split into launches (15 + 15 + 3 images):
+    every launch's partial sums enter the one reduction exactly once.
+    Images alternate between two seeded patterns A and B, so the result is
+    17 dw(A) + 16 dw(B), each term from the oracle on one image."""
+    gen = torch.Generator(device="cuda").manual_seed(13)
+    # N(0, 1/16^2) inputs keep sums over 33 M pixels inside fp16's range
+    xa, xb = ((torch.randn((1, HW, HW, C), device="cuda", generator=gen) / 16).to(torch.float16) for _ in range(2))
+    da, db = ((torch.randn((1, HW, HW, C), device="cuda", generator=gen) / 16).to(torch.float16) for _ in range(2))
+    x = torch.cat([xa if n % 2 == 0 else xb for n in range(N)]).contiguous()
+    dy = torch.cat([da if n % 2 == 0 else db for n in range(N)]).contiguous()
+    assert x.numel() >= 1 << 31
+    dw = G.conv_bwd_weight(x, dy, C, (3, 3), (1, 1), (1, 1), (1, 1))
+    torch.cuda.synchronize()
+    got = dw.to("cpu", torch.float64).numpy()
+    del x, dy
+
+    def one(xi, di):
+        return oracle.conv_bwd_weight(xi.to("cpu", torch.float64).numpy(), di.to("cpu", torch.float64).numpy(),
+                                      C, (3, 3), (1, 1), (1, 1), (1, 1))
+    ra, sa = one(xa, da)
+    rb, sb = one(xb, db)
+    r = U.check(got, 17 * ra + 16 * rb, 17 * sa + 16 * sb, "f16", "bwd_weight split batch")
+    # one launch dropped or counted twice moves every element by a whole image's share
+    assert np.abs(got - (17 * ra + 15 * rb)).max() > 0.1
+    print("bwd_weight over 3 launches: max err/tol %.3f" % r)

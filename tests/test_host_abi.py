@@ -245,10 +245,11 @@ def test_bwd_weight_workspace_and_validation():
     # one thread per weight element (fp32): weights that alone fill the chip need no partial sums
     big = G.make_desc(2, "f32", 64, 8, 1024, 1024, (14, 14), (3, 3), (1, 1), (1, 1), (1, 1))
     assert G.gconv_bwd_weight_workspace(big) == 0
-    # the 4 x 8 tiled route (bf16, Cpg % 8 == 0, Kpg % 4 == 0) has 32x fewer threads: it chunks
+    # the matrix-core route (bf16, 128-channel groups): a few chunks of partial sums per weight
     tiled = G.make_desc(2, "bf16", 64, 8, 1024, 1024, (14, 14), (3, 3), (1, 1), (1, 1), (1, 1))
     wbytes = 1024 * 9 * 128 * 4
-    assert G.gconv_bwd_weight_workspace(tiled) == 8 * wbytes
+    n = G.gconv_bwd_weight_workspace(tiled)
+    assert n % wbytes == 0 and 2 <= n // wbytes <= 64
     bad = G.make_desc(2, "f16", 1, 3, 8, 9, (9, 9), (3, 3), (1, 1), (1, 1), (1, 1))   # C % G != 0
     with pytest.raises(G.GconvError):
         G.gconv_bwd_weight_workspace(bad)
@@ -267,8 +268,12 @@ def test_large_batch_splits_into_whole_image_launches():
     assert plan == G.gconv_get_plan(small)        # (2^31 - 1) // 2^27 bytes = 15 images per launch
     fifteen = G.make_desc(2, "f16", 15, 64, 64, 64, (1024, 1024), (3, 3), (1, 1), (1, 1), (1, 1))
     assert plan == G.gconv_get_plan(fifteen)
-    # backward weight reduces over the whole batch: no split
+    # backward weight reduces over the whole batch: a split batch needs a
+    # chunk of partial sums per launch in the workspace
     assert G.gconv_bwd_weight(d, 16, 16, 16, None, 0) == G.GCONV_ERR_TOO_LARGE
+    need = G.gconv_bwd_weight_workspace(d)
+    assert need >= 3 * 64 * 9 * 4     # three launches (15 + 15 + 3 images), depthwise weights
+    assert G.gconv_bwd_weight(d, 16, 16, 16, 32, 64 * 9 * 4 * 2) == G.GCONV_ERR_TOO_LARGE
 
 
 # ---- the header as a plain C / C++ consumer sees it ------------------------
