@@ -33,11 +33,15 @@
 // workgroup's input channels) are loaded into LDS, double-buffered: the next
 // step's loads are in flight while this step's MFMAs run.  Every tap reads
 // the same box at a shifted pixel offset, so x crosses into LDS once per
-// step, not once per tap.  Wave (wk, wc) of the workgroup owns KW output
-// tiles of 16 channels x all taps x one input tile of 16 channels; a
-// workgroup owns a chunk of consecutive steps and writes its partial sums
-// once: [chunk][g][k][t][c] in the fp32 workspace, or dw itself, rounded
-// once, when there is a single chunk.
+// step, not once per tap.  Wave (sg, wk, wc) of the workgroup owns, in its
+// super-group sg, KW output tiles of 16 channels x all taps x one input
+// tile of 16 channels; a workgroup whose tiles cover whole super-groups
+// takes SG consecutive ones, so its loads read longer channel runs.  Pixel
+// rows of 128 bytes or more in LDS get one 16-byte pad slot, which spreads
+// the four pixels of a transposing read over distinct banks.  A workgroup
+// owns a chunk of consecutive steps and writes its partial sums once:
+// [chunk][g][k][t][c] in the fp32 workspace, or dw itself, rounded once,
+// when there is a single chunk.
 #include "device_common.h"
 #include "gconv_internal.h"
 #include "smallg_common.h"
@@ -53,10 +57,13 @@ using smallg::Mfma;
 using smallg::rsrc_t;
 
 constexpr unsigned kOob = 0x80000000u;   // a buffer offset past any tensor: loads zero
-constexpr int kMaxBoxIns = 12;           // box DMA instructions per wave and step
-constexpr int kMaxDyIns = 4;             // dy-tile DMA instructions per wave and step
-constexpr int kMaxLds = 64 * 1024;       // both buffers
+constexpr int kMaxBoxIns = 16;           // box DMA instructions per wave and step
+constexpr int kMaxDyIns = 8;             // dy-tile DMA instructions per wave and step
+constexpr int kMaxLds = 80 * 1024;       // both buffers: two workgroups per CU
 constexpr int kTargetWaves = 8192;       // about eight waves per CU, two rounds
+// chunks are also capped so that stage 2 (which reads every chunk's partial
+// sums) moves at most kStage2Share x the bytes of x and dy
+constexpr double kStage2Share = 1.0;
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
@@ -70,12 +77,16 @@ struct Params {
     int BH, BW, BP;          // input box rows, columns, pixels (all planes)
     int nrb, nwb;            // row and column blocks per output plane
     int nkb, ncb;            // output- and input-channel blocks per super-group
+    int WK, WC, SG;          // waves along output tiles, along input tiles, super-groups per workgroup
+    int SPB, SPD;            // 16-byte slots per box pixel / dy-tile pixel (a pad slot included)
+    int CB, CD;              // channels per box pixel / dy-tile pixel (the workgroup's)
     int steps, spc;          // steps in all, steps per chunk
     int box_ins, dy_ins;     // DMA instructions per step (whole workgroup)
     unsigned box_bytes, buf_bytes;
     unsigned x_bytes, dy_bytes;
     int welems;
     float rbhw, rbw;         // 1 / (BH BW), 1 / BW
+    float rspb, rspd;        // 1 / SPB, 1 / SPD
 };
 
 // n / d for 0 <= n < 2^22 from a float reciprocal of d (off by at most one
@@ -104,16 +115,14 @@ __device__ __forceinline__ typename Mfma<T>::V operand(v4s lo, v4s hi)
     return __builtin_bit_cast(typename Mfma<T>::V, pair);
 }
 
-template <typename T, int KW, int WK, int WC, int TAPS>
-__global__ __launch_bounds__(64 * WK * WC) void kernel(Params q, const T *__restrict__ x,
+template <typename T, int KW, int TAPS>
+__global__ __launch_bounds__(256) void kernel(Params q, const T *__restrict__ x,
                                                         const T *__restrict__ dy, float *__restrict__ ws,
                                                         T *__restrict__ dwout)
 {
-    constexpr int NW = WK * WC;
-    constexpr int SPB = 2 * WC;             // 16-byte slots per box pixel
-    constexpr int SPD = 2 * KW * WK;        // 16-byte slots per dy-tile pixel
-    constexpr int PS = 16 * SPB;            // box pixel stride, bytes
-    constexpr int PD = 16 * SPD;            // dy-tile pixel stride, bytes
+    const int NW = q.WK * q.WC * q.SG;
+    const int PS = 16 * q.SPB;              // box pixel stride, bytes
+    const int PD = 16 * q.SPD;              // dy-tile pixel stride, bytes
     constexpr int NKC = 4;                  // at most 4 x 32 pixels per step
     typedef typename Mfma<T>::V V;
     extern __shared__ uint4 lds[];
@@ -122,7 +131,7 @@ __global__ __launch_bounds__(64 * WK * WC) void kernel(Params q, const T *__rest
 
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int lane = (int)threadIdx.x & 63;
-    const int wk = wave % WK, wc = wave / WK;
+    const int wc = wave % q.WC, wk = (wave / q.WC) % q.WK, sg = wave / (q.WC * q.WK);
     const int s16 = lane & 15, qg = lane >> 4;
 
     int tile = (int)blockIdx.x;
@@ -130,22 +139,23 @@ __global__ __launch_bounds__(64 * WK * WC) void kernel(Params q, const T *__rest
     const int kbk = tile % q.nkb;
     const int gq = tile / q.nkb;
     const int chunk = (int)blockIdx.y;
-    const int c0 = cbk * 16 * WC;                 // first input channel of the block (in the super-group)
-    const int k0 = kbk * 16 * KW * WK;            // first output channel of the block
+    const int c0 = cbk * 16 * q.WC;               // first input channel of the block (in the super-group)
+    const int k0 = kbk * 16 * KW * q.WK;          // first output channel of the block
     const int st0 = chunk * q.spc;
     const int st1 = st0 + q.spc < q.steps ? st0 + q.spc : q.steps;
 
     // ---- step-invariant DMA plans.  Box slot L (16 bytes) = pixel L / SPB,
-    //      channel chunk L % SPB; dy-tile slot L = pixel L / SPD, chunk L % SPD.
+    //      channel chunk L % SPB (the pad slot, if any, loads zeros); dy-tile
+    //      slot L = pixel L / SPD, chunk L % SPD.
     unsigned bplan[kMaxBoxIns];   // bz << 24 | by << 12 | bx, with the chunk in the top bits; ~0: dead
     unsigned dplan[kMaxDyIns];    // r << 16 | c << 4 | chunk; ~0: dead
 #pragma unroll
     for (int m = 0; m < kMaxBoxIns; ++m) {
         const int ins = wave + NW * m;
         const int L = ins * 64 + lane;
-        const int P = L / SPB, j = L % SPB;
+        const int P = fdivr(L, q.SPB, q.rspb), j = L - P * q.SPB;
         bplan[m] = ~0u;
-        if (ins < q.box_ins && P < q.BP) {
+        if (ins < q.box_ins && P < q.BP && j * 8 < q.CB) {
             const int bz = fdivr(P, q.BH * q.BW, q.rbhw);
             const int rem = P - bz * q.BH * q.BW;
             const int by = fdivr(rem, q.BW, q.rbw), bx = rem - by * q.BW;
@@ -156,9 +166,9 @@ __global__ __launch_bounds__(64 * WK * WC) void kernel(Params q, const T *__rest
     for (int m = 0; m < kMaxDyIns; ++m) {
         const int ins = wave + NW * m;
         const int L = ins * 64 + lane;
-        const int pix = L / SPD, j = L % SPD;
+        const int pix = fdivr(L, q.SPD, q.rspd), j = L - pix * q.SPD;
         dplan[m] = ~0u;
-        if (ins < q.dy_ins && pix < q.SR * q.SC) {
+        if (ins < q.dy_ins && pix < q.SR * q.SC && j * 8 < q.CD) {
             const int r = pix / q.SC, c = pix - (pix / q.SC) * q.SC;
             dplan[m] = ((unsigned)r << 16) | ((unsigned)c << 4) | (unsigned)j;
         }
@@ -167,8 +177,8 @@ __global__ __launch_bounds__(64 * WK * WC) void kernel(Params q, const T *__rest
     const int ndy = (q.dy_ins - wave + NW - 1) / NW;
     const rsrc_t rx = make_rsrc(x, q.x_bytes);
     const rsrc_t rd = make_rsrc(dy, q.dy_bytes);
-    const unsigned cx = (unsigned)(gq * q.Cq + c0);   // first x channel of the block
-    const unsigned cy = (unsigned)(gq * q.Kq + k0);   // first dy channel of the block
+    const unsigned cx = (unsigned)(gq * q.SG * q.Cq + c0);   // first x channel of the block
+    const unsigned cy = (unsigned)(gq * q.SG * q.Kq + k0);   // first dy channel of the block
 
     auto issue = [&](int st, int buf) __attribute__((always_inline)) {
         int r = st;
@@ -226,8 +236,9 @@ __global__ __launch_bounds__(64 * WK * WC) void kernel(Params q, const T *__rest
             aoff[kc][h] = (unsigned)pix * PD;
             boff[kc][h] = (unsigned)((r * q.sh) * q.BW + c * q.sw) * PS;
         }
-    const unsigned a_ch = (unsigned)(4 * (s16 & 3)) * 2u;              // channel offset within a tile
-    const unsigned b_ch = (unsigned)(16 * wc + 4 * (s16 & 3)) * 2u;
+    // this wave's channels within a box / dy-tile pixel
+    const unsigned a_ch = (unsigned)(sg * 16 * KW * q.WK + 4 * (s16 & 3)) * 2u;
+    const unsigned b_ch = (unsigned)(sg * 16 * q.WC + 16 * wc + 4 * (s16 & 3)) * 2u;
     int tofs[TAPS];   // box byte offset of each tap
 #pragma unroll
     for (int t = 0; t < TAPS; ++t) {
@@ -260,7 +271,7 @@ __global__ __launch_bounds__(64 * WK * WC) void kernel(Params q, const T *__rest
                 V af[KW];
 #pragma unroll
                 for (int a = 0; a < KW; ++a) {
-                    const unsigned ch = (unsigned)(16 * (wk * KW + a)) * 2u + a_ch;
+                    const unsigned ch = (unsigned)(16 * (wk * KW + a)) * 2u + a_ch;   // sg's tile wk * KW + a
                     af[a] = operand<T>(tr_read(lds_c, db + aoff[kc][0] + ch), tr_read(lds_c, db + aoff[kc][1] + ch));
                 }
 #pragma unroll
@@ -278,7 +289,7 @@ __global__ __launch_bounds__(64 * WK * WC) void kernel(Params q, const T *__rest
 
     // ---- results: lane holds rows 4 qg + i (output channels) of column s16
     //      (input channel) of each 16 x 16 tile; only a group's own block counts
-    const int cq = c0 + 16 * wc + s16;            // input channel in the super-group
+    const int cq = c0 + 16 * wc + s16;            // input channel in super-group gq * SG + sg
     const int gc = cq / q.Cpg, c = cq - gc * q.Cpg;
 #pragma unroll
     for (int a = 0; a < KW; ++a)
@@ -287,7 +298,7 @@ __global__ __launch_bounds__(64 * WK * WC) void kernel(Params q, const T *__rest
             const int kq = k0 + 16 * (wk * KW + a) + 4 * qg + i;
             const int gk = kq / q.Kpg, k = kq - gk * q.Kpg;
             if (gk != gc) continue;
-            const int g = gq * q.GN + gk;
+            const int g = (gq * q.SG + sg) * q.GN + gk;
             const size_t fb = ((size_t)(g * q.Kpg + k) * q.taps) * q.Cpg + c;
 #pragma unroll
             for (int t = 0; t < TAPS; ++t) {
@@ -301,7 +312,7 @@ __global__ __launch_bounds__(64 * WK * WC) void kernel(Params q, const T *__rest
 // ----------------------------------------------------------------- host side
 
 struct Config {
-    int GN, KW, WK, WC, taps;
+    int GN, KW, WK, WC, SG, taps;
     Params q;
     int tiles, nch, threads, lds;
 };
@@ -338,26 +349,56 @@ bool configure(const Problem &p, Config &c)
     q.dd = p.dd; q.dh = p.dh; q.dw = p.dw;
     q.Y = p.Y; q.X = p.X; q.taps = taps;
     q.Cpg = p.Cpg; q.Kpg = p.Kpg; q.GN = c.GN; q.Kq = Kq; q.Cq = Cq;
-    // step: SC columns (the whole row when it has <= 64) x SR rows, SR
-    // chosen for the best use of the 32-pixel MFMA slices over the rows'
-    // blocks (the larger SR on a tie: fewer halo rows per pixel)
+    // Layout search: super-groups per workgroup (a workgroup whose tiles
+    // cover whole super-groups takes up to four waves' worth of them; more
+    // is preferred: longer channel runs per load), then the step rows SR for
+    // the best use of the 32-pixel MFMA slices over the rows' blocks (the
+    // larger SR on a tie: fewer halo rows per pixel), within the LDS and
+    // DMA-instruction budgets.  SC is the whole row when it has <= 64 columns.
     q.SC = p.Wo <= 64 ? p.Wo : 32;
-    q.SR = 1;
-    double best = -1.0;
-    for (int sr = 1; sr * q.SC <= 128 && sr <= p.Ho; ++sr) {
-        const int nrb = (p.Ho + sr - 1) / sr;
-        const double use = (double)p.Ho * q.SC / ((double)nrb * ((sr * q.SC + 31) / 32 * 32));
-        if (use >= best - 1e-9) {
-            best = use;
-            q.SR = sr;
-        }
-    }
-    q.SP = (q.SR * q.SC + 31) / 32 * 32;
     const long long BD = (long long)(p.Z - 1) * p.dd + 1;
-    const long long BH = (long long)(q.SR - 1) * p.sh + (long long)(p.Y - 1) * p.dh + 1;
     const long long BW = (long long)(q.SC - 1) * p.sw + (long long)(p.X - 1) * p.dw + 1;
-    if (BD >= 32 || BH >= 4096 || BW >= 4096) return false;
-    q.BH = (int)BH; q.BW = (int)BW; q.BP = (int)(BD * BH * BW);
+    if (BD >= 32 || BW >= 4096) return false;
+    bool found = false;
+    for (int sgn : {4, 2, 1}) {
+        if (sgn > 1 && !(kgroups == c.WK && CTn == c.WC && sgn * c.WK * c.WC <= 4 && (p.G / c.GN) % sgn == 0))
+            continue;
+        const int NW = c.WK * c.WC * sgn;
+        const int CB = 16 * c.WC * sgn, CD = 16 * c.KW * c.WK * sgn;
+        const int SPB = CB / 8 + (CB / 8 % 8 == 0 ? 1 : 0);
+        const int SPD = CD / 8 + (CD / 8 % 8 == 0 ? 1 : 0);
+        double best = -1.0;
+        for (int sr = 1; sr * q.SC <= 128 && sr <= p.Ho; ++sr) {
+            const long long BH = (long long)(sr - 1) * p.sh + (long long)(p.Y - 1) * p.dh + 1;
+            if (BH >= 4096) break;
+            const int SP = (sr * q.SC + 31) / 32 * 32;
+            const long long box_ins = (BD * BH * BW * SPB + 63) / 64;
+            const long long dy_ins = ((long long)SP * SPD + 63) / 64;
+            if (box_ins > kMaxBoxIns * NW || dy_ins > kMaxDyIns * NW) continue;
+            if (2 * (box_ins + dy_ins) * 1024 > kMaxLds) continue;   // at least two buffers
+            const int nrb = (p.Ho + sr - 1) / sr;
+            const double use = (double)p.Ho * q.SC / ((double)nrb * SP);
+            if (use >= best - 1e-9) {
+                best = use;
+                found = true;
+                c.SG = sgn;
+                q.SR = sr;
+                q.SP = SP;
+                q.BH = (int)BH;
+                q.SPB = SPB; q.SPD = SPD; q.CB = CB; q.CD = CD;
+                q.box_ins = (int)box_ins;
+                q.dy_ins = (int)dy_ins;
+            }
+        }
+        if (found) break;
+    }
+    if (!found) return false;
+    q.WK = c.WK; q.WC = c.WC; q.SG = c.SG;
+    q.rspb = 1.0f / (float)q.SPB;
+    q.rspd = 1.0f / (float)q.SPD;
+    q.BW = (int)BW;
+    q.BP = (int)(BD * q.BH * BW);
+    const long long BH = q.BH;
     q.nrb = (p.Ho + q.SR - 1) / q.SR;
     q.nwb = (p.Wo + q.SC - 1) / q.SC;
     q.nkb = kgroups / c.WK;
@@ -365,15 +406,10 @@ bool configure(const Problem &p, Config &c)
     const long long steps = (long long)p.N * p.Do * q.nrb * q.nwb;
     if (steps >= (1LL << 30)) return false;
     q.steps = (int)steps;
-    const int NW = c.WK * c.WC;
-    const long long box_slots = (long long)q.BP * 2 * c.WC;
-    q.box_ins = (int)((box_slots + 63) / 64);
-    q.dy_ins = (q.SP * 2 * c.KW * c.WK + 63) / 64;
-    if (q.box_ins > kMaxBoxIns * NW || q.dy_ins > kMaxDyIns * NW) return false;
+    const int NW = c.WK * c.WC * c.SG;
     q.box_bytes = (unsigned)q.box_ins * 1024u;
     q.buf_bytes = q.box_bytes + (unsigned)q.dy_ins * 1024u;
     c.lds = 2 * (int)q.buf_bytes;
-    if (c.lds > kMaxLds) return false;
     const long long xb = (long long)p.N * p.D * p.H * p.W * p.C() * 2;
     const long long yb = (long long)p.N * p.Do * p.Ho * p.Wo * p.K() * 2;
     if (xb >= (1LL << 31) || yb >= (1LL << 31)) return false;
@@ -382,12 +418,14 @@ bool configure(const Problem &p, Config &c)
     q.welems = p.G * p.Kpg * taps * p.Cpg;
     q.rbhw = 1.0f / (float)(BH * BW);
     q.rbw = 1.0f / (float)BW;
-    c.tiles = (p.G / c.GN) * q.nkb * q.ncb;
+    c.tiles = (p.G / c.GN / c.SG) * q.nkb * q.ncb;
     c.threads = 64 * NW;
     // chunks: enough workgroups for about kTargetWaves waves, each chunk at
     // least two steps (the loads of one overlap the MFMAs of the other)
     long long want = ((long long)kTargetWaves / NW + c.tiles - 1) / c.tiles;
     if (want > (steps + 1) / 2) want = (steps + 1) / 2;
+    const double s2cap = kStage2Share * (double)(xb + yb) / ((double)q.welems * 4.0);
+    if (want > (long long)s2cap) want = (long long)s2cap;
     if (want > 65535) want = 65535;
     if (want < 1) want = 1;
     q.spc = (int)((steps + want - 1) / want);
@@ -395,8 +433,8 @@ bool configure(const Problem &p, Config &c)
     return true;
 }
 
-template <typename T, int KW, int WK, int WC, int TAPS>
-hipError_t go5(const Config &c, const void *x, const void *dy, float *ws, void *dw, int nch, int *used,
+template <typename T, int KW, int TAPS>
+hipError_t go3(const Config &c, const void *x, const void *dy, float *ws, void *dw, int nch, int *used,
                hipStream_t s)
 {
     Params q = c.q;
@@ -404,45 +442,30 @@ hipError_t go5(const Config &c, const void *x, const void *dy, float *ws, void *
     q.spc = (q.steps + nch - 1) / nch;
     const int n = (q.steps + q.spc - 1) / q.spc;
     *used = n;
-    Args a{};
-    return enqueue(kernel<T, KW, WK, WC, TAPS>, dim3((unsigned)c.tiles, (unsigned)n), dim3(64 * WK * WC),
-                   (unsigned)c.lds, s, a, q, (const T *)x, (const T *)dy, ws, (T *)dw);
-}
-
-template <typename T, int KW, int WK, int WC>
-hipError_t go4(const Config &c, const void *x, const void *dy, float *ws, void *dw, int nch, int *used,
-               hipStream_t s)
-{
-    switch (c.taps) {
-    case 1: return go5<T, KW, WK, WC, 1>(c, x, dy, ws, dw, nch, used, s);
-    case 9: return go5<T, KW, WK, WC, 9>(c, x, dy, ws, dw, nch, used, s);
-    default:
-        // two output tiles per wave only for windows of up to 9 taps
-        if constexpr (KW == 1) {
-            if (c.taps == 25) return go5<T, KW, WK, WC, 25>(c, x, dy, ws, dw, nch, used, s);
-            return go5<T, KW, WK, WC, 27>(c, x, dy, ws, dw, nch, used, s);
-        }
-        return hipErrorInvalidValue;
+    static std::atomic<unsigned long long> lds_set{0};
+    if (c.lds > 64 * 1024) {
+        const hipError_t e = allow_lds((const void *)kernel<T, KW, TAPS>, lds_set, kMaxLds);
+        if (e != hipSuccess) return e;
     }
+    Args a{};
+    return enqueue(kernel<T, KW, TAPS>, dim3((unsigned)c.tiles, (unsigned)n), dim3((unsigned)c.threads),
+                   (unsigned)c.lds, s, a, q, (const T *)x, (const T *)dy, ws, (T *)dw);
 }
 
 template <typename T>
 hipError_t go(const Config &c, const void *x, const void *dy, float *ws, void *dw, int nch, int *used,
               hipStream_t s)
 {
-    // (KW, WK, WC) as configure() picks them
-    const int key = c.KW * 100 + c.WK * 10 + c.WC;
-    switch (key) {
-    case 222: return go4<T, 2, 2, 2>(c, x, dy, ws, dw, nch, used, s);
-    case 212: return go4<T, 2, 1, 2>(c, x, dy, ws, dw, nch, used, s);
-    case 241: return go4<T, 2, 4, 1>(c, x, dy, ws, dw, nch, used, s);
-    case 221: return go4<T, 2, 2, 1>(c, x, dy, ws, dw, nch, used, s);
-    case 211: return go4<T, 2, 1, 1>(c, x, dy, ws, dw, nch, used, s);
-    case 122: return go4<T, 1, 2, 2>(c, x, dy, ws, dw, nch, used, s);
-    case 112: return go4<T, 1, 1, 2>(c, x, dy, ws, dw, nch, used, s);
-    case 141: return go4<T, 1, 4, 1>(c, x, dy, ws, dw, nch, used, s);
-    case 121: return go4<T, 1, 2, 1>(c, x, dy, ws, dw, nch, used, s);
-    default: return go4<T, 1, 1, 1>(c, x, dy, ws, dw, nch, used, s);
+    // two output tiles per wave only for windows of up to 9 taps
+    if (c.KW == 2) {
+        if (c.taps == 1) return go3<T, 2, 1>(c, x, dy, ws, dw, nch, used, s);
+        return go3<T, 2, 9>(c, x, dy, ws, dw, nch, used, s);
+    }
+    switch (c.taps) {
+    case 1: return go3<T, 1, 1>(c, x, dy, ws, dw, nch, used, s);
+    case 9: return go3<T, 1, 9>(c, x, dy, ws, dw, nch, used, s);
+    case 25: return go3<T, 1, 25>(c, x, dy, ws, dw, nch, used, s);
+    default: return go3<T, 1, 27>(c, x, dy, ws, dw, nch, used, s);
     }
 }
 
