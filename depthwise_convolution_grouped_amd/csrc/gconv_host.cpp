@@ -12,6 +12,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "gconv_internal.h"
 
 #define GCONV_API extern "C" __attribute__((visibility("default")))
@@ -517,6 +519,32 @@ int run_bwd_weight(const gconv_desc *d, const void *x, const void *dy, void *dw,
     return GCONV_OK;
 }
 
+// ---- the entry point that allocates nothing
+//
+// Its partial sums live in a file-scope device array, one copy per GPU,
+// allocated when the library's code object is loaded and held until the
+// process ends.  Host code must not pass the array's name to a kernel (in
+// host code it is a stand-in, not a device address): each device's address
+// comes from hipGetSymbolAddress, taken once per device with that device
+// current, and kept here.
+constexpr size_t kScratchBytes = GCONV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+// The scratch array's address on the current device (nullptr on failure).
+void *scratch_ptr()
+{
+    constexpr int kMaxDevices = 64;
+    static std::atomic<void *> ptrs[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void *p = ptrs[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    void *q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+    ptrs[dev].store(q, std::memory_order_release);   // a racing caller stores the same address
+    return q;
+}
+
 }  // namespace
 }  // namespace gconv
 
@@ -643,6 +671,23 @@ GCONV_API int gconv_bwd_weight(const gconv_desc *d, const void *x, const void *d
     return run_bwd_weight(d, x, dy, dw, workspace, workspace_bytes, stream);
 }
 
+GCONV_API int gconv_bwd_weight_noalloc(const gconv_desc *d, const void *x, const void *dy, void *dw,
+                                       void *stream)
+{
+    int64_t out[3];
+    int rc = check_desc(d, out);
+    if (rc != GCONV_OK) return rc;
+    if (!x || !dy || !dw) return GCONV_ERR_NULL_PTR;
+    // the sizes are checked against the fixed scratch before any HIP call
+    BwdwPlan pl;
+    rc = bwdw_plan(d, out, kScratchBytes, true, pl);
+    if (rc == GCONV_ERR_TOO_LARGE && images_per_launch(d, out) >= 1) return GCONV_ERR_SCRATCH;
+    if (rc != GCONV_OK) return rc;
+    void *ws = scratch_ptr();
+    if (!ws) return GCONV_ERR_LAUNCH;
+    return run_bwd_weight(d, x, dy, dw, ws, kScratchBytes, stream);
+}
+
 GCONV_API const char *gconv_status_str(int status)
 {
     switch (status) {
@@ -655,6 +700,7 @@ GCONV_API const char *gconv_status_str(int status)
     case GCONV_ERR_BAD_PATH: return "unknown path";
     case GCONV_ERR_PATH_UNSUPPORTED: return "path cannot run this problem";
     case GCONV_ERR_LAUNCH: return "kernel launch failed";
+    case GCONV_ERR_SCRATCH: return "needs more than the fixed device scratch of the no-allocation entry point";
     default: return "unknown status";
     }
 }

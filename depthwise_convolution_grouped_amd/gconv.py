@@ -33,6 +33,8 @@ GCONV_ERR_MISALIGNED = -5
 GCONV_ERR_BAD_PATH = -6
 GCONV_ERR_PATH_UNSUPPORTED = -7
 GCONV_ERR_LAUNCH = -8
+GCONV_ERR_SCRATCH = -9
+GCONV_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 GCONV_PATH_AUTO = -1
 GCONV_PATH_GENERIC = 0
@@ -46,7 +48,7 @@ PATHS = {"generic": 0, "depthwise": 1, "smallg_mfma": 2, "igemm_mfma": 3, "ighal
 EXPORTS = ("gconv_validate", "gconv_out_dims", "gconv_select_path", "gconv_path_supported",
            "gconv_get_plan", "gconv_fwd", "gconv_fwd_path", "gconv_fwd_timed",
            "gconv_bwd_data_workspace", "gconv_bwd_data", "gconv_bwd_data_direct",
-           "gconv_bwd_weight_workspace", "gconv_bwd_weight",
+           "gconv_bwd_weight_workspace", "gconv_bwd_weight", "gconv_bwd_weight_noalloc",
            "gconv_status_str", "gconv_path_name", "gconv_abi_version")
 
 
@@ -107,6 +109,7 @@ def lib():
     L.gconv_bwd_data_direct.argtypes = [pd, vp, vp, vp, vp]
     L.gconv_bwd_weight_workspace.argtypes = [pd, ctypes.POINTER(ctypes.c_size_t)]
     L.gconv_bwd_weight.argtypes = [pd, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.gconv_bwd_weight_noalloc.argtypes = [pd, vp, vp, vp, vp]
     L.gconv_status_str.argtypes = [ctypes.c_int]
     L.gconv_status_str.restype = ctypes.c_char_p
     L.gconv_path_name.argtypes = [ctypes.c_int]
@@ -115,7 +118,7 @@ def lib():
     for name in ("gconv_validate", "gconv_out_dims", "gconv_select_path", "gconv_path_supported",
                  "gconv_get_plan", "gconv_fwd", "gconv_fwd_path", "gconv_fwd_timed",
                  "gconv_bwd_data_workspace", "gconv_bwd_data", "gconv_bwd_data_direct",
-                 "gconv_bwd_weight_workspace", "gconv_bwd_weight", "gconv_abi_version"):
+                 "gconv_bwd_weight_workspace", "gconv_bwd_weight", "gconv_bwd_weight_noalloc", "gconv_abi_version"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -228,6 +231,12 @@ def gconv_bwd_weight(d: gconv_desc, x: int, dy: int, dw: int, workspace: Optiona
     """Raw call with device addresses (ints); returns the status code."""
     return lib().gconv_bwd_weight(ctypes.byref(d), x, dy, dw, workspace or None, int(workspace_bytes),
                                   stream or None)
+
+
+def gconv_bwd_weight_noalloc(d: gconv_desc, x: int, dy: int, dw: int, stream: int = 0) -> int:
+    """Raw call with device addresses (ints); the library's own device scratch
+    holds the partial sums.  Returns the status code."""
+    return lib().gconv_bwd_weight_noalloc(ctypes.byref(d), x, dy, dw, stream or None)
 
 
 def gconv_status_str(status: int) -> str:

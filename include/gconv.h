@@ -88,7 +88,9 @@ typedef enum gconv_status {
     GCONV_ERR_MISALIGNED = -5,      /* a pointer is not aligned as the path needs */
     GCONV_ERR_BAD_PATH = -6,        /* unknown path id */
     GCONV_ERR_PATH_UNSUPPORTED = -7,/* forced path cannot run this problem */
-    GCONV_ERR_LAUNCH = -8           /* the HIP launch reported an error */
+    GCONV_ERR_LAUNCH = -8,          /* the HIP launch reported an error */
+    GCONV_ERR_SCRATCH = -9          /* gconv_bwd_weight_noalloc: the problem needs more than
+                                       GCONV_NOALLOC_SCRATCH_BYTES of partial sums */
 } gconv_status;
 
 /* Kernel paths.  gconv_fwd picks one from the descriptor. */
@@ -267,6 +269,28 @@ int gconv_bwd_weight_workspace(const gconv_desc *d, size_t *bytes);
  * that size).  Status codes as for gconv_fwd. */
 int gconv_bwd_weight(const gconv_desc *d, const void *x, const void *dy, void *dw,
                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of the device scratch gconv_bwd_weight_noalloc uses (one copy per
+ * GPU, held by the library until the process ends). */
+#define GCONV_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* Backward weight for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): as gconv_bwd_weight with a workspace of
+ * GCONV_NOALLOC_SCRATCH_BYTES, except that the workspace is the library's
+ * own device array on the current GPU instead of the caller's.  It calls no
+ * allocator.  Partial sums are split over as many chunks as the scratch
+ * holds (at most the gconv_bwd_weight_workspace amount), so the result is
+ * bitwise that of gconv_bwd_weight with a workspace of
+ * min(GCONV_NOALLOC_SCRATCH_BYTES, gconv_bwd_weight_workspace) bytes.
+ * Returns GCONV_ERR_SCRATCH, before any HIP call, when a batch that must be
+ * split into launches needs more than the scratch holds (one chunk of
+ * partial sums per launch).  Every call on one GPU uses that GPU's one
+ * scratch array: calls that overlap on the same GPU (other streams or host
+ * threads) race and must be serialised by the caller.  Status codes
+ * otherwise as gconv_bwd_weight. */
+int gconv_bwd_weight_noalloc(const gconv_desc *d, const void *x, const void *dy, void *dw,
+                             void *stream);
 
 /* Static strings; never NULL.  A status string names why a call failed; the
  * CK grouped_conv tile-engine README records a failed launch as a result of
