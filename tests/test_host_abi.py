@@ -382,3 +382,13 @@ def test_image_beyond_one_launch_is_split_into_slices():
     assert G.gconv_select_path(big3) >= 0
     # backward data accepts it as well (dx slices with the dy slices reaching them)
     assert G.gconv_bwd_data_workspace(big) == 64 * 9 * 2
+
+
+def test_noalloc_entry_validates_before_any_hip_call():
+    # a batch split into 5 launches needs 5 x 9.4 MB of partial sums > the 32 MiB scratch
+    d = G.make_desc(2, "bf16", 40, 1, 512, 512, (512, 512), (3, 3), (1, 1), (1, 1), (1, 1))
+    assert G.gconv_bwd_weight_noalloc(d, 256, 256, 256) == G.GCONV_ERR_SCRATCH
+    assert "scratch" in G.gconv_status_str(G.GCONV_ERR_SCRATCH)
+    assert G.gconv_bwd_weight_noalloc(d, 0, 256, 256) == G.GCONV_ERR_NULL_PTR
+    bad = G.make_desc(2, "f16", 1, 3, 8, 9, (9, 9), (3, 3), (1, 1), (1, 1), (1, 1))
+    assert G.gconv_bwd_weight_noalloc(bad, 256, 256, 256) == G.GCONV_ERR_BAD_DESC
