@@ -291,6 +291,7 @@ bool path_ok(const Problem &p, int path)
     case GCONV_PATH_SMALLG: return smallg::supported(p);
     case GCONV_PATH_IGEMM: return igemm::supported(p);
     case GCONV_PATH_IGHALO: return ighalo::supported(p);
+    case GCONV_PATH_DIRECT: return direct::supported(p);
     default: return false;
     }
 }
@@ -299,7 +300,8 @@ bool path_ok(const Problem &p, int path)
 // direct kernel; large per-group contractions (Cpg, Kpg >= 32, half types)
 // are a real GEMM per group and go to the implicit-GEMM MFMA kernel; small
 // groups in half types merge several groups into one block-diagonal MFMA
-// tile; everything else takes the generic kernel.
+// tile; the rest (fp32 grouped above all) takes the register-blocked VALU
+// kernel when there is enough work to fill the chip, else the generic one.
 int select(const Problem &p)
 {
     if (p.pd < 0 || p.ph < 0 || p.pw < 0) return GCONV_PATH_GENERIC;
@@ -311,6 +313,7 @@ int select(const Problem &p)
     if (smallg::supported(p)) return GCONV_PATH_SMALLG;
     if (ighalo::supported(p)) return GCONV_PATH_IGHALO;
     if (igemm::supported(p)) return GCONV_PATH_IGEMM;
+    if (direct::preferred(p)) return GCONV_PATH_DIRECT;
     return GCONV_PATH_GENERIC;
 }
 
@@ -321,6 +324,7 @@ gconv_plan plan_of(const Problem &p, int path)
     case GCONV_PATH_SMALLG: return smallg::plan(p);
     case GCONV_PATH_IGEMM: return igemm::plan(p);
     case GCONV_PATH_IGHALO: return ighalo::plan(p);
+    case GCONV_PATH_DIRECT: return direct::plan(p);
     default: return generic::plan(p);
     }
 }
@@ -348,6 +352,7 @@ int launch_problem(const Problem &p, int path, const Args &a, hipStream_t s)
     case GCONV_PATH_SMALLG: e = smallg::launch(p, a, s); break;
     case GCONV_PATH_IGEMM: e = igemm::launch(p, a, s); break;
     case GCONV_PATH_IGHALO: e = ighalo::launch(p, a, s); break;
+    case GCONV_PATH_DIRECT: e = direct::launch(p, a, s); break;
     default: e = generic::launch(p, a, s); break;
     }
     return e == hipSuccess ? GCONV_OK : GCONV_ERR_LAUNCH;
@@ -714,6 +719,7 @@ GCONV_API const char *gconv_path_name(int path)
     case GCONV_PATH_SMALLG: return "smallg_mfma";
     case GCONV_PATH_IGEMM: return "igemm_mfma";
     case GCONV_PATH_IGHALO: return "ighalo_mfma";
+    case GCONV_PATH_DIRECT: return "direct_valu";
     default: return "unknown";
     }
 }

@@ -90,6 +90,14 @@ bool supported(const Problem &p);
 gconv_plan plan(const Problem &p);
 hipError_t launch(const Problem &p, const Args &a, hipStream_t s);
 }
+// Register-blocked VALU direct kernel (k_direct.hip); `preferred` says
+// whether it beats the generic kernel for the problem (enough work).
+namespace direct {
+bool supported(const Problem &p);
+bool preferred(const Problem &p);
+gconv_plan plan(const Problem &p);
+hipError_t launch(const Problem &p, const Args &a, hipStream_t s);
+}
 // The halo path's variant with the whole input box resident in LDS; the
 // halo path runs it whenever it takes the problem.
 namespace ighalo_box {

@@ -1,0 +1,200 @@
+// Register-blocked direct kernel on the vector ALUs: the path for grouped
+// problems the matrix-core kernels do not take, above all fp32 (the TileOPs
+// PR 1568 review's grouped kernels and the CK tile engine's datatypes
+// include fp32; CK grouped_conv tile-engine README, Hardware).
+//
+// A thread owns KB output channels of one group x PW consecutive output
+// pixels of one output row.  For each tap of the window and each vector of
+// VC input channels of the group it loads the PW input vectors (one per
+// output pixel, shared by its KB channels) and the KB weight vectors (shared
+// by its PW pixels) and does KB x PW x VC fused multiply-adds in fp32, so a
+// 16-byte load feeds up to 32 FMAs.  Consecutive threads take consecutive
+// (channel block, group) pairs of the same pixels: their x loads are
+// neighbouring channel vectors of one pixel and their stores neighbouring
+// runs of its output channels.  Taps outside the input contribute nothing
+// (their loads are skipped).  The epilogue adds the bias, rounds once and
+// stores.
+#include "device_common.h"
+#include "gconv_internal.h"
+
+namespace gconv {
+namespace direct {
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kPW = 4;                  // output pixels per thread along a row
+constexpr long long kMinThreads = 32768;  // below this the generic kernel's split reductions win
+
+template <typename T, int VC> struct VecT;
+template <typename T> struct VecT<T, 1> {
+    static __device__ __forceinline__ void load(const T *p, float (&v)[1]) { v[0] = to_f32(p[0]); }
+};
+template <> struct VecT<float, 4> {
+    static __device__ __forceinline__ void load(const float *p, float (&v)[4])
+    {
+        const float4 q = *reinterpret_cast<const float4 *>(p);
+        v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+    }
+};
+template <typename T> struct VecT<T, 4> {   // fp16 / bf16: 8 bytes
+    static __device__ __forceinline__ void load(const T *p, float (&v)[4])
+    {
+        const uint2 q = *reinterpret_cast<const uint2 *>(p);
+        const T *e = reinterpret_cast<const T *>(&q);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = to_f32(e[i]);
+    }
+};
+
+template <typename T, int KB, int VC>
+__global__ __launch_bounds__(kBlock) void kernel(Problem p, const T *__restrict__ x, const T *__restrict__ w,
+                                                 const T *__restrict__ bias, T *__restrict__ y, int nkb,
+                                                 int nwb, int total)
+{
+    const int tid = blockIdx.x * kBlock + threadIdx.x;
+    if (tid >= total) return;
+    int r = tid;
+    const int kb = r % nkb;   r /= nkb;
+    const int g = r % p.G;    r /= p.G;
+    const int wb = r % nwb;   r /= nwb;
+    const int oh = r % p.Ho;  r /= p.Ho;
+    const int od = r % p.Do;
+    const int n = r / p.Do;
+    const int k0 = kb * KB, ow0 = wb * kPW;
+    const int C = p.G * p.Cpg, K = p.G * p.Kpg, taps = p.Z * p.Y * p.X;
+    float acc[KB][kPW];
+#pragma unroll
+    for (int a = 0; a < KB; ++a)
+#pragma unroll
+        for (int j = 0; j < kPW; ++j) acc[a][j] = 0.f;
+    for (int z = 0; z < p.Z; ++z) {
+        const int id = od * p.sd - p.pd + z * p.dd;
+        if (id < 0 || id >= p.D) continue;
+        for (int yy = 0; yy < p.Y; ++yy) {
+            const int ih = oh * p.sh - p.ph + yy * p.dh;
+            if (ih < 0 || ih >= p.H) continue;
+            const T *xrow = x + ((size_t)((n * p.D + id) * p.H + ih) * p.W) * C + g * p.Cpg;
+            for (int xx = 0; xx < p.X; ++xx) {
+                const int tap = (z * p.Y + yy) * p.X + xx;
+                const T *wt = w + ((size_t)(g * p.Kpg + k0) * taps + tap) * p.Cpg;
+                int iw[kPW];
+                bool ok[kPW];
+#pragma unroll
+                for (int j = 0; j < kPW; ++j) {
+                    iw[j] = (ow0 + j) * p.sw - p.pw + xx * p.dw;
+                    ok[j] = ow0 + j < p.Wo && iw[j] >= 0 && iw[j] < p.W;
+                }
+                for (int c = 0; c < p.Cpg; c += VC) {
+                    float xv[kPW][VC], wv[KB][VC];
+#pragma unroll
+                    for (int j = 0; j < kPW; ++j) {
+                        if (ok[j]) VecT<T, VC>::load(xrow + (size_t)iw[j] * C + c, xv[j]);
+                        else
+#pragma unroll
+                            for (int v = 0; v < VC; ++v) xv[j][v] = 0.f;
+                    }
+#pragma unroll
+                    for (int a = 0; a < KB; ++a) VecT<T, VC>::load(wt + (size_t)a * taps * p.Cpg + c, wv[a]);
+#pragma unroll
+                    for (int v = 0; v < VC; ++v)
+#pragma unroll
+                        for (int a = 0; a < KB; ++a)
+#pragma unroll
+                            for (int j = 0; j < kPW; ++j) acc[a][j] = fmaf(xv[j][v], wv[a][v], acc[a][j]);
+                }
+            }
+        }
+    }
+    const int ch0 = g * p.Kpg + k0;
+#pragma unroll
+    for (int j = 0; j < kPW; ++j) {
+        if (ow0 + j >= p.Wo) continue;
+        T *yp = y + ((size_t)((n * p.Do + od) * p.Ho + oh) * p.Wo + ow0 + j) * K + ch0;
+#pragma unroll
+        for (int a = 0; a < KB; ++a) yp[a] = finish<T>(acc[a][j], bias, ch0 + a);
+    }
+}
+
+struct Config {
+    int KB, VC, nkb, nwb;
+    long long threads;
+};
+
+void configure(const Problem &p, Config &c)
+{
+    c.KB = p.Kpg % 8 == 0 ? 8 : p.Kpg % 4 == 0 ? 4 : p.Kpg % 2 == 0 ? 2 : 1;
+    c.VC = p.Cpg % 4 == 0 ? 4 : 1;
+    c.nkb = p.Kpg / c.KB;
+    c.nwb = (p.Wo + kPW - 1) / kPW;
+    c.threads = (long long)p.N * p.Do * p.Ho * c.nwb * p.G * c.nkb;
+}
+
+template <typename T, int KB>
+hipError_t go2(const Problem &p, const Config &c, const Args &a, hipStream_t s)
+{
+    const int total = (int)c.threads;
+    const dim3 grid((unsigned)((c.threads + kBlock - 1) / kBlock));
+    if (c.VC == 4)
+        return enqueue(kernel<T, KB, 4>, grid, dim3(kBlock), 0, s, a, p, (const T *)a.x, (const T *)a.w,
+                       (const T *)a.bias, (T *)a.y, c.nkb, c.nwb, total);
+    return enqueue(kernel<T, KB, 1>, grid, dim3(kBlock), 0, s, a, p, (const T *)a.x, (const T *)a.w,
+                   (const T *)a.bias, (T *)a.y, c.nkb, c.nwb, total);
+}
+
+template <typename T>
+hipError_t go(const Problem &p, const Config &c, const Args &a, hipStream_t s)
+{
+    switch (c.KB) {
+    case 8: return go2<T, 8>(p, c, a, s);
+    case 4: return go2<T, 4>(p, c, a, s);
+    case 2: return go2<T, 2>(p, c, a, s);
+    default: return go2<T, 1>(p, c, a, s);
+    }
+}
+
+}  // namespace
+
+bool supported(const Problem &p)
+{
+    Config c;
+    configure(p, c);
+    return c.threads < (1LL << 31);
+}
+
+// Whether the dispatcher should prefer this path over the generic kernel:
+// enough threads to fill the chip with register-blocked work.
+bool preferred(const Problem &p)
+{
+    Config c;
+    configure(p, c);
+    return c.threads >= kMinThreads && c.threads < (1LL << 31);
+}
+
+gconv_plan plan(const Problem &p)
+{
+    Config c;
+    configure(p, c);
+    gconv_plan pl{};
+    pl.path = GCONV_PATH_DIRECT;
+    pl.grid[0] = (uint32_t)((c.threads + kBlock - 1) / kBlock);
+    pl.grid[1] = pl.grid[2] = 1;
+    pl.block = kBlock;
+    pl.lds_bytes = 0;
+    pl.groups_per_tile = 1;
+    return pl;
+}
+
+hipError_t launch(const Problem &p, const Args &a, hipStream_t s)
+{
+    Config c;
+    configure(p, c);
+    if (c.threads >= (1LL << 31)) return hipErrorInvalidValue;
+    switch (p.dtype) {
+    case GCONV_F32: return go<float>(p, c, a, s);
+    case GCONV_F16: return go<_Float16>(p, c, a, s);
+    default: return go<__bf16>(p, c, a, s);
+    }
+}
+
+}  // namespace direct
+}  // namespace gconv

@@ -42,8 +42,9 @@ GCONV_PATH_DEPTHWISE = 1
 GCONV_PATH_SMALLG = 2
 GCONV_PATH_IGEMM = 3
 GCONV_PATH_IGHALO = 4
-GCONV_NUM_PATHS = 5
-PATHS = {"generic": 0, "depthwise": 1, "smallg_mfma": 2, "igemm_mfma": 3, "ighalo_mfma": 4}
+GCONV_PATH_DIRECT = 5
+GCONV_NUM_PATHS = 6
+PATHS = {"generic": 0, "depthwise": 1, "smallg_mfma": 2, "igemm_mfma": 3, "ighalo_mfma": 4, "direct_valu": 5}
 
 EXPORTS = ("gconv_validate", "gconv_out_dims", "gconv_select_path", "gconv_path_supported",
            "gconv_get_plan", "gconv_fwd", "gconv_fwd_path", "gconv_fwd_timed",

@@ -37,10 +37,11 @@ PATH_SOURCES = {
                     "smallg_common.h", "smallg_ring.h"),
     "igemm_mfma": "k_igemm.hip",
     "ighalo_mfma": ("k_ighalo.hip", "k_ighalo_box.hip"),
+    "direct_valu": "k_direct.hip",
 }
 SHARED = ("device_common.h", "gconv_internal.h")
 KERNEL_TAGS = {"generic": "generic", "depthwise": "depthwise", "smallg_mfma": "smallg",
-               "igemm_mfma": "igemm", "ighalo_mfma": "ighalo"}
+               "igemm_mfma": "igemm", "ighalo_mfma": "ighalo", "direct_valu": "direct"}
 
 
 def source_hash(path_name: str) -> str:

@@ -102,7 +102,9 @@ typedef enum gconv_path {
     GCONV_PATH_IGEMM = 3,       /* large groups: M-tiled implicit GEMM, group on grid z, MFMA */
     GCONV_PATH_IGHALO = 4,      /* large groups: implicit GEMM over an LDS input box per
                                    output block, persistent, MFMA */
-    GCONV_NUM_PATHS = 5
+    GCONV_PATH_DIRECT = 5,      /* register-blocked direct kernel on the vector ALUs
+                                   (fp32 grouped; any shape) */
+    GCONV_NUM_PATHS = 6
 } gconv_path;
 
 /* Problem descriptor.  Spatial arrays are (depth, height, width); a 2D

@@ -396,3 +396,28 @@ def test_nonfinite_input_stays_in_its_merged_tile(name, N):
         print("%s path=%s groups_per_tile=%d NaN outside the Inf's group: %d of %d allowed"
               % (name, G.gconv_path_name(path), gpt, int((~np.isfinite(y) & ~ref_bad).sum()),
                  int((may_differ & ~ref_bad).sum())))
+
+
+FP32_GROUPED = [
+    inputs.conv2d("f32", N=4, G=32, C=256, K=256, H=56, W=56, Y=3, X=3, stride=1, pad=1, bias=False),
+    inputs.conv2d("f32", N=2, G=8, C=1024, K=1024, H=14, W=14, Y=3, X=3, stride=1, pad=2, dil=2, bias=True),
+    inputs.conv3d("f32", N=2, G=32, C=64, K=128, D=8, H=28, W=28, Z=3, Y=3, X=3, stride=1, pad=1, bias=True),
+    inputs.Problem(2, "f32", 3, 6, 18, 30, (1, 23, 37), (1, 5, 3), (1, 2, 2), (0, 2, 1), (1, 1, 1), True),
+]
+
+
+@pytest.mark.parametrize("case", range(len(FP32_GROUPED)))
+def test_fp32_grouped_register_blocked_kernel(case):
+    """fp32 grouped problems on the register-blocked VALU kernel, element by
+    element (ResNeXt-style, large groups with dilation 2, 3D, and a ragged
+    one with 3 channels per group, 5 per output group, stride 2)."""
+    p = FP32_GROUPED[case]
+    d = G.desc_from_problem(p)
+    assert G.gconv_path_supported(d, G.GCONV_PATH_DIRECT) == 1
+    t = inputs.make_tensors(p, 77000 + case)
+    y = run_and_fetch(p, t, G.GCONV_PATH_DIRECT)
+    st, pd, dl = p.spatial_args()
+    ref, scale = oracle.conv_fwd(*U.oracle_inputs(p, t), p.G, st, pd, dl)
+    r = U.check(y, ref, scale, p.dtype, "direct_valu case %d" % case)
+    print("direct_valu case %d (auto path %s) max err/tol %.3f"
+          % (case, G.gconv_path_name(G.gconv_select_path(d)), r))

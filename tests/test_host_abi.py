@@ -132,7 +132,7 @@ def _built_paths():
     for name, pid in G.PATHS.items():
         probe = {"depthwise": "depthwise2d_f16", "smallg_mfma": "grouped2d_resnext_bf16",
                  "igemm_mfma": "grouped2d_large_bf16", "ighalo_mfma": "grouped2d_large_bf16",
-                 "generic": "depthwise2d_f16"}[name]
+                 "direct_valu": "grouped2d_small_f32", "generic": "depthwise2d_f16"}[name]
         d = G.desc_from_problem(inputs.WORKLOADS[probe].problem)
         if G.gconv_path_supported(d, pid) == 1:
             out.add(name)
@@ -189,7 +189,8 @@ def test_forced_vector_path_needs_16_byte_alignment():
         if name == "generic" or name not in _built_paths():
             continue
         probe = {"depthwise": "depthwise2d_f16", "smallg_mfma": "grouped2d_resnext_bf16",
-                 "igemm_mfma": "grouped2d_large_bf16", "ighalo_mfma": "grouped2d_large_bf16"}[name]
+                 "igemm_mfma": "grouped2d_large_bf16", "ighalo_mfma": "grouped2d_large_bf16",
+                 "direct_valu": "grouped2d_small_f32"}[name]
         d = G.desc_from_problem(inputs.WORKLOADS[probe].problem)
         assert G.gconv_fwd_path(d, pid, 256 + 2, 256, None, 512) == G.GCONV_ERR_MISALIGNED
         # bias is read in 16-byte vectors too
@@ -392,3 +393,17 @@ def test_noalloc_entry_validates_before_any_hip_call():
     assert G.gconv_bwd_weight_noalloc(d, 0, 256, 256) == G.GCONV_ERR_NULL_PTR
     bad = G.make_desc(2, "f16", 1, 3, 8, 9, (9, 9), (3, 3), (1, 1), (1, 1), (1, 1))
     assert G.gconv_bwd_weight_noalloc(bad, 256, 256, 256) == G.GCONV_ERR_BAD_DESC
+
+
+def test_fp32_grouped_problems_leave_the_generic_kernel():
+    # fp32 ResNeXt-shaped and large-group problems: the register-blocked VALU kernel
+    for C, G_ in ((256, 32), (1024, 8), (96, 32)):
+        d = G.make_desc(2, "f32", 32, G_, C, C, (56, 56), (3, 3), (1, 1), (1, 1), (1, 1))
+        assert G.gconv_path_name(G.gconv_select_path(d)) == "direct_valu"
+    # a 3D fp32 grouped problem as well
+    d = G.make_desc(3, "f32", 8, 32, 64, 128, (8, 28, 28), (3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1))
+    assert G.gconv_path_name(G.gconv_select_path(d)) == "direct_valu"
+    # too little work to fill the chip: the generic kernel's split reductions
+    d = G.desc_from_problem(inputs.WORKLOADS["grouped2d_small_f32"].problem)
+    assert G.gconv_path_name(G.gconv_select_path(d)) == "generic"
+    assert G.gconv_path_supported(d, G.GCONV_PATH_DIRECT) == 1
