@@ -19,6 +19,13 @@
 #define GCONV_API extern "C" __attribute__((visibility("default")))
 
 namespace gconv {
+
+int &tile_choice()
+{
+    static thread_local int choice = -1;
+    return choice;
+}
+
 namespace {
 
 constexpr int64_t kMaxElems = (int64_t)INT32_MAX;  // elements a launch may index in 32 bits
@@ -302,20 +309,55 @@ bool path_ok(const Problem &p, int path)
 // groups in half types merge several groups into one block-diagonal MFMA
 // tile; the rest (fp32 grouped above all) takes the register-blocked VALU
 // kernel when there is enough work to fill the chip, else the generic one.
+//
+// Between the two implicit GEMMs: the halo kernel reuses each staged input
+// pixel across the window's taps, which pays at stride 1 with a window of
+// more than one tap on 2D images and on 3D planes of up to 16 x 16 pixels;
+// the M-tiled one measured faster elsewhere (the tile sweep: 3D planes of
+// 28 x 28 and 56 x 56, stride 2, 1 x 1 windows).  A 1 x 1 window over groups
+// of fewer than 8 input channels measured faster on the VALU kernel.
+bool halo_pays(const Problem &p)
+{
+    if (p.sd != 1 || p.sh != 1 || p.sw != 1 || p.taps() == 1) return false;
+    return p.ndim == 2 || (long long)p.Ho * p.Wo <= 256;
+}
+
 int select(const Problem &p)
 {
     if (p.pd < 0 || p.ph < 0 || p.pw < 0) return GCONV_PATH_GENERIC;
     if (depthwise::supported(p)) return GCONV_PATH_DEPTHWISE;
     if (p.dtype != GCONV_F32 && p.Cpg >= 32 && p.Kpg >= 32) {
-        if (ighalo::supported(p)) return GCONV_PATH_IGHALO;
+        const bool halo = halo_pays(p);
+        if (halo && ighalo::supported(p)) return GCONV_PATH_IGHALO;
         if (igemm::supported(p)) return GCONV_PATH_IGEMM;
+        if (ighalo::supported(p)) return GCONV_PATH_IGHALO;
     }
+    if (p.taps() == 1 && p.Cpg < 8 && direct::preferred(p)) return GCONV_PATH_DIRECT;
     if (smallg::supported(p)) return GCONV_PATH_SMALLG;
     if (ighalo::supported(p)) return GCONV_PATH_IGHALO;
     if (igemm::supported(p)) return GCONV_PATH_IGEMM;
     if (direct::preferred(p)) return GCONV_PATH_DIRECT;
     return GCONV_PATH_GENERIC;
 }
+
+int tiles_of(const Problem &p, int path, int *picked)
+{
+    switch (path) {
+    case GCONV_PATH_DEPTHWISE: return depthwise::tiles(p, picked);
+    case GCONV_PATH_SMALLG: return smallg::tiles(p, picked);
+    case GCONV_PATH_IGEMM: return igemm::tiles(p, picked);
+    case GCONV_PATH_IGHALO: return ighalo::tiles(p, picked);
+    case GCONV_PATH_DIRECT: return direct::tiles(p, picked);
+    default: return generic::tiles(p, picked);
+    }
+}
+
+// Sets the tile choice of this host thread for the length of one call.
+struct TileScope {
+    int saved;
+    explicit TileScope(int t) : saved(tile_choice()) { tile_choice() = t; }
+    ~TileScope() { tile_choice() = saved; }
+};
 
 gconv_plan plan_of(const Problem &p, int path)
 {
@@ -605,8 +647,36 @@ GCONV_API int gconv_get_plan(const gconv_desc *d, int path, gconv_plan *plan)
     if (path == GCONV_PATH_AUTO) path = select(p);
     else if (path < 0 || path >= GCONV_NUM_PATHS) return GCONV_ERR_BAD_PATH;
     else if (!path_ok(p, path)) return GCONV_ERR_PATH_UNSUPPORTED;
+    TileScope own(-1);
     *plan = plan_of(p, path);
     return GCONV_OK;
+}
+
+GCONV_API int gconv_tile_count(const gconv_desc *d, int path, int *picked)
+{
+    int64_t out[3];
+    int rc = check_desc(d, out);
+    if (rc != GCONV_OK) return rc;
+    const Problem p = first_piece(d, out);
+    if (path == GCONV_PATH_AUTO) path = select(p);
+    else if (path < 0 || path >= GCONV_NUM_PATHS) return GCONV_ERR_BAD_PATH;
+    else if (!path_ok(p, path)) return GCONV_ERR_PATH_UNSUPPORTED;
+    TileScope own(-1);
+    int pk = 0;
+    const int n = tiles_of(p, path, &pk);
+    if (picked) *picked = pk;
+    return n;
+}
+
+GCONV_API int gconv_fwd_tile(const gconv_desc *d, int path, int tile, const void *x, const void *w,
+                             const void *bias, void *y, void *stream)
+{
+    if (path == GCONV_PATH_AUTO) return GCONV_ERR_BAD_PATH;
+    const int n = gconv_tile_count(d, path, nullptr);
+    if (n < 0) return n;
+    if (tile < -1 || tile >= n) return GCONV_ERR_BAD_PATH;
+    TileScope scope(tile);
+    return run(d, path, x, w, bias, y, stream);
 }
 
 GCONV_API int gconv_fwd(const gconv_desc *d, const void *x, const void *w, const void *bias,

@@ -68,24 +68,34 @@ inline hipError_t allow_lds(const void *k, std::atomic<unsigned long long> &done
     return e;
 }
 
+// The tile choice of the current call on this host thread: -1 = each
+// path's own pick, k >= 0 = entry k of the path's tile menu (set for the
+// length of one gconv_fwd_tile call).  Each path's `tiles` returns the size
+// of its menu for a problem (>= 1) and stores its own pick in *picked.
+int &tile_choice();
+
 // Per-path hooks.  `supported` and `plan` are pure host functions (no HIP
 // call); `launch` enqueues exactly one kernel on `stream`.
 namespace generic {
+int tiles(const Problem &p, int *picked);
 bool supported(const Problem &p);
 gconv_plan plan(const Problem &p);
 hipError_t launch(const Problem &p, const Args &a, hipStream_t s);
 }
 namespace depthwise {
+int tiles(const Problem &p, int *picked);
 bool supported(const Problem &p);
 gconv_plan plan(const Problem &p);
 hipError_t launch(const Problem &p, const Args &a, hipStream_t s);
 }
 namespace smallg {
+int tiles(const Problem &p, int *picked);
 bool supported(const Problem &p);
 gconv_plan plan(const Problem &p);
 hipError_t launch(const Problem &p, const Args &a, hipStream_t s);
 }
 namespace igemm {
+int tiles(const Problem &p, int *picked);
 bool supported(const Problem &p);
 gconv_plan plan(const Problem &p);
 hipError_t launch(const Problem &p, const Args &a, hipStream_t s);
@@ -93,6 +103,7 @@ hipError_t launch(const Problem &p, const Args &a, hipStream_t s);
 // Register-blocked VALU direct kernel (k_direct.hip); `preferred` says
 // whether it beats the generic kernel for the problem (enough work).
 namespace direct {
+int tiles(const Problem &p, int *picked);
 bool supported(const Problem &p);
 bool preferred(const Problem &p);
 gconv_plan plan(const Problem &p);
@@ -106,6 +117,7 @@ gconv_plan plan(const Problem &p);
 hipError_t launch(const Problem &p, const Args &a, hipStream_t s);
 }
 namespace ighalo {
+int tiles(const Problem &p, int *picked);
 bool supported(const Problem &p);
 gconv_plan plan(const Problem &p);
 hipError_t launch(const Problem &p, const Args &a, hipStream_t s);

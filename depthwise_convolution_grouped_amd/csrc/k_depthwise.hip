@@ -317,12 +317,16 @@ bool configure(const Problem &p, Config &c)
     // Measured on the MobileNetV2 shapes, about one wave per SIMD (1024 in
     // all) with the longest run that gives is best; R comes from a small menu
     // of compiled run lengths (shorter for stride 2, whose runs read twice
-    // the rows).
+    // the rows).  The tile sweep over random shapes found the next longer
+    // run still best up to 1.5x the run that gives 1024 waves.
     const long long wave_rows = (long long)p.Ho * c.nseg * p.N;
     const long long want = (wave_rows + kTargetWaves - 1) / kTargetWaves;
     c.R = 4;
     for (int r : {7, 14, 28})
-        if (r <= want && (p.sh == 1 || r <= 14)) c.R = r;
+        if (2 * r <= 3 * want && (p.sh == 1 || r <= 14)) c.R = r;
+    // tile menu: R = 4, 7, 14 (and 28 at stride 1)
+    const int t = tile_choice();
+    if (t >= 0 && t < (p.sh == 1 ? 4 : 3)) c.R = t == 0 ? 4 : t == 1 ? 7 : t == 2 ? 14 : 28;
     c.nchunk = (p.Ho + c.R - 1) / c.R;
     return row_vecs < (1LL << 30) && (long long)c.nsb * c.nchunk * p.N < (1LL << 31);
 }
@@ -372,6 +376,17 @@ bool supported(const Problem &p)
 {
     Config c;
     return shape_ok(p) && configure(p, c);
+}
+
+int tiles(const Problem &p, int *picked)
+{
+    const int saved = tile_choice();
+    tile_choice() = -1;
+    Config c;
+    configure(p, c);
+    tile_choice() = saved;
+    *picked = c.R == 4 ? 0 : c.R == 7 ? 1 : c.R == 14 ? 2 : 3;
+    return p.sh == 1 ? 4 : 3;
 }
 
 gconv_plan plan(const Problem &p)

@@ -120,9 +120,21 @@ struct Config {
     long long threads;
 };
 
+// tile menu: the output channels per thread among 8, 4, 2, 1 that divide Kpg
+int kb_menu(const Problem &p, int *kb)
+{
+    int n = 0;
+    for (int v : {8, 4, 2, 1})
+        if (p.Kpg % v == 0) kb[n++] = v;
+    return n;
+}
+
 void configure(const Problem &p, Config &c)
 {
-    c.KB = p.Kpg % 8 == 0 ? 8 : p.Kpg % 4 == 0 ? 4 : p.Kpg % 2 == 0 ? 2 : 1;
+    int kb[4];
+    const int n = kb_menu(p, kb);
+    const int t = tile_choice();
+    c.KB = t >= 0 && t < n ? kb[t] : kb[0];
     c.VC = p.Cpg % 4 == 0 ? 4 : 1;
     c.nkb = p.Kpg / c.KB;
     c.nwb = (p.Wo + kPW - 1) / kPW;
@@ -159,6 +171,13 @@ bool supported(const Problem &p)
     Config c;
     configure(p, c);
     return c.threads < (1LL << 31);
+}
+
+int tiles(const Problem &p, int *picked)
+{
+    int kb[4];
+    *picked = 0;
+    return kb_menu(p, kb);
 }
 
 // Whether the dispatcher should prefer this path over the generic kernel:

@@ -62,12 +62,19 @@ __global__ __launch_bounds__(kBlock) void kernel(Problem p, const T *__restrict_
 
 // threads per output: enough threads to fill the chip, at most the channels
 // a thread would otherwise walk alone
-int lanes_for(const Problem &p)
+int own_lanes(const Problem &p)
 {
     const long long outs = p.y_elems();
     int L = 1;
     while (L < 16 && outs * L < 256LL * kBlock && 2 * L <= p.Cpg * p.taps()) L *= 2;
     return L;
+}
+
+// tile menu: L = 1, 2, 4, 8, 16 threads per output
+int lanes_for(const Problem &p)
+{
+    const int t = tile_choice();
+    return t >= 0 && t < 5 ? 1 << t : own_lanes(p);
 }
 
 template <int DT, int L>
@@ -95,6 +102,14 @@ hipError_t go(const Problem &p, const Args &a, hipStream_t s)
 }  // namespace
 
 bool supported(const Problem &) { return true; }
+
+int tiles(const Problem &p, int *picked)
+{
+    int L = own_lanes(p), i = 0;
+    while ((1 << i) < L) ++i;
+    *picked = i;
+    return 5;
+}
 
 gconv_plan plan(const Problem &p)
 {

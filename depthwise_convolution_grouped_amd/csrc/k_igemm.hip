@@ -270,8 +270,29 @@ bool configure(const Problem &p, Config &c)
     if (xb >= (1LL << 31) || wb >= (1LL << 31)) return false;
     const long long M = (long long)p.N * p.Do * p.Ho * p.Wo;
     if (M >= (1LL << 31)) return false;
+    // Own pick (from the tile sweep): the widest output-channel tile with
+    // 32-channel reduction steps (half the LDS, more workgroups resident),
+    // unless that leaves fewer than two workgroups per CU: then 64-channel
+    // tiles with 64-channel steps.
+    const long long mt = (M + BM - 1) / BM;
     c.BN = p.Kpg % 128 == 0 ? 128 : (p.Kpg % 64 == 0 ? 64 : 32);
-    c.KT = p.Cpg % 64 == 0 ? 64 : 32;
+    c.KT = 32;
+    if (mt * (p.Kpg / c.BN) * p.G < 512 && c.BN == 128 && p.Cpg % 64 == 0) {
+        c.BN = 64;
+        c.KT = 64;
+    }
+    // tile menu: (BN, KT) over BN in 128, 64, 32 dividing Kpg and KT in 64,
+    // 32 dividing Cpg, largest first
+    const int t = tile_choice();
+    if (t >= 0) {
+        int i = 0;
+        for (int bn : {128, 64, 32})
+            for (int kt : {64, 32})
+                if (p.Kpg % bn == 0 && p.Cpg % kt == 0 && i++ == t) {
+                    c.BN = bn;
+                    c.KT = kt;
+                }
+    }
     c.mtiles = (int)((M + BM - 1) / BM);
     c.ntiles = p.Kpg / c.BN;
     c.stages = p.taps() * p.Cpg / c.KT;
@@ -317,6 +338,24 @@ bool supported(const Problem &p)
 {
     Config c;
     return configure(p, c);
+}
+
+int tiles(const Problem &p, int *picked)
+{
+    const int saved = tile_choice();
+    tile_choice() = -1;
+    Config c;
+    const bool ok = configure(p, c);
+    tile_choice() = saved;
+    int n = 0;
+    *picked = 0;
+    for (int bn : {128, 64, 32})
+        for (int kt : {64, 32})
+            if (p.Kpg % bn == 0 && p.Cpg % kt == 0) {
+                if (ok && bn == c.BN && kt == c.KT) *picked = n;
+                ++n;
+            }
+    return n < 1 ? 1 : n;
 }
 
 gconv_plan plan(const Problem &p)

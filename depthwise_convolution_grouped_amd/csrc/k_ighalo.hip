@@ -622,15 +622,32 @@ hipError_t go(const Problem &p, const Config &c, const Args &a, hipStream_t s)
 
 }  // namespace
 
+// tile menu: the whole-box variant (where it applies), then the
+// chunk-streaming one (where it applies); the own pick is the first
+bool use_box(const Problem &p)
+{
+    if (!ighalo_box::supported(p)) return false;
+    const int t = tile_choice();
+    Config c;
+    return !(t == 1 && configure(p, c));
+}
+
 bool supported(const Problem &p)
 {
     Config c;
     return ighalo_box::supported(p) || configure(p, c);
 }
 
+int tiles(const Problem &p, int *picked)
+{
+    Config c;
+    *picked = 0;
+    return (ighalo_box::supported(p) ? 1 : 0) + (configure(p, c) ? 1 : 0);
+}
+
 gconv_plan plan(const Problem &p)
 {
-    if (ighalo_box::supported(p)) return ighalo_box::plan(p);
+    if (use_box(p)) return ighalo_box::plan(p);
     Config c;
     configure(p, c);
     gconv_plan pl{};
@@ -646,7 +663,7 @@ gconv_plan plan(const Problem &p)
 
 hipError_t launch(const Problem &p, const Args &a, hipStream_t s)
 {
-    if (ighalo_box::supported(p)) return ighalo_box::launch(p, a, s);
+    if (use_box(p)) return ighalo_box::launch(p, a, s);
     Config c;
     if (!configure(p, c)) return hipErrorInvalidValue;
     if (p.dtype == GCONV_F16) return go<_Float16>(p, c, a, s);

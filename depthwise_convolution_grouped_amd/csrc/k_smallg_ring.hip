@@ -82,6 +82,14 @@ bool ring_configure(const Problem &p, RingConfig &c)
     return blocks < (1LL << 31);
 }
 
+void ring_set_rows(const Problem &p, RingConfig &c, int R)
+{
+    if (p.ndim != 2 || p.sh != 1 || (R != 14 && R != 28)) return;
+    c.R = R;
+    c.nchunk = (p.Ho + c.R - 1) / c.R;
+    c.blocks = (int)((long long)c.nmt * c.nchunk * c.ntb * p.Do * p.N);
+}
+
 hipError_t ring_launch(const Problem &p, const RingConfig &c, const Args &a, hipStream_t s)
 {
     if (c.DZ == 3) return ring3d_launch(p, c, a, s);

@@ -151,6 +151,9 @@ struct RingConfig {
     int GN, CH8, NT, NTW, TPB, ntb, DZ, R, CV, IW, RS, NINS, nmt, nchunk, blocks, lds;
 };
 bool ring_configure(const Problem &p, RingConfig &c);
+// Rows per workgroup of a configured ring: 14 or 28 for 2D stride 1 (the
+// tile menu), the configured value otherwise.
+void ring_set_rows(const Problem &p, RingConfig &c, int R);
 hipError_t ring_launch(const Problem &p, const RingConfig &c, const Args &a, hipStream_t s);
 hipError_t ring3d_launch(const Problem &p, const RingConfig &c, const Args &a, hipStream_t s);
 

@@ -48,6 +48,7 @@ PATHS = {"generic": 0, "depthwise": 1, "smallg_mfma": 2, "igemm_mfma": 3, "ighal
 
 EXPORTS = ("gconv_validate", "gconv_out_dims", "gconv_select_path", "gconv_path_supported",
            "gconv_get_plan", "gconv_fwd", "gconv_fwd_path", "gconv_fwd_timed",
+           "gconv_tile_count", "gconv_fwd_tile",
            "gconv_bwd_data_workspace", "gconv_bwd_data", "gconv_bwd_data_direct",
            "gconv_bwd_weight_workspace", "gconv_bwd_weight", "gconv_bwd_weight_noalloc",
            "gconv_status_str", "gconv_path_name", "gconv_abi_version")
@@ -105,6 +106,8 @@ def lib():
     L.gconv_fwd.argtypes = [pd, vp, vp, vp, vp, vp]
     L.gconv_fwd_path.argtypes = [pd, ctypes.c_int, vp, vp, vp, vp, vp]
     L.gconv_fwd_timed.argtypes = [pd, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp]
+    L.gconv_tile_count.argtypes = [pd, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    L.gconv_fwd_tile.argtypes = [pd, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp]
     L.gconv_bwd_data_workspace.argtypes = [pd, ctypes.POINTER(ctypes.c_size_t)]
     L.gconv_bwd_data.argtypes = [pd, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.gconv_bwd_data_direct.argtypes = [pd, vp, vp, vp, vp]
@@ -118,7 +121,7 @@ def lib():
     L.gconv_abi_version.argtypes = []
     for name in ("gconv_validate", "gconv_out_dims", "gconv_select_path", "gconv_path_supported",
                  "gconv_get_plan", "gconv_fwd", "gconv_fwd_path", "gconv_fwd_timed",
-                 "gconv_bwd_data_workspace", "gconv_bwd_data", "gconv_bwd_data_direct",
+                 "gconv_tile_count", "gconv_fwd_tile", "gconv_bwd_data_workspace", "gconv_bwd_data", "gconv_bwd_data_direct",
                  "gconv_bwd_weight_workspace", "gconv_bwd_weight", "gconv_bwd_weight_noalloc", "gconv_abi_version"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -238,6 +241,21 @@ def gconv_bwd_weight_noalloc(d: gconv_desc, x: int, dy: int, dw: int, stream: in
     """Raw call with device addresses (ints); the library's own device scratch
     holds the partial sums.  Returns the status code."""
     return lib().gconv_bwd_weight_noalloc(ctypes.byref(d), x, dy, dw, stream or None)
+
+
+def gconv_tile_count(d: gconv_desc, path: int = GCONV_PATH_AUTO):
+    """(menu size, the path's own pick) for d on `path`; raises GconvError on a bad descriptor or path."""
+    picked = ctypes.c_int(-1)
+    n = lib().gconv_tile_count(ctypes.byref(d), int(path), ctypes.byref(picked))
+    if n < 0:
+        raise GconvError(n, "gconv_tile_count")
+    return n, picked.value
+
+
+def gconv_fwd_tile(d: gconv_desc, path: int, tile: int, x: int, w: int, bias: Optional[int], y: int,
+                   stream: int = 0) -> int:
+    """Raw call with device addresses (ints); returns the status code."""
+    return lib().gconv_fwd_tile(ctypes.byref(d), int(path), int(tile), x, w, bias or None, y, stream or None)
 
 
 def gconv_status_str(status: int) -> str:

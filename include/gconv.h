@@ -193,6 +193,23 @@ int gconv_fwd(const gconv_desc *d, const void *x, const void *w,
 int gconv_fwd_path(const gconv_desc *d, int path, const void *x, const void *w,
                    const void *bias, void *y, void *stream);
 
+/* Tile variants of `path` (GCONV_PATH_AUTO: the selected path) for d: the
+ * size of the path's tile menu (>= 1) or a negative status; *picked (may
+ * be NULL) receives the index of the path's own analytic pick.  The menus
+ * (run lengths, rows per workgroup, kernel variant, output-channel and
+ * reduction tiles, threads per output) are the counterpart of the tile
+ * sizes and pipeline variants the CK grouped_conv tile-engine README
+ * enumerates per problem (How It Works, Kernel Enumeration); measuring each
+ * is how the analytic pick is checked against the best. */
+int gconv_tile_count(const gconv_desc *d, int path, int *picked);
+
+/* As gconv_fwd_path on a named path (not GCONV_PATH_AUTO) with tile
+ * variant `tile` of its menu (0 .. gconv_tile_count - 1; -1 = the path's own
+ * pick).  Every variant computes the same result within the tolerance of
+ * the fp32 accumulation; for tests and tile sweeps. */
+int gconv_fwd_tile(const gconv_desc *d, int path, int tile, const void *x, const void *w,
+                   const void *bias, void *y, void *stream);
+
 /* As gconv_fwd_path, and binds two HIP events (hipEvent_t, either may be
  * NULL; created by the caller, with timing enabled) to the kernel dispatch
  * (the start event to the first and the stop event to the last launch of a

@@ -421,3 +421,35 @@ def test_fp32_grouped_register_blocked_kernel(case):
     r = U.check(y, ref, scale, p.dtype, "direct_valu case %d" % case)
     print("direct_valu case %d (auto path %s) max err/tol %.3f"
           % (case, G.gconv_path_name(G.gconv_select_path(d)), r))
+
+
+TILE_CASES = [("depthwise2d_f16", 2), ("depthwise2d_s2_f16", 2), ("grouped2d_resnext_bf16", 2),
+              ("grouped3d_f16_n8", 1), ("grouped2d_large_bf16", 2), ("grouped2d_large_dil2_bf16", 1)]
+
+
+@pytest.mark.parametrize("name,N", TILE_CASES)
+def test_every_tile_of_every_path(name, N):
+    """Every entry of every path's tile menu (gconv_fwd_tile) matches the oracle."""
+    wl = inputs.WORKLOADS[name]
+    p = reduced(wl.problem, N)
+    t = inputs.make_tensors(p, wl.seed + 11, wl.x_dist, wl.w_dist, wl.b_dist)
+    st, pd, dl = p.spatial_args()
+    ref, scale = oracle.conv_fwd(*U.oracle_inputs(p, t), p.G, st, pd, dl)
+    d = G.desc_from_problem(p)
+    x, w, b = U.device_tensors(p, t)
+    ran = 0
+    for path, pid in G.PATHS.items():
+        if path == "generic" or G.gconv_path_supported(d, pid) != 1:
+            continue
+        n, _ = G.gconv_tile_count(d, pid)
+        for tile in range(n):
+            y = poisoned_out(p)
+            rc = G.gconv_fwd_tile(d, pid, tile, x.data_ptr(), w.data_ptr(),
+                                  b.data_ptr() if b is not None else None, y.data_ptr(),
+                                  torch.cuda.current_stream().cuda_stream)
+            assert rc == 0, G.gconv_status_str(rc)
+            torch.cuda.synchronize()
+            U.check(U.to_f64(y), ref, scale, p.dtype, "%s path=%s tile=%d" % (name, path, tile))
+            ran += 1
+    assert ran >= 2
+    print("%s N=%d: %d tile variants checked" % (name, N, ran))

@@ -407,3 +407,24 @@ def test_fp32_grouped_problems_leave_the_generic_kernel():
     d = G.desc_from_problem(inputs.WORKLOADS["grouped2d_small_f32"].problem)
     assert G.gconv_path_name(G.gconv_select_path(d)) == "generic"
     assert G.gconv_path_supported(d, G.GCONV_PATH_DIRECT) == 1
+
+
+def test_tile_menus():
+    # depthwise: run lengths 4, 7, 14, 28 (stride 1) / 4, 7, 14 (stride 2)
+    n, pk = G.gconv_tile_count(G.desc_from_problem(inputs.WORKLOADS["depthwise2d_f16"].problem))
+    assert n == 4 and 0 <= pk < 4
+    n, pk = G.gconv_tile_count(G.desc_from_problem(inputs.WORKLOADS["depthwise2d_s2_f16"].problem))
+    assert n == 3 and 0 <= pk < 3
+    # small groups 2D stride 1: ring with 14 or 28 rows, then the other variants that apply
+    d = G.desc_from_problem(inputs.WORKLOADS["grouped2d_resnext_bf16"].problem)
+    n, pk = G.gconv_tile_count(d)
+    assert n >= 3 and pk in (0, 1)
+    # generic: 1, 2, 4, 8, 16 threads per output, on any problem
+    assert G.gconv_tile_count(d, G.GCONV_PATH_GENERIC)[0] == 5
+    # a path that cannot take the problem, and AUTO on the tile entry, are errors
+    with pytest.raises(G.GconvError):
+        G.gconv_tile_count(d, G.GCONV_PATH_DEPTHWISE)
+    assert G.gconv_fwd_tile(d, G.GCONV_PATH_AUTO, 0, 256, 256, None, 512) == G.GCONV_ERR_BAD_PATH
+    assert G.gconv_fwd_tile(d, G.GCONV_PATH_SMALLG, n, 256, 256, None, 512) == G.GCONV_ERR_BAD_PATH
+    # the plan of the own pick does not depend on a tile choice made before
+    assert G.gconv_get_plan(d) == G.gconv_get_plan(d, G.gconv_select_path(d))
