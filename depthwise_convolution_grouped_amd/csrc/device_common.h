@@ -126,6 +126,26 @@ __device__ __forceinline__ void vm_wait(int n)
         : "s96", "s97", "s98", "scc", "memory");
 }
 
+// n / d for 0 <= n < 2^16 and 1 <= d < 2^16 as umulhi(n, m) with
+// m = ceil(2^32 / d): the rounding error n * (m - 2^32 / d) / 2^32 stays below
+// 1 / d when n * d < 2^32, so the floor is exact.  d = 1 would need m = 2^32
+// and is passed through unchanged.
+struct Div {
+    unsigned m;
+    int d;
+};
+inline Div make_div(int d)
+{
+    Div r;
+    r.d = d;
+    r.m = d > 1 ? (unsigned)((0x100000000ull + (unsigned long long)d - 1) / (unsigned long long)d) : 0u;
+    return r;
+}
+__device__ __forceinline__ int fdiv(int n, Div v)
+{
+    return v.d == 1 ? n : (int)__umulhi((unsigned)n, v.m);
+}
+
 // Epilogue for one output element: optional bias of output channel `ch`.
 template <typename T>
 __device__ __forceinline__ T finish(float acc, const T *__restrict__ bias, int ch)

@@ -307,19 +307,23 @@ bool path_ok(const Problem &p, int path)
 // direct kernel; large per-group contractions (Cpg, Kpg >= 32, half types)
 // are a real GEMM per group and go to the implicit-GEMM MFMA kernel; small
 // groups in half types merge several groups into one block-diagonal MFMA
-// tile; the rest (fp32 grouped above all) takes the register-blocked VALU
-// kernel when there is enough work to fill the chip, else the generic one.
+// tile; half-type groups neither takes (8k input channels that are not 32k,
+// more than 16 output channels over narrow inputs) run the M-tiled implicit
+// GEMM with its K walked in 8-channel chunks; the rest (fp32 grouped above
+// all) takes the register-blocked VALU kernel when there is enough work to
+// fill the chip, else the generic one.
 //
 // Between the two implicit GEMMs: the halo kernel reuses each staged input
 // pixel across the window's taps, which pays at stride 1 with a window of
-// more than one tap on 2D images and on 3D planes of up to 16 x 16 pixels;
-// the M-tiled one measured faster elsewhere (the tile sweep: 3D planes of
-// 28 x 28 and 56 x 56, stride 2, 1 x 1 windows).  A 1 x 1 window over groups
+// more than one tap on 2D images, on 3D planes of up to 16 x 16 pixels and
+// wherever its whole-box variant covers the problem in one round of
+// workgroups; the M-tiled one measured faster elsewhere (the tile sweep: 3D
+// planes of 28 x 28 and 56 x 56 in several rounds, stride 2, 1 x 1 windows).  A 1 x 1 window over groups
 // of fewer than 8 input channels measured faster on the VALU kernel.
 bool halo_pays(const Problem &p)
 {
     if (p.sd != 1 || p.sh != 1 || p.sw != 1 || p.taps() == 1) return false;
-    return p.ndim == 2 || (long long)p.Ho * p.Wo <= 256;
+    return p.ndim == 2 || (long long)p.Ho * p.Wo <= 256 || ighalo_box::supported(p);
 }
 
 int select(const Problem &p)

@@ -1,5 +1,6 @@
 // Implicit-GEMM grouped convolution on the matrix cores (fp16 / bf16, 2D and
-// 3D), for groups with many channels (Cpg % 32 == 0, Kpg % 32 == 0).
+// 3D), for groups of 8k input and 4k output channels that the small-group
+// kernels do not take (wider groups, or more output than input channels).
 //
 // Per group g the convolution is a GEMM: M = output pixels (N * Do * Ho *
 // Wo), N = Kpg output channels, K = taps * Cpg.  The group is the grid's z
@@ -7,11 +8,16 @@
 // scheme of rocm-libraries PR 10064 (Technical Details: the launch grid is
 // (gn, gm, groups)).  K is decoded into (tap, channel in group) with the
 // channel fastest, as that page's A descriptor does, so the im2col operand is
-// never materialised: for one K stage (one tap, KT consecutive channels) each
-// output pixel needs KT contiguous input channels of one input pixel, or
-// zeros when the tap falls into the padding.  The weight operand of a stage
-// is KT contiguous values of each output channel's GKZYXC row (the B
-// descriptor's channel extent is Cpg).
+// never materialised.  When KT divides Cpg a K stage is one tap and KT
+// consecutive channels: each output pixel needs KT contiguous input channels
+// of one input pixel, or zeros when the tap falls into the padding.  Other
+// widths (Cpg = 8, 16, 24, 40, ...) walk K in 8-channel chunks q = tap *
+// Cpg/8 + c8, KT/8 chunks per stage, so a stage may span taps: each 16-byte
+// slot decodes its own (tap, chunk), and chunks past taps * Cpg/8 are zero.
+// Either way the weight operand of a stage is KT contiguous values of each
+// output channel's GKZYXC row (the B descriptor's channel extent is Cpg).
+// Output-channel tiles past Kpg (Kpg not a multiple of BN) read zero weights
+// and store nothing.
 //
 // A workgroup (4 waves, 2 x 2) computes a BM x BN output tile.  Every K stage
 // of both operands is staged in LDS by direct-to-LDS buffer loads (zero fill
@@ -44,7 +50,9 @@ struct Params {
     int sd, sh, sw, pd, ph, pw, dd, dh, dw;
     int M;                 // N * Do * Ho * Wo
     int mtiles, ntiles;    // grid x, y
-    int stages;            // taps * Cpg / KT
+    int stages;            // K stages: ceil(taps * Cpg / KT)
+    int nq8;               // 8-channel chunks of K: taps * Cpg / 8
+    Div dCH8, dX, dY;      // Cpg / 8, X, Y (chunk decode of the general K walk)
     unsigned x_bytes, w_bytes;
 };
 
@@ -87,8 +95,9 @@ template <> struct Mfma<__bf16> {
 };
 
 // BN: output channels per tile (32, 64 or 128; each of the two waves along
-// N takes BN / 2); KT: K per stage (32 or 64).
-template <typename T, int BN, int KT>
+// N takes BN / 2); KT: K per stage (32 or 64); CHUNKED: K walked in 8-channel
+// chunks across taps (KT does not divide Cpg).
+template <typename T, int BN, int KT, bool CHUNKED>
 __global__ __launch_bounds__(kBlock) void kernel(Params q, const T *__restrict__ x,
                                                  const T *__restrict__ w,
                                                  const T *__restrict__ bias, T *__restrict__ y)
@@ -160,24 +169,37 @@ __global__ __launch_bounds__(kBlock) void kernel(Params q, const T *__restrict__
             if (L < B_SLOTS && n0 + row < q.Kpg) ld_wrow[i] = g * q.Kpg + n0 + row;
         }
     }
-    // issue stage st (tap st / (Cpg/KT), channels c0 .. c0+KT-1) into buffer b
-    const int cstages = q.Cpg / KT;
+    // issue stage st into buffer b: tap st / (Cpg/KT), channels c0 .. c0+KT-1,
+    // or, chunked, chunks st * KT/8 .. st * KT/8 + KT/8 - 1 of the K walk
+    const int cstages = CHUNKED ? 1 : q.Cpg / KT;
     auto issue = [&](int st, int b) {
-        const int tap = st / cstages;
-        const int c0 = (st - tap * cstages) * KT;
-        const int xx = tap % q.X, yy = (tap / q.X) % q.Y, zz = tap / (q.X * q.Y);
+        int tap = st / cstages;
+        int c0 = (st - tap * cstages) * KT;
+        int xx = tap % q.X, yy = (tap / q.X) % q.Y, zz = tap / (q.X * q.Y);
         const unsigned base = lds_b + (unsigned)(b * STAGE_BYTES);
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
             if (i < nld) {
                 unsigned vo = kOob;
-                if (ld_kind[i] == 1 && ld_slot[i] < RS - 1 && ld_pix_n[i] >= 0) {
+                bool live = true;
+                if constexpr (CHUNKED) {
+                    // this slot's chunk: its own tap and 8 channels
+                    const int q8 = st * (KT / 8) + ld_slot[i];
+                    live = q8 < q.nq8;
+                    tap = fdiv(q8, q.dCH8);
+                    c0 = (q8 - tap * q.dCH8.d) * 8 - ld_slot[i] * 8;
+                    const int t1 = fdiv(tap, q.dX);
+                    xx = tap - t1 * q.X;
+                    zz = fdiv(t1, q.dY);
+                    yy = t1 - zz * q.Y;
+                }
+                if (ld_kind[i] == 1 && ld_slot[i] < RS - 1 && ld_pix_n[i] >= 0 && live) {
                     const int id = ld_pix_d[i] + zz * q.dd, ih = ld_pix_h[i] + yy * q.dh,
                               iw = ld_pix_w[i] + xx * q.dw;
                     if (id >= 0 && id < q.D && ih >= 0 && ih < q.H && iw >= 0 && iw < q.W)
                         vo = ((unsigned)(((ld_pix_n[i] * q.D + id) * q.H + ih) * q.W + iw) * (unsigned)q.C +
                               (unsigned)(g * q.Cpg + c0 + ld_slot[i] * 8)) * es;
-                } else if (ld_kind[i] == 2 && ld_slot[i] < RS - 1 && ld_wrow[i] >= 0) {
+                } else if (ld_kind[i] == 2 && ld_slot[i] < RS - 1 && ld_wrow[i] >= 0 && live) {
                     vo = ((unsigned)(ld_wrow[i] * taps + tap) * (unsigned)q.Cpg +
                           (unsigned)(c0 + ld_slot[i] * 8)) * es;
                 }
@@ -258,51 +280,94 @@ __global__ __launch_bounds__(kBlock) void kernel(Params q, const T *__restrict__
 // ----------------------------------------------------------------- host side
 
 struct Config {
-    int BN, KT, mtiles, ntiles, stages, lds;
+    int BN, KT, mtiles, ntiles, stages, nq8, lds;
+    bool chunked;
 };
+
+// Groups of 32k input and output channels ("wide") run one tap per stage;
+// other widths need 8k input and 4k output channels and walk K in chunks.
+bool wide(const Problem &p) { return p.Cpg % 32 == 0 && p.Kpg % 32 == 0; }
+
+// Tile menu: (BN, KT) pairs, widest first.  Wide groups take BN dividing Kpg
+// and KT dividing Cpg; other widths take BN of 32, or 64 and 128 while the
+// tile is less than twice Kpg, each with both KT.
+int menu(const Problem &p, int (*m)[2])
+{
+    const bool wd = wide(p);
+    int n = 0;
+    for (int bn : {128, 64, 32})
+        for (int kt : {64, 32}) {
+            const bool ok = wd ? (p.Kpg % bn == 0 && p.Cpg % kt == 0) : (bn == 32 || bn < 2 * p.Kpg);
+            if (ok) {
+                m[n][0] = bn;
+                m[n][1] = kt;
+                ++n;
+            }
+        }
+    return n;
+}
+
+// Own pick (from the tile sweep).  Wide groups: the widest output-channel
+// tile with 32-channel reduction steps (half the LDS, more workgroups
+// resident); with fewer 128-channel tiles than CUs, 64-channel tiles with
+// 64-channel steps; 64-channel tiles take 64-channel steps while there are
+// fewer than two per CU.  Other widths: the widest tile that pads Kpg no more
+// than 32-channel tiles do, with 32-channel steps.
+void own_pick(const Problem &p, long long mt, Config &c)
+{
+    c.KT = 32;
+    if (wide(p)) {
+        c.BN = p.Kpg % 128 == 0 ? 128 : (p.Kpg % 64 == 0 ? 64 : 32);
+        const long long tiles = mt * (p.Kpg / c.BN) * p.G;
+        if (c.BN == 128 && tiles < 256 && p.Cpg % 64 == 0) {
+            c.BN = 64;
+            c.KT = 64;
+        } else if (c.BN == 64 && tiles < 512 && p.Cpg % 64 == 0) {
+            c.KT = 64;
+        }
+        return;
+    }
+    const int pad32 = (p.Kpg + 31) / 32 * 32;
+    c.BN = 32;
+    for (int bn : {128, 64})
+        if (bn < 2 * p.Kpg && (p.Kpg + bn - 1) / bn * bn <= pad32) {
+            c.BN = bn;
+            break;
+        }
+}
 
 bool configure(const Problem &p, Config &c)
 {
     if (p.dtype != GCONV_F16 && p.dtype != GCONV_BF16) return false;
-    if (p.Cpg % 32 != 0 || p.Kpg % 32 != 0) return false;
+    if (p.Cpg % 8 != 0 || p.Kpg % 4 != 0) return false;
     const long long xb = (long long)p.N * p.D * p.H * p.W * p.C() * 2;
     const long long wb = (long long)p.K() * p.taps() * p.Cpg * 2;
     if (xb >= (1LL << 31) || wb >= (1LL << 31)) return false;
     const long long M = (long long)p.N * p.Do * p.Ho * p.Wo;
     if (M >= (1LL << 31)) return false;
-    // Own pick (from the tile sweep): the widest output-channel tile with
-    // 32-channel reduction steps (half the LDS, more workgroups resident),
-    // unless that leaves fewer than two workgroups per CU: then 64-channel
-    // tiles with 64-channel steps.
+    // the chunk decode divides exactly below 2^16
+    const long long nq8 = (long long)p.taps() * (p.Cpg / 8);
+    if (nq8 + 8 >= (1LL << 16)) return false;
     const long long mt = (M + BM - 1) / BM;
-    c.BN = p.Kpg % 128 == 0 ? 128 : (p.Kpg % 64 == 0 ? 64 : 32);
-    c.KT = 32;
-    if (mt * (p.Kpg / c.BN) * p.G < 512 && c.BN == 128 && p.Cpg % 64 == 0) {
-        c.BN = 64;
-        c.KT = 64;
-    }
-    // tile menu: (BN, KT) over BN in 128, 64, 32 dividing Kpg and KT in 64,
-    // 32 dividing Cpg, largest first
+    own_pick(p, mt, c);
     const int t = tile_choice();
-    if (t >= 0) {
-        int i = 0;
-        for (int bn : {128, 64, 32})
-            for (int kt : {64, 32})
-                if (p.Kpg % bn == 0 && p.Cpg % kt == 0 && i++ == t) {
-                    c.BN = bn;
-                    c.KT = kt;
-                }
+    int m[6][2];
+    if (t >= 0 && t < menu(p, m)) {
+        c.BN = m[t][0];
+        c.KT = m[t][1];
     }
-    c.mtiles = (int)((M + BM - 1) / BM);
-    c.ntiles = p.Kpg / c.BN;
-    c.stages = p.taps() * p.Cpg / c.KT;
+    c.chunked = p.Cpg % c.KT != 0;
+    c.nq8 = (int)nq8;
+    c.mtiles = (int)mt;
+    c.ntiles = (p.Kpg + c.BN - 1) / c.BN;
+    c.stages = (int)((nq8 + c.KT / 8 - 1) / (c.KT / 8));
     const int RS = c.KT / 8 + 1;
     c.lds = 2 * (BM + c.BN) * RS * 16;
     return c.mtiles < (1 << 30) && c.ntiles < 65536 && p.G < 65536;
 }
 
-template <typename T, int BN, int KT>
-hipError_t go3(const Problem &p, const Config &c, const Args &a, hipStream_t s)
+template <typename T, int BN, int KT, bool CHUNKED>
+hipError_t go4(const Problem &p, const Config &c, const Args &a, hipStream_t s)
 {
     Params q;
     q.N = p.N; q.G = p.G; q.Cpg = p.Cpg; q.Kpg = p.Kpg; q.C = p.C(); q.K = p.K();
@@ -311,10 +376,11 @@ hipError_t go3(const Problem &p, const Config &c, const Args &a, hipStream_t s)
     q.sd = p.sd; q.sh = p.sh; q.sw = p.sw; q.pd = p.pd; q.ph = p.ph; q.pw = p.pw;
     q.dd = p.dd; q.dh = p.dh; q.dw = p.dw;
     q.M = p.N * p.Do * p.Ho * p.Wo;
-    q.mtiles = c.mtiles; q.ntiles = c.ntiles; q.stages = c.stages;
+    q.mtiles = c.mtiles; q.ntiles = c.ntiles; q.stages = c.stages; q.nq8 = c.nq8;
+    q.dCH8 = make_div(p.Cpg / 8); q.dX = make_div(p.X); q.dY = make_div(p.Y);
     q.x_bytes = (unsigned)((long long)p.N * p.D * p.H * p.W * p.C() * 2);
     q.w_bytes = (unsigned)((long long)p.K() * p.taps() * p.Cpg * 2);
-    auto k = kernel<T, BN, KT>;
+    auto k = kernel<T, BN, KT, CHUNKED>;
     static std::atomic<unsigned long long> lds_set{0};
     if (c.lds > 64 * 1024) {
         const hipError_t e = allow_lds((const void *)k, lds_set, 160 * 1024);
@@ -322,6 +388,12 @@ hipError_t go3(const Problem &p, const Config &c, const Args &a, hipStream_t s)
     }
     return enqueue(k, dim3(c.mtiles, c.ntiles, p.G), dim3(kBlock), c.lds, s, a, q,
                    (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y);
+}
+
+template <typename T, int BN, int KT>
+hipError_t go3(const Problem &p, const Config &c, const Args &a, hipStream_t s)
+{
+    return c.chunked ? go4<T, BN, KT, true>(p, c, a, s) : go4<T, BN, KT, false>(p, c, a, s);
 }
 
 template <typename T>
@@ -347,14 +419,11 @@ int tiles(const Problem &p, int *picked)
     Config c;
     const bool ok = configure(p, c);
     tile_choice() = saved;
-    int n = 0;
+    int m[6][2];
+    const int n = menu(p, m);
     *picked = 0;
-    for (int bn : {128, 64, 32})
-        for (int kt : {64, 32})
-            if (p.Kpg % bn == 0 && p.Cpg % kt == 0) {
-                if (ok && bn == c.BN && kt == c.KT) *picked = n;
-                ++n;
-            }
+    for (int i = 0; i < n; ++i)
+        if (ok && m[i][0] == c.BN && m[i][1] == c.KT) *picked = i;
     return n < 1 ? 1 : n;
 }
 

@@ -21,26 +21,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-// n / d for 0 <= n < 2^16 and 1 <= d < 2^16 as umulhi(n, m) with
-// m = ceil(2^32 / d): the rounding error n * (m - 2^32 / d) / 2^32 stays below
-// 1 / d when n * d < 2^32, so the floor is exact.  d = 1 would need m = 2^32
-// and is passed through unchanged.
-struct Div {
-    unsigned m;
-    int d;
-};
-inline Div make_div(int d)
-{
-    Div r;
-    r.d = d;
-    r.m = d > 1 ? (unsigned)((0x100000000ull + (unsigned long long)d - 1) / (unsigned long long)d) : 0u;
-    return r;
-}
-__device__ __forceinline__ int fdiv(int n, Div v)
-{
-    return v.d == 1 ? n : (int)__umulhi((unsigned)n, v.m);
-}
-
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, unsigned bytes)
 {
     const unsigned long long a = (unsigned long long)base;

@@ -4,7 +4,9 @@
   in seconds, else at sampled outputs (random positions plus every corner);
 * reduced-batch versions of the large workloads element by element;
 * every kernel path forced on shapes it can take, including random small
-  2D/3D problems with odd channel counts, strides, paddings and dilations;
+  2D/3D problems with odd channel counts, strides, paddings and dilations,
+  and every tile of each path's menu on the workloads and on group widths
+  off the 32-channel grid;
 * output poisoned with NaN before the call (every element must be written),
   canary elements after y (nothing written past the end), bitwise run-to-run
   determinism, and a non-default stream.
@@ -357,6 +359,52 @@ def test_igemm_32_channel_tiles(case):
     y = run_and_fetch(p, t, G.GCONV_PATH_IGEMM)
     r = U.check(y, ref, scale, p.dtype, "igemm %r" % (IGEMM_ONLY_CASES[case],))
     print("igemm 32-channel case %d max err/tol %.3f plan %s" % (case, r, G.gconv_get_plan(d)))
+
+
+CHUNKED_CASES = [
+    # groups of 8k input channels that are not 32k, or more than 16 output
+    # channels over narrow inputs: the M-tiled implicit GEMM walks K in
+    # 8-channel chunks across taps
+    (3, "bf16", 1, 4, 16, 32, (4, 6, 7), (3, 3, 3), 1, 1, 1, True),          # 16 in / 32 out, 3D
+    (2, "f16", 2, 3, 24, 24, (1, 13, 11), (1, 3, 3), 2, 1, 1, True),         # 24-channel groups, stride 2
+    (2, "bf16", 3, 5, 8, 32, (1, 9, 10), (1, 1, 1), 2, 0, 1, False),         # 1x1 stride 2, one chunk per tap
+    (2, "f16", 1, 2, 40, 48, (1, 10, 9), (1, 5, 3), 1, (0, 2, 2), (1, 1, 2), True),  # 5x3, width dilation
+    (3, "f16", 1, 2, 56, 112, (3, 5, 6), (3, 3, 3), 1, 1, (2, 1, 1), True),  # 112 of a 128-channel tile
+    (2, "bf16", 2, 7, 16, 12, (1, 8, 8), (1, 3, 3), 1, 1, 1, True),          # 12 output channels, odd G
+    (2, "bf16", 3, 4, 24, 24, (1, 28, 28), (1, 3, 3), 1, 1, 1, False),       # many M tiles, ragged tail
+]
+
+
+@pytest.mark.parametrize("case", range(len(CHUNKED_CASES)))
+def test_igemm_chunked_k_every_tile(case):
+    """Every tile of the implicit GEMM's menu on group widths outside the
+    32-channel grid, element by element against the oracle."""
+    nd, dt, N, Gr, Cpg, Kpg, sp, fl, s, pd, dl, bias = CHUNKED_CASES[case]
+    tr = lambda v: (v if isinstance(v, tuple) else (v, v, v))
+    st, pad, dil = tr(s), tr(pd), tr(dl)
+    if nd == 2:
+        st, pad, dil = (1, st[1], st[2]), (0, pad[1], pad[2]), (1, dil[1], dil[2])
+    p = inputs.Problem(nd, dt, N, Gr, Gr * Cpg, Gr * Kpg, sp, fl, st, pad, dil, bias)
+    d = G.desc_from_problem(p)
+    assert G.gconv_select_path(d) == G.GCONV_PATH_IGEMM
+    t = inputs.make_tensors(p, 7700 + case)
+    sa, pa, da = p.spatial_args()
+    ref, scale = oracle.conv_fwd(*U.oracle_inputs(p, t), p.G, sa, pa, da)
+    x, w, b = U.device_tensors(p, t)
+    n, picked = G.gconv_tile_count(d, G.GCONV_PATH_IGEMM)
+    assert n >= 2
+    for tile in range(n):
+        y = poisoned_out(p)
+        rc = G.gconv_fwd_tile(d, G.GCONV_PATH_IGEMM, tile, x.data_ptr(), w.data_ptr(),
+                              b.data_ptr() if b is not None else None, y.data_ptr(),
+                              torch.cuda.current_stream().cuda_stream)
+        assert rc == 0, G.gconv_status_str(rc)
+        torch.cuda.synchronize()
+        r = U.check(U.to_f64(y), ref, scale, p.dtype, "chunked case %d tile %d" % (case, tile))
+    y = run_and_fetch(p, t)
+    U.check(y, ref, scale, p.dtype, "chunked case %d auto" % case)
+    print("igemm chunked case %d: %d tiles (own %d), last max err/tol %.3f plan %s"
+          % (case, n, picked, r, G.gconv_get_plan(d)))
 
 
 @pytest.mark.parametrize("name,N", [("grouped2d_resnext_bf16", 1), ("grouped3d_f16_n1", 1)])

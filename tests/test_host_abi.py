@@ -428,3 +428,29 @@ def test_tile_menus():
     assert G.gconv_fwd_tile(d, G.GCONV_PATH_SMALLG, n, 256, 256, None, 512) == G.GCONV_ERR_BAD_PATH
     # the plan of the own pick does not depend on a tile choice made before
     assert G.gconv_get_plan(d) == G.gconv_get_plan(d, G.gconv_select_path(d))
+
+
+def test_half_type_groups_off_the_32_channel_grid_take_the_implicit_gemm():
+    # widths of 8k input / 4k output channels that neither the small-group nor
+    # the halo kernels take run the M-tiled implicit GEMM (K walked in chunks)
+    for nd, Cpg, Kpg, G_ in ((3, 16, 32, 32), (2, 24, 24, 16), (2, 40, 48, 4), (2, 56, 56, 8),
+                             (2, 16, 12, 7), (2, 8, 32, 16)):
+        sp, fl = ((8, 14, 14), (3, 3, 3)) if nd == 3 else ((28, 28), (3, 3))
+        one = (1,) * nd
+        d = G.make_desc(nd, "bf16", 4, G_, G_ * Cpg, G_ * Kpg, sp, fl, one, one, one)
+        assert G.gconv_path_name(G.gconv_select_path(d)) == "igemm_mfma", (nd, Cpg, Kpg)
+        n, pk = G.gconv_tile_count(d, G.GCONV_PATH_IGEMM)
+        assert n >= 2 and 0 <= pk < n
+    # channel counts off the 8-channel grid stay off the matrix cores
+    d = G.make_desc(2, "bf16", 4, 8, 8 * 12, 8 * 32, (28, 28), (3, 3), (1, 1), (1, 1), (1, 1))
+    assert G.gconv_path_supported(d, G.GCONV_PATH_IGEMM) == 0
+    # the large-group workloads keep their 32-channel tile menu (BN x KT dividing Kpg x Cpg)
+    d = G.desc_from_problem(inputs.WORKLOADS["grouped2d_large_bf16"].problem)
+    assert G.gconv_tile_count(d, G.GCONV_PATH_IGEMM)[0] == 6
+
+
+def test_generic_kernel_splits_long_reductions_of_small_outputs():
+    # 200k outputs of 1728-long reductions: 8 threads per output (the 4th tile)
+    d = G.make_desc(3, "f32", 1, 8, 512, 512, (4, 28, 28), (3, 3, 3), (2, 2, 2), (1, 1, 1), (1, 1, 1))
+    assert G.gconv_path_name(G.gconv_select_path(d)) == "generic"
+    assert G.gconv_tile_count(d, G.GCONV_PATH_GENERIC) == (5, 3)
