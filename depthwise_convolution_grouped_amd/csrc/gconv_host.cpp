@@ -318,8 +318,11 @@ bool path_ok(const Problem &p, int path)
 // more than one tap on 2D images, on 3D planes of up to 16 x 16 pixels and
 // wherever its whole-box variant covers the problem in one round of
 // workgroups; the M-tiled one measured faster elsewhere (the tile sweep: 3D
-// planes of 28 x 28 and 56 x 56 in several rounds, stride 2, 1 x 1 windows).  A 1 x 1 window over groups
-// of fewer than 8 input channels measured faster on the VALU kernel.
+// planes of 28 x 28 and 56 x 56 in several rounds, stride 2, 1 x 1
+// windows).  A 1 x 1 window over groups of fewer than 8 input channels
+// measured faster on the VALU kernel, and a dilated window over small groups
+// that only the halo-box variant of the small-group kernel takes measured
+// faster on the M-tiled implicit GEMM (1.1-1.5x on 8-channel groups).
 bool halo_pays(const Problem &p)
 {
     if (p.sd != 1 || p.sh != 1 || p.sw != 1 || p.taps() == 1) return false;
@@ -337,6 +340,8 @@ int select(const Problem &p)
         if (ighalo::supported(p)) return GCONV_PATH_IGHALO;
     }
     if (p.taps() == 1 && p.Cpg < 8 && direct::preferred(p)) return GCONV_PATH_DIRECT;
+    const bool dilated = p.dd > 1 || p.dh > 1 || p.dw > 1;
+    if (dilated && !smallg::streams(p) && igemm::supported(p)) return GCONV_PATH_IGEMM;
     if (smallg::supported(p)) return GCONV_PATH_SMALLG;
     if (ighalo::supported(p)) return GCONV_PATH_IGHALO;
     if (igemm::supported(p)) return GCONV_PATH_IGEMM;

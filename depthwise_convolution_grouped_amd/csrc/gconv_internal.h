@@ -91,6 +91,8 @@ hipError_t launch(const Problem &p, const Args &a, hipStream_t s);
 namespace smallg {
 int tiles(const Problem &p, int *picked);
 bool supported(const Problem &p);
+// whether a row-walking variant (LDS ring or row streaming) takes the problem
+bool streams(const Problem &p);
 gconv_plan plan(const Problem &p);
 hipError_t launch(const Problem &p, const Args &a, hipStream_t s);
 }

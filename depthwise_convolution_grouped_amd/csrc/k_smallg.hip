@@ -410,6 +410,13 @@ bool supported(const Problem &p)
     return shape_ok(p) && configure(p, c);
 }
 
+bool streams(const Problem &p)
+{
+    RingConfig gc;
+    RowConfig rc;
+    return shape_ok(p) && (ring_configure(p, gc) || rows_configure(p, rc));
+}
+
 int tiles(const Problem &p, int *picked)
 {
     Choice m[4];

@@ -454,3 +454,14 @@ def test_generic_kernel_splits_long_reductions_of_small_outputs():
     d = G.make_desc(3, "f32", 1, 8, 512, 512, (4, 28, 28), (3, 3, 3), (2, 2, 2), (1, 1, 1), (1, 1, 1))
     assert G.gconv_path_name(G.gconv_select_path(d)) == "generic"
     assert G.gconv_tile_count(d, G.GCONV_PATH_GENERIC) == (5, 3)
+
+
+def test_dilated_small_groups_without_a_row_variant_take_the_implicit_gemm():
+    # 8-channel groups, 3x3 dilation 2: only the small-group halo box would
+    # take it, and the chunked implicit GEMM measured faster
+    d = G.make_desc(2, "bf16", 11, 32, 256, 256, (28, 28), (3, 3), (1, 1), (2, 2), (2, 2))
+    assert G.gconv_path_name(G.gconv_select_path(d)) == "igemm_mfma"
+    assert G.gconv_path_supported(d, G.GCONV_PATH_SMALLG) == 1
+    # the same without dilation streams rows on the small-group kernel
+    d = G.make_desc(2, "bf16", 11, 32, 256, 256, (28, 28), (3, 3), (1, 1), (1, 1), (1, 1))
+    assert G.gconv_path_name(G.gconv_select_path(d)) == "smallg_mfma"
