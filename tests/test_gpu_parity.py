@@ -335,6 +335,36 @@ def test_igemm_shapes(case, path):
     print("%s case %d max err/tol %.3f plan %s" % (path, case, r, G.gconv_get_plan(d, pid)))
 
 
+@pytest.mark.parametrize("case", range(len(IGEMM_CASES)))
+def test_halo_every_variant(case):
+    """Every variant of the halo implicit GEMM's menu (whole box, chunk
+    streaming, warp-specialised whole box) that takes the shape matches the
+    oracle element by element."""
+    nd, dt, N, Gr, Cpg, Kpg, sp, fl, s, pd, dl, bias = IGEMM_CASES[case]
+    tr = lambda v: (v if isinstance(v, tuple) else (v, v, v))
+    st, pad, dil = tr(s), tr(pd), tr(dl)
+    if nd == 2:
+        st, pad, dil = (1, st[1], st[2]), (0, pad[1], pad[2]), (1, dil[1], dil[2])
+    p = inputs.Problem(nd, dt, N, Gr, Gr * Cpg, Gr * Kpg, sp, fl, st, pad, dil, bias)
+    d = G.desc_from_problem(p)
+    if G.gconv_path_supported(d, G.GCONV_PATH_IGHALO) != 1:
+        pytest.skip("the halo path does not take this shape")
+    t = inputs.make_tensors(p, 7000 + case)
+    sa, pa, da = p.spatial_args()
+    ref, scale = oracle.conv_fwd(*U.oracle_inputs(p, t), p.G, sa, pa, da)
+    x, w, b = U.device_tensors(p, t)
+    n, _ = G.gconv_tile_count(d, G.GCONV_PATH_IGHALO)
+    for tile in range(n):
+        y = poisoned_out(p)
+        rc = G.gconv_fwd_tile(d, G.GCONV_PATH_IGHALO, tile, x.data_ptr(), w.data_ptr(),
+                              b.data_ptr() if b is not None else None, y.data_ptr(),
+                              torch.cuda.current_stream().cuda_stream)
+        assert rc == 0, G.gconv_status_str(rc)
+        torch.cuda.synchronize()
+        r = U.check(U.to_f64(y), ref, scale, p.dtype, "halo case %d tile %d" % (case, tile))
+        print("halo case %d tile %d/%d max err/tol %.3f" % (case, tile, n, r))
+
+
 IGEMM_ONLY_CASES = [
     # groups of 32 output channels: only the M-tiled implicit GEMM takes them (32-channel tiles)
     (2, "bf16", 4, 8, 32, 32, (1, 28, 28), (1, 3, 3), 1, 1, 1, True),
