@@ -326,16 +326,16 @@ def bench_bwd_weight(a, G, torch):
     ds = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
     avg_ms = sum(ds) / len(ds)
     r = metrics.rates(p, avg_ms * 1e-3)
+    # stage 1 runs on the matrix cores for half types (the implicit GEMM over
+    # output pixels) and on the vector ALUs for fp32; stage 2 is a short fp32 sum
     peak_tf = metrics.PEAK_TFLOPS["f32_vector"] if p.dtype == "f32" else metrics.PEAK_TFLOPS[p.dtype]
-    # the reduction runs on the vector ALUs (fp32 FMA) whatever the element type
-    alu_peak = metrics.PEAK_TFLOPS["f32_vector"]
     ai = metrics.flops(p) / metrics.total_bytes(p)
-    if ai < alu_peak * 1e12 / (metrics.PEAK_HBM_GBS * 1e9):
+    if ai < peak_tf * 1e12 / (metrics.PEAK_HBM_GBS * 1e9):
         roof = {"bound": "hbm", "achieved": r["gbs"], "peak": metrics.PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": r["frac_hbm"]}
     else:
-        roof = {"bound": "alu", "achieved": r["tflops"], "peak": alu_peak, "unit": "TFLOP/s",
-                "frac": r["tflops"] / alu_peak}
+        roof = {"bound": "alu" if p.dtype == "f32" else "mfma", "achieved": r["tflops"], "peak": peak_tf,
+                "unit": "TFLOP/s", "frac": r["tflops"] / peak_tf}
     route = "two-stage reduction (%d B of partial sums)" % need if need else "one-stage reduction"
     roof.update({"traffic": stored_traffic("bwd_weight:" + name, "bwd_weight"),
                  "kernel": "bwd_weight (%s)" % route, "workload": name,
