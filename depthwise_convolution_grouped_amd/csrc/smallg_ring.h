@@ -198,23 +198,28 @@ __global__ __launch_bounds__(kBlock) void ring_kernel(RingParams q, const T *__r
 #pragma unroll
         for (int j = 0; j < NTW; ++j) acc[o][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // stores issued at step st (compile time): the flush of the output row
-    // completed at step st - 1, 16 * kStageChunks / kBlock per wave
-    auto stores_at = [](int st) constexpr {
-        return (st >= 3 && (st - 3) % S == 0 && (st - 3) / S < R) ? (16 * kStageChunks + kBlock - 1) / kBlock : 0;
+    // flushes issued at step st (compile time): the output row completed at
+    // step st - 1.  A flush's 16 * kStageChunks stores go to threads in order,
+    // so this wave issues one store instruction per pass of 256 threads that
+    // reaches its first lane, and none when the row has fewer stores than the
+    // waves before it have lanes (3D rings of 8-chunk pixels: 128 stores).
+    auto flushes_at = [](int st) constexpr {
+        return (st >= 3 && (st - 3) % S == 0 && (st - 3) / S < R) ? 1 : 0;
     };
+    constexpr int kFlushStores = 16 * kStageChunks;
+    const int wave_stores = kFlushStores > wave * 64 ? (kFlushStores - wave * 64 + kBlock - 1) / kBlock : 0;
     static_for(std::make_integer_sequence<int, NI>{}, [&](auto ic) __attribute__((always_inline)) {
         constexpr int i = decltype(ic)::value;
         // this wave's DMAs of row i are done when only later rows' DMAs and
         // the stores issued since remain: rows i+1 .. i+PF-1 and the stores
         // of steps i-PF .. i-1
         constexpr int later_rows = (i + PF - 1 < NI - 1 ? i + PF - 1 : NI - 1) - i;
-        constexpr int later_stores = [=]() constexpr {
+        constexpr int later_flushes = [=]() constexpr {
             int n = 0;
-            for (int k = i - PF; k < i; ++k) n += k >= 0 ? stores_at(k) : 0;
+            for (int k = i - PF; k < i; ++k) n += k >= 0 ? flushes_at(k) : 0;
             return n;
         }();
-        vm_wait(later_rows * nins + later_stores);
+        vm_wait(later_rows * nins + later_flushes * wave_stores);
         __syncthreads();
         // the slot of row i + PF was last read at step i - 1: refill it
         if constexpr (i + PF < NI) issue_row(i + PF);

@@ -437,6 +437,27 @@ def test_igemm_chunked_k_every_tile(case):
           % (case, n, picked, r, G.gconv_get_plan(d)))
 
 
+def test_ring_3d_with_fewer_stores_than_lanes():
+    """3D ring of 8-chunk pixels (2 merged 8/8 groups per tile, one tile per
+    wave): a staged output row is 128 stores for 256 threads, so two waves
+    issue none.  Their wait for a ring row must not count stores they did
+    not issue (it once let them pass the barrier with their row loads in
+    flight).  Several launches, each element by element."""
+    p = inputs.conv3d("bf16", 4, 8, 64, 64, 8, 40, 56, 3, 3, 3, 1, 1)
+    d = G.desc_from_problem(p)
+    assert G.gconv_select_path(d) == G.GCONV_PATH_SMALLG
+    assert G.gconv_get_plan(d)["groups_per_tile"] == 2
+    t = inputs.make_tensors(p, 7900)
+    sa, pa, da = p.spatial_args()
+    ref, scale = oracle.conv_fwd(*U.oracle_inputs(p, t), p.G, sa, pa, da)
+    x, w, b = U.device_tensors(p, t)
+    for rep in range(6):
+        y = U.run(p, x, w, b, out=poisoned_out(p))
+        torch.cuda.synchronize()
+        r = U.check(U.to_f64(y), ref, scale, p.dtype, "3D ring launch %d" % rep)
+    print("3D ring, 8-chunk pixels: 6 launches, last max err/tol %.3f, plan %s" % (r, G.gconv_get_plan(d)))
+
+
 @pytest.mark.parametrize("name,N", [("grouped2d_resnext_bf16", 1), ("grouped3d_f16_n1", 1)])
 def test_nonfinite_input_stays_in_its_merged_tile(name, N):
     """One Inf in one group's input.  The generic path keeps it inside that
