@@ -320,9 +320,13 @@ bool path_ok(const Problem &p, int path)
 // workgroups; the M-tiled one measured faster elsewhere (the tile sweep: 3D
 // planes of 28 x 28 and 56 x 56 in several rounds, stride 2, 1 x 1
 // windows).  A 1 x 1 window over groups of fewer than 8 input channels
-// measured faster on the VALU kernel, and a dilated window over small groups
-// that only the halo-box variant of the small-group kernel takes measured
-// faster on the M-tiled implicit GEMM (1.1-1.5x on 8-channel groups).
+// measured faster on the VALU kernel.  Small groups that only the halo-box
+// variant of the small-group kernel takes measured faster on the M-tiled
+// implicit GEMM when the window is dilated (1.1-1.5x on 8-channel groups) or
+// has at most 4 taps, where the box's halo load and staging outweigh its
+// reuse (1.7-2.4x on 8- and 16-channel groups with 1x1, 1x2 and 2x2
+// windows: the residue classes of a stride-2 backward data); with 25 taps
+// the box won by 2-3x.
 bool halo_pays(const Problem &p)
 {
     if (p.sd != 1 || p.sh != 1 || p.sw != 1 || p.taps() == 1) return false;
@@ -341,7 +345,7 @@ int select(const Problem &p)
     }
     if (p.taps() == 1 && p.Cpg < 8 && direct::preferred(p)) return GCONV_PATH_DIRECT;
     const bool dilated = p.dd > 1 || p.dh > 1 || p.dw > 1;
-    if (dilated && !smallg::streams(p) && igemm::supported(p)) return GCONV_PATH_IGEMM;
+    if ((dilated || p.taps() <= 4) && !smallg::streams(p) && igemm::supported(p)) return GCONV_PATH_IGEMM;
     if (smallg::supported(p)) return GCONV_PATH_SMALLG;
     if (ighalo::supported(p)) return GCONV_PATH_IGHALO;
     if (igemm::supported(p)) return GCONV_PATH_IGEMM;
@@ -471,6 +475,167 @@ size_t weight_bytes(const gconv_desc *d)
            (size_t)(d->C / d->G) * (size_t)elem_size(d->dtype);
 }
 
+// ---- backward data at stride > 1: the polyphase route
+//
+// Per axis, the dx positions i = r + s m of residue class r receive the taps
+// t with (t dil - r - pad) divisible by s: the progression t0 + j s' (s' =
+// s / gcd(dil, s), J terms), which read dy at m - q0 - j dil' (q0 = (t0 dil -
+// r - pad) / s, dil' = dil / gcd(dil, s)).  Taken in reverse order that is a
+// stride-1 forward convolution of dy at dilation dil' under leading pad
+// q0 + (J - 1) dil', whose outputs are the class's ceil((in - r) / s)
+// positions.  Each combination of the axes' classes is one forward launch
+// (the forward dispatcher on the class's problem, weights transformed into
+// the workspace) into a dense buffer, and one scatter of it into dx; a
+// combination with no tap on some axis scatters zeros.
+struct AxisPhase {
+    int t0, st, J, M, P, dl;
+};
+
+int gcd_int(int a, int b)
+{
+    while (b) {
+        const int t = a % b;
+        a = b;
+        b = t;
+    }
+    return a;
+}
+
+AxisPhase axis_phase(int k, int s, int dil, int pad, int r, int in)
+{
+    AxisPhase a{};
+    const int g = gcd_int(dil, s);
+    a.st = s / g;
+    a.dl = dil / g;
+    a.M = r < in ? (in - r + s - 1) / s : 0;
+    // the taps of the class form one residue class modulo s / gcd(dil, s),
+    // so the first of them, if any, is below that
+    a.t0 = -1;
+    for (int t = 0; t < k && t < a.st; ++t)
+        if (((t * dil - r - pad) % s + s) % s == 0) {
+            a.t0 = t;
+            break;
+        }
+    if (a.t0 < 0) {
+        a.t0 = 0;
+        a.J = 0;
+        return a;
+    }
+    a.J = (k - 1 - a.t0) / a.st + 1;
+    a.P = (a.t0 * dil - r - pad) / s + (a.J - 1) * a.dl;   // an exact division
+    return a;
+}
+
+struct BwdPhase {
+    bwd::PhaseTaps taps;
+    int r[3], M[3], P[3], dl[3];
+    bool any;        // every axis has a tap
+    size_t w_off;    // the class's weights in the workspace
+};
+
+constexpr int kMaxPhases = 64;
+
+size_t round256(size_t v) { return (v + 255) / 256 * 256; }
+
+// The classes of a strided backward data and the workspace they need
+// (transformed weights, then the dense buffer of the largest class); false
+// where the route does not apply: stride 1, depthwise problems (their
+// channel-vector direct kernel is faster), more than kMaxPhases classes, or
+// tensors that would need more than one launch.
+bool bwd_phases(const Problem &p, BwdPhase *ph, int *nph, size_t *w_bytes, size_t *tmp_bytes)
+{
+    const int st[3] = {p.sd, p.sh, p.sw}, kk[3] = {p.Z, p.Y, p.X}, dl[3] = {p.dd, p.dh, p.dw};
+    const int pd[3] = {p.pd, p.ph, p.pw}, in[3] = {p.D, p.H, p.W};
+    if (st[0] == 1 && st[1] == 1 && st[2] == 1) return false;
+    if (p.Cpg == 1 && p.Kpg == 1) return false;
+    const long long n = (long long)st[0] * st[1] * st[2];
+    if (n > kMaxPhases) return false;
+    const long long es = elem_size(p.dtype);
+    if ((long long)p.N * p.D * p.H * p.W * p.C() * es >= kLim ||
+        (long long)p.N * p.Do * p.Ho * p.Wo * p.K() * es >= kLim)
+        return false;
+    size_t wb = 0, tb = 0;
+    int cnt = 0;
+    for (int r0 = 0; r0 < st[0]; ++r0)
+        for (int r1 = 0; r1 < st[1]; ++r1)
+            for (int r2 = 0; r2 < st[2]; ++r2) {
+                BwdPhase &f = ph[cnt++];
+                const int r[3] = {r0, r1, r2};
+                f.any = true;
+                long long taps = 1, pix = 1;
+                for (int a = 0; a < 3; ++a) {
+                    const AxisPhase x = axis_phase(kk[a], st[a], dl[a], pd[a], r[a], in[a]);
+                    f.taps.t0[a] = x.t0;
+                    f.taps.st[a] = x.st;
+                    f.taps.J[a] = x.J;
+                    f.r[a] = r[a];
+                    f.M[a] = x.M;
+                    f.P[a] = x.P;
+                    f.dl[a] = x.dl;
+                    f.any = f.any && x.J > 0;
+                    taps *= x.J;
+                    pix *= x.M;
+                }
+                f.w_off = wb;
+                if (f.any) wb += round256((size_t)(p.G * (long long)p.Kpg * p.Cpg * taps * es));
+                const size_t cls = (size_t)(p.N * pix * p.C() * es);
+                if (f.any && round256(cls) > tb) tb = round256(cls);
+            }
+    *nph = cnt;
+    *w_bytes = wb;
+    *tmp_bytes = tb;
+    return true;
+}
+
+// The forward problem computing class f: input dy, output the class's dense
+// positions, the class's sub-kernel at stride 1.
+Problem phase_problem(const Problem &p, const BwdPhase &f)
+{
+    Problem t = p;
+    t.Cpg = p.Kpg;
+    t.Kpg = p.Cpg;
+    t.D = p.Do; t.H = p.Ho; t.W = p.Wo;
+    t.Z = f.taps.J[0]; t.Y = f.taps.J[1]; t.X = f.taps.J[2];
+    t.Do = f.M[0]; t.Ho = f.M[1]; t.Wo = f.M[2];
+    t.sd = t.sh = t.sw = 1;
+    t.pd = f.P[0]; t.ph = f.P[1]; t.pw = f.P[2];
+    t.dd = f.dl[0]; t.dh = f.dl[1]; t.dw = f.dl[2];
+    return t;
+}
+
+int run_bwd_polyphase(const Problem &p, const BwdPhase *ph, int nph, size_t w_bytes, const void *dy,
+                      const void *w, void *dx, void *ws, hipStream_t s)
+{
+    char *wsb = (char *)ws;
+    void *tmp = wsb + w_bytes;
+    for (int i = 0; i < nph; ++i)
+        if (ph[i].any && bwd::launch_phase_flip(p, ph[i].taps, w, wsb + ph[i].w_off, s) != hipSuccess)
+            return GCONV_ERR_LAUNCH;
+    for (int i = 0; i < nph; ++i) {
+        const BwdPhase &f = ph[i];
+        if ((long long)f.M[0] * f.M[1] * f.M[2] == 0) continue;
+        if (f.any) {
+            const Problem t = phase_problem(p, f);
+            const int pth = launch_path(t, GCONV_PATH_AUTO, dy, wsb + f.w_off, nullptr, tmp);
+            if (pth < 0) return pth;
+            Args a{dy, wsb + f.w_off, nullptr, tmp};
+            const int rc = launch_problem(t, pth, a, s);
+            if (rc != GCONV_OK) return rc;
+        }
+        bwd::PhaseScatter q{};
+        q.N = p.N; q.D = p.D; q.H = p.H; q.W = p.W;
+        for (int a = 0; a < 3; ++a) {
+            q.M[a] = f.M[a];
+            q.r[a] = f.r[a];
+        }
+        q.s[0] = p.sd; q.s[1] = p.sh; q.s[2] = p.sw;
+        q.cv = p.C();
+        q.zero = f.any ? 0 : 1;
+        if (bwd::launch_phase_scatter(q, elem_size(p.dtype), tmp, dx, s) != hipSuccess) return GCONV_ERR_LAUNCH;
+    }
+    return GCONV_OK;
+}
+
 int run_bwd_data(const gconv_desc *d, const void *dy, const void *w, void *dx, void *ws,
                  size_t ws_bytes, bool direct, void *stream)
 {
@@ -481,6 +646,14 @@ int run_bwd_data(const gconv_desc *d, const void *dy, const void *w, void *dx, v
     const uintptr_t es = (uintptr_t)elem_size(d->dtype);
     if (!aligned(dy, es) || !aligned(w, es) || !aligned(dx, es)) return GCONV_ERR_MISALIGNED;
     hipStream_t s = (hipStream_t)stream;
+    if (!direct && ws && aligned(ws, 16)) {
+        const Problem whole = to_problem(d, out);
+        BwdPhase ph[kMaxPhases];
+        int nph = 0;
+        size_t wb = 0, tb = 0;
+        if (bwd_phases(whole, ph, &nph, &wb, &tb) && ws_bytes >= wb + tb)
+            return run_bwd_polyphase(whole, ph, nph, wb, dy, w, dx, ws, s);
+    }
     const bool route = !direct && bwd_as_forward(d) && ws && ws_bytes >= weight_bytes(d) && aligned(ws, 16);
     if (route) {
         Problem whole = to_problem(d, out);
@@ -713,7 +886,11 @@ GCONV_API int gconv_bwd_data_workspace(const gconv_desc *d, size_t *bytes)
     int64_t out[3];
     int rc = check_desc(d, out);
     if (rc != GCONV_OK) return rc;
-    *bytes = bwd_as_forward(d) ? weight_bytes(d) : 0;
+    BwdPhase ph[kMaxPhases];
+    int nph = 0;
+    size_t wb = 0, tb = 0;
+    if (bwd_phases(to_problem(d, out), ph, &nph, &wb, &tb)) *bytes = wb + tb;
+    else *bytes = bwd_as_forward(d) ? weight_bytes(d) : 0;
     return GCONV_OK;
 }
 

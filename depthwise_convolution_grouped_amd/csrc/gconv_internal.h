@@ -130,6 +130,22 @@ hipError_t launch(const Problem &p, const Args &a, hipStream_t s);
 namespace bwd {
 hipError_t launch_direct(const Problem &p, const void *dy, const void *w, void *dx, hipStream_t s);
 hipError_t launch_flip(const Problem &p, const void *w, void *wt, hipStream_t s);
+// One residue class of a strided backward data: per axis the taps
+// t0 + j st (j < J) of the original filter.
+struct PhaseTaps {
+    int t0[3], st[3], J[3];
+};
+// Its placement in dx: dx extents D, H, W; class extents M; residues r;
+// strides s; channels per pixel cv (the launcher turns it into units);
+// zero: write zeros instead of the class's values.
+struct PhaseScatter {
+    int N, D, H, W;
+    int M[3], r[3], s[3];
+    int cv, zero;
+    long long total;
+};
+hipError_t launch_phase_flip(const Problem &p, const PhaseTaps &ph, const void *w, void *wt, hipStream_t s);
+hipError_t launch_phase_scatter(PhaseScatter q, int elem, const void *src, void *dx, hipStream_t s);
 }
 
 // Backward weight (k_bwd_weight.hip).  `p` is the forward problem of one

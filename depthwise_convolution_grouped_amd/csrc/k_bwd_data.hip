@@ -20,7 +20,16 @@
 //     C and K exchanged (wt[g][c][Z-1-z][Y-1-y][X-1-x][k] = w[g][k][z][y][x][c]:
 //     reversing the flat tap index reverses all three axes)
 //     under padding dil (k - 1) - pad, so the host runs this transform into
-//     a caller workspace and then the forward dispatcher.
+//     a caller workspace and then the forward dispatcher;
+//   - the two kernels of the strided (polyphase) route: at stride s > 1 the
+//     dx positions of one residue class r (i = r + s m per axis) receive only
+//     the taps t with (t dil - r - pad) divisible by s, which form the
+//     progression t0, t0 + s', ... (s' = s / gcd(dil, s)); in m they are a
+//     stride-1 convolution of dy with that sub-kernel, reversed and with C and
+//     K exchanged, at dilation dil / gcd(dil, s).  phase_flip_kernel writes
+//     one class's sub-kernel, the forward dispatcher computes the class into
+//     a dense buffer, and phase_scatter_kernel places it (or zeros, for a
+//     class no tap reaches) at its positions of dx.
 #include "device_common.h"
 #include "gconv_internal.h"
 
@@ -237,6 +246,93 @@ hipError_t launch_direct(const Problem &p, const void *dy, const void *w, void *
     case GCONV_F16: return go<_Float16>(p, dy, w, dx, s);
     default: return go<__bf16>(p, dy, w, dx, s);
     }
+}
+
+namespace {
+
+template <typename U>
+__global__ __launch_bounds__(kBlock) void phase_flip_kernel(Problem p, PhaseTaps ph, const U *__restrict__ w,
+                                                            U *__restrict__ wt)
+{
+    __shared__ U tile[32][33];
+    const int T = p.Z * p.Y * p.X;
+    const int Tp = ph.J[0] * ph.J[1] * ph.J[2];
+    const int nct = (p.Cpg + 31) / 32;
+    const int gt = blockIdx.x / nct;            // g * Tp + destination tap
+    const int g = gt / Tp, tp = gt - g * Tp;
+    // destination tap (jz, jy, jx), x fastest; its source tap runs backwards
+    // through the class's progression on every axis
+    const int jx = tp % ph.J[2], jy = (tp / ph.J[2]) % ph.J[1], jz = tp / (ph.J[2] * ph.J[1]);
+    const int sz = ph.t0[0] + (ph.J[0] - 1 - jz) * ph.st[0];
+    const int sy = ph.t0[1] + (ph.J[1] - 1 - jy) * ph.st[1];
+    const int sx = ph.t0[2] + (ph.J[2] - 1 - jx) * ph.st[2];
+    const int ts = (sz * p.Y + sy) * p.X + sx;
+    const int c0 = (blockIdx.x - gt * nct) * 32, k0 = blockIdx.y * 32;
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 32 x 8 threads
+    const U *src = w + ((size_t)g * p.Kpg * T + ts) * p.Cpg;  // + k * T * Cpg + c
+#pragma unroll
+    for (int j = 0; j < 32; j += 8) {
+        const int k = k0 + ty + j, c = c0 + tx;
+        if (k < p.Kpg && c < p.Cpg) tile[ty + j][tx] = src[(size_t)k * T * p.Cpg + c];
+    }
+    __syncthreads();
+    U *dst = wt + ((size_t)g * p.Cpg * Tp + tp) * p.Kpg;     // + c * Tp * Kpg + k
+#pragma unroll
+    for (int j = 0; j < 32; j += 8) {
+        const int c = c0 + ty + j, k = k0 + tx;
+        if (c < p.Cpg && k < p.Kpg) dst[(size_t)c * Tp * p.Kpg + k] = tile[tx][ty + j];
+    }
+}
+
+// dx[n][r0 + s0 m0][r1 + s1 m1][r2 + s2 m2][v] = src[n][m0][m1][m2][v] (v: a
+// channel unit, 16 bytes when the channels allow), or 0 for a class no tap
+// reaches.
+template <typename U>
+__global__ __launch_bounds__(kBlock) void phase_scatter_kernel(PhaseScatter q, const U *__restrict__ src,
+                                                               U *__restrict__ dx)
+{
+    const long long i = (long long)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= q.total) return;
+    long long r = i / q.cv;
+    const int v = (int)(i - r * q.cv);
+    const int m2 = (int)(r % q.M[2]); r /= q.M[2];
+    const int m1 = (int)(r % q.M[1]); r /= q.M[1];
+    const int m0 = (int)(r % q.M[0]);
+    const int n = (int)(r / q.M[0]);
+    const int z = q.r[0] + q.s[0] * m0, y = q.r[1] + q.s[1] * m1, x = q.r[2] + q.s[2] * m2;
+    const size_t o = ((((size_t)n * q.D + z) * q.H + y) * q.W + x) * q.cv + v;
+    if (q.zero) dx[o] = U{};
+    else dx[o] = src[i];
+}
+
+}  // namespace
+
+hipError_t launch_phase_flip(const Problem &p, const PhaseTaps &ph, const void *w, void *wt, hipStream_t s)
+{
+    const int Tp = ph.J[0] * ph.J[1] * ph.J[2];
+    const dim3 grid((unsigned)((long long)p.G * Tp * ((p.Cpg + 31) / 32)), (p.Kpg + 31) / 32, 1);
+    Args a{};
+    if (elem_size(p.dtype) == 4)
+        return enqueue(phase_flip_kernel<uint32_t>, grid, dim3(kBlock), 0, s, a, p, ph, (const uint32_t *)w,
+                       (uint32_t *)wt);
+    return enqueue(phase_flip_kernel<uint16_t>, grid, dim3(kBlock), 0, s, a, p, ph, (const uint16_t *)w,
+                   (uint16_t *)wt);
+}
+
+hipError_t launch_phase_scatter(PhaseScatter q, int elem, const void *src, void *dx, hipStream_t s)
+{
+    // 16-byte units when a pixel's channels are whole units and both buffers are aligned
+    const long long bytes = (long long)q.cv * elem;   // q.cv holds the channels on entry
+    const bool vec = bytes % 16 == 0 && ((uintptr_t)src & 15) == 0 && ((uintptr_t)dx & 15) == 0;
+    const int unit = vec ? 16 : elem;
+    q.cv = (int)(bytes / unit);
+    q.total = (long long)q.N * q.M[0] * q.M[1] * q.M[2] * q.cv;
+    if (q.total == 0) return hipSuccess;
+    const dim3 grid((unsigned)((q.total + kBlock - 1) / kBlock));
+    Args a{};
+    if (unit == 16) return enqueue(phase_scatter_kernel<uint4>, grid, dim3(kBlock), 0, s, a, q, (const uint4 *)src, (uint4 *)dx);
+    if (unit == 4) return enqueue(phase_scatter_kernel<uint32_t>, grid, dim3(kBlock), 0, s, a, q, (const uint32_t *)src, (uint32_t *)dx);
+    return enqueue(phase_scatter_kernel<uint16_t>, grid, dim3(kBlock), 0, s, a, q, (const uint16_t *)src, (uint16_t *)dx);
 }
 
 hipError_t launch_flip(const Problem &p, const void *w, void *wt, hipStream_t s)

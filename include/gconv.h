@@ -237,16 +237,24 @@ int gconv_fwd_timed(const gconv_desc *d, int path, const void *x, const void *w,
  */
 
 /* Bytes of device workspace gconv_bwd_data can use for d (0 when it has no
- * use for any): at stride 1 with dil*(k-1) >= pad on every axis it is the
- * size of w, and the call becomes a weight transform plus one forward
- * launch on the fastest forward path. */
+ * use for any):
+ *  - at stride 1 with dil*(k-1) >= pad on every axis, the size of w: the call
+ *    becomes a weight transform plus one forward launch on the fastest
+ *    forward path;
+ *  - at a stride above 1, for groups other than depthwise, whose tensors fit
+ *    one launch: the weights of every residue class of dx (per axis the dx
+ *    positions i = r + stride*m receive only the taps t with (t*dil - r - pad)
+ *    divisible by the stride, a stride-1 convolution of dy), each rounded up
+ *    to 256 bytes, plus a dense buffer for the largest class; the call then
+ *    runs per class a weight transform, one forward launch on the fastest
+ *    forward path and a scatter into dx (zeros for a class no tap reaches). */
 int gconv_bwd_data_workspace(const gconv_desc *d, size_t *bytes);
 
 /* Backward data, asynchronous on `stream`.  `workspace` (device memory the
  * caller owns, 16-byte aligned, may be NULL) of `workspace_bytes`: when it
- * holds gconv_bwd_data_workspace bytes, two kernels run (the weight
- * transform into the workspace, then the forward kernel); otherwise one
- * direct kernel runs.  Tensors too large for one launch are split as in
+ * holds gconv_bwd_data_workspace bytes, the workspace route runs (at stride
+ * 1 the weight transform and the forward kernel; at larger strides three
+ * kernels per residue class); otherwise one direct kernel runs.  Tensors too large for one launch are split as in
  * gconv_fwd: whole images, else slices of dx along the outermost spatial
  * axis, each with the dy slices that reach it.  The workspace may be reused
  * once the stream has passed the call.  Deterministic from run to run.

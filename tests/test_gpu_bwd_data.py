@@ -5,8 +5,10 @@ forward contract with scale = sum |dy * w| over the terms of each dx element:
     fp32:       |dx_gpu - dx| <= 1e-5 * scale
     fp16/bf16:  |dx_gpu - dx| <= 4e-3 * scale + 1e-6
 
-Both routes are checked on every case: the stride-1 route (weight transform
-into a workspace, then the forward dispatcher on the transposed problem) and
+Both routes are checked on every case: the workspace route (at stride 1 a
+weight transform and the forward dispatcher on the transposed problem; at
+larger strides, for groups other than depthwise, one stride-1 forward launch
+per residue class of dx on its reversed sub-kernel, scattered into dx) and
 the direct kernel.  Inputs are seeded and synthetic: w as the forward
 workloads draw it, dy ~ N(0, 1).
 """
@@ -71,6 +73,13 @@ CASES = [
     (2, "f32", 2, 12, 12, 12, (11, 10), (3, 3), 2, 1, 2),       # depthwise fp32, channel vectors of 4
     (3, "bf16", 1, 24, 24, 24, (5, 9, 8), (3, 3, 3), 2, 1, 1),  # depthwise 3D stride 2, vectors of 8
     (2, "f16", 1, 20, 20, 20, (9, 9), (3, 3), 2, 1, 1),         # depthwise, C not a multiple of 8: scalar
+    # strided, grouped: residue classes of dx on the forward kernels
+    (2, "bf16", 2, 4, 512, 512, (14, 13), (3, 3), 2, 1, 1),     # large groups: the classes on the halo / M-tiled GEMMs
+    (2, "bf16", 2, 32, 256, 256, (15, 14), (3, 3), 2, 1, 1),    # ResNeXt-like 8/8 groups, stride 2
+    (2, "bf16", 1, 8, 64, 64, (13, 11), (3, 3), 2, 2, 2),       # stride 2 with dilation 2: one class per axis takes every tap
+    (2, "f16", 1, 2, 32, 32, (17, 15), (3, 3), 4, 0, 1),        # stride 4 > window: classes no tap reaches are zero
+    (2, "f16", 2, 8, 128, 64, (12, 13), (5, 5), 3, 2, 1),       # stride 3, 5x5
+    (3, "bf16", 1, 4, 64, 128, (5, 7, 6), (3, 3, 3), 2, 1, 1),  # 3D stride 2: 8 classes
 ]
 
 

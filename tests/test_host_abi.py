@@ -220,8 +220,14 @@ def test_bwd_data_workspace_sizes():
     assert G.gconv_bwd_data_workspace(d) == 32 * 3 * 3 * 16 * 2
     d = G.make_desc(3, "f32", 1, 2, 4, 6, (5, 6, 7), (3, 1, 3), (1, 1, 1), (1, 0, 2), (1, 1, 1))
     assert G.gconv_bwd_data_workspace(d) == 6 * 3 * 1 * 3 * 2 * 4
-    # a stride above 1, or a pad beyond the dilated filter, has no use for one
+    # stride 2, groups other than depthwise: the residue classes' reversed
+    # sub-kernels (1x1, 1x2, 2x1, 2x2 of 8 x 8 channels, each rounded to 256
+    # bytes) and a dense buffer for the largest class (5 x 5 pixels of 8)
     d = G.make_desc(2, "f16", 1, 1, 8, 8, (9, 9), (3, 3), (2, 2), (1, 1), (1, 1))
+    assert G.gconv_bwd_data_workspace(d) == 256 + 256 + 256 + 512 + 512
+    # depthwise at stride 2 runs its channel-vector direct kernel, and a pad
+    # beyond the dilated filter has no use for one
+    d = G.make_desc(2, "f16", 1, 16, 16, 16, (9, 9), (3, 3), (2, 2), (1, 1), (1, 1))
     assert G.gconv_bwd_data_workspace(d) == 0
     d = G.make_desc(2, "f16", 1, 1, 8, 8, (9, 9), (3, 3), (1, 1), (3, 3), (1, 1))
     assert G.gconv_bwd_data_workspace(d) == 0
