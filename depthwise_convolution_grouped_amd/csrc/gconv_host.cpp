@@ -322,7 +322,8 @@ bool path_ok(const Problem &p, int path)
 // windows).  A 1 x 1 window over groups of fewer than 8 input channels
 // measured faster on the VALU kernel.  Small groups that only the halo-box
 // variant of the small-group kernel takes measured faster on the M-tiled
-// implicit GEMM when the window is dilated (1.1-1.5x on 8-channel groups) or
+// implicit GEMM when a window of at most 9 taps is dilated (1.1-1.5x on
+// 8-channel groups; a dilated 3x3x3 window measured faster on the box) or it
 // has at most 4 taps, where the box's halo load and staging outweigh its
 // reuse (1.7-2.4x on 8- and 16-channel groups with 1x1, 1x2 and 2x2
 // windows: the residue classes of a stride-2 backward data); with 25 taps
@@ -330,7 +331,15 @@ bool path_ok(const Problem &p, int path)
 bool halo_pays(const Problem &p)
 {
     if (p.sd != 1 || p.sh != 1 || p.sw != 1 || p.taps() == 1) return false;
-    return p.ndim == 2 || (long long)p.Ho * p.Wo <= 256 || ighalo_box::supported(p);
+    if (p.ndim == 2) {
+        // the box's extra pixels against the window's reuse: a 7x7 image
+        // under a dilated 3x3 window (121 box pixels for 49 outputs, 9 taps)
+        // ran 1.3-1.4x faster on M tiles, the same box under a dilated 5x5
+        // window (25 taps) 1.3-2.9x faster on the halo kernel
+        const long long box = (long long)(p.Ho + p.dh * (p.Y - 1)) * (p.Wo + p.dw * (p.X - 1));
+        return 4 * box <= (long long)p.taps() * p.Ho * p.Wo;
+    }
+    return (long long)p.Ho * p.Wo <= 256 || ighalo_box::supported(p);
 }
 
 int select(const Problem &p)
@@ -345,7 +354,8 @@ int select(const Problem &p)
     }
     if (p.taps() == 1 && p.Cpg < 8 && direct::preferred(p)) return GCONV_PATH_DIRECT;
     const bool dilated = p.dd > 1 || p.dh > 1 || p.dw > 1;
-    if ((dilated || p.taps() <= 4) && !smallg::streams(p) && igemm::supported(p)) return GCONV_PATH_IGEMM;
+    if (((dilated && p.taps() <= 9) || p.taps() <= 4) && !smallg::streams(p) && igemm::supported(p))
+        return GCONV_PATH_IGEMM;
     if (smallg::supported(p)) return GCONV_PATH_SMALLG;
     if (ighalo::supported(p)) return GCONV_PATH_IGHALO;
     if (igemm::supported(p)) return GCONV_PATH_IGEMM;

@@ -129,12 +129,29 @@ int kb_menu(const Problem &p, int *kb)
     return n;
 }
 
+long long threads_at(const Problem &p, int KB)
+{
+    return (long long)p.N * p.Do * p.Ho * ((p.Wo + kPW - 1) / kPW) * p.G * (p.Kpg / KB);
+}
+
+// own pick: the widest channel block of at least 4 that still leaves
+// kMinThreads threads (the tile sweep: a large-group fp32 problem of few
+// pixels ran 8x faster on 4-channel blocks than on the generic kernel it
+// fell to with 8; with 1- or 2-channel blocks the generic kernel's split
+// reductions measured slightly faster)
+int own_kb(const Problem &p, const int *kb, int n)
+{
+    for (int i = 0; i < n; ++i)
+        if (kb[i] >= 4 && threads_at(p, kb[i]) >= kMinThreads) return i;
+    return 0;
+}
+
 void configure(const Problem &p, Config &c)
 {
     int kb[4];
     const int n = kb_menu(p, kb);
     const int t = tile_choice();
-    c.KB = t >= 0 && t < n ? kb[t] : kb[0];
+    c.KB = t >= 0 && t < n ? kb[t] : kb[own_kb(p, kb, n)];
     c.VC = p.Cpg % 4 == 0 ? 4 : 1;
     c.nkb = p.Kpg / c.KB;
     c.nwb = (p.Wo + kPW - 1) / kPW;
@@ -176,16 +193,20 @@ bool supported(const Problem &p)
 int tiles(const Problem &p, int *picked)
 {
     int kb[4];
-    *picked = 0;
-    return kb_menu(p, kb);
+    const int n = kb_menu(p, kb);
+    *picked = own_kb(p, kb, n);
+    return n;
 }
 
 // Whether the dispatcher should prefer this path over the generic kernel:
 // enough threads to fill the chip with register-blocked work.
 bool preferred(const Problem &p)
 {
+    const int saved = tile_choice();
+    tile_choice() = -1;
     Config c;
     configure(p, c);
+    tile_choice() = saved;
     return c.threads >= kMinThreads && c.threads < (1LL << 31);
 }
 

@@ -310,8 +310,7 @@ int menu(const Problem &p, int (*m)[2])
 // Own pick (from the tile sweep).  Wide groups: the widest output-channel
 // tile with 32-channel reduction steps (half the LDS, more workgroups
 // resident); with fewer 128-channel tiles than CUs, 64-channel tiles with
-// 64-channel steps; 64-channel tiles take 64-channel steps while there are
-// fewer than two per CU.  Other widths: the widest tile that pads Kpg no more
+// 64-channel steps; with fewer than two tiles per CU, 64-channel steps.  Other widths: the widest tile that pads Kpg no more
 // than 32-channel tiles do, with 32-channel steps.
 void own_pick(const Problem &p, long long mt, Config &c)
 {
@@ -319,10 +318,14 @@ void own_pick(const Problem &p, long long mt, Config &c)
     if (wide(p)) {
         c.BN = p.Kpg % 128 == 0 ? 128 : (p.Kpg % 64 == 0 ? 64 : 32);
         const long long tiles = mt * (p.Kpg / c.BN) * p.G;
-        if (c.BN == 128 && tiles < 256 && p.Cpg % 64 == 0) {
+        if (p.ndim == 3) {
+            // 27-tap windows: 128-channel tiles with 64-channel steps below
+            // four tiles per CU (1.1-1.2x over the 2D choices in the sweep)
+            if (tiles < 1024 && p.Cpg % 64 == 0) c.KT = 64;
+        } else if (c.BN == 128 && tiles < 256 && p.Cpg % 64 == 0) {
             c.BN = 64;
             c.KT = 64;
-        } else if (c.BN == 64 && tiles < 512 && p.Cpg % 64 == 0) {
+        } else if (tiles < 512 && p.Cpg % 64 == 0) {
             c.KT = 64;
         }
         return;

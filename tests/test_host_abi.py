@@ -471,3 +471,22 @@ def test_dilated_small_groups_without_a_row_variant_take_the_implicit_gemm():
     # the same without dilation streams rows on the small-group kernel
     d = G.make_desc(2, "bf16", 11, 32, 256, 256, (28, 28), (3, 3), (1, 1), (1, 1), (1, 1))
     assert G.gconv_path_name(G.gconv_select_path(d)) == "smallg_mfma"
+
+
+def test_selection_rules_from_the_held_out_sweep():
+    # fp32 large groups with few pixels: the register-blocked kernel on
+    # 4-channel blocks (8-channel blocks would leave too few threads)
+    d = G.make_desc(3, "f32", 1, 1, 256, 256, (4, 28, 28), (3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1))
+    assert G.gconv_path_name(G.gconv_select_path(d)) == "direct_valu"
+    assert G.gconv_tile_count(d, G.GCONV_PATH_DIRECT) == (4, 1)
+    # depthwise on 7-row images: runs of 7 rows (none past the image, none ragged)
+    d = G.make_desc(2, "bf16", 256, 384, 384, 384, (7, 7), (3, 3), (1, 1), (1, 1), (1, 1))
+    assert G.gconv_tile_count(d, G.GCONV_PATH_DEPTHWISE)[1] == 1
+    d = G.make_desc(2, "f32", 164, 96, 96, 96, (14, 14), (3, 3), (2, 2), (1, 1), (1, 1))
+    assert G.gconv_tile_count(d, G.GCONV_PATH_DEPTHWISE)[1] == 1
+    # a 7x7 image under a dilation-2 window is mostly halo: M-tiled GEMM
+    d = G.make_desc(2, "f16", 235, 2, 512, 512, (7, 7), (3, 3), (1, 1), (2, 2), (2, 2))
+    assert G.gconv_path_name(G.gconv_select_path(d)) == "igemm_mfma"
+    # the dilation-2 large-group workload keeps the halo kernel (18x18 box for 14x14)
+    d = G.desc_from_problem(inputs.WORKLOADS["grouped2d_large_dil2_bf16"].problem)
+    assert G.gconv_path_name(G.gconv_select_path(d)) == "ighalo_mfma"
