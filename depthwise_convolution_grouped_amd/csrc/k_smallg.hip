@@ -367,7 +367,8 @@ int menu(const Problem &p, Choice *m, int *own)
 {
     int n = 0;
     *own = -1;
-    if (!shape_ok(p)) return 0;
+    // fp32 runs on the ring variant only (16x16x4 MFMAs)
+    if (!shape_ok(p) && p.dtype != GCONV_F32) return 0;
     RingConfig gc;
     if (ring_configure(p, gc)) {
         if (p.ndim == 2 && p.sh == 1) {
@@ -379,6 +380,7 @@ int menu(const Problem &p, Choice *m, int *own)
             *own = 0;
         }
     }
+    if (p.dtype == GCONV_F32) return n;
     RowConfig rc;
     if (rows_configure(p, rc)) {
         if (*own < 0 || (p.ndim == 2 && p.sh == 2)) *own = n;
@@ -407,6 +409,8 @@ Choice choose(const Problem &p)
 bool supported(const Problem &p)
 {
     Config c;
+    RingConfig gc;
+    if (p.dtype == GCONV_F32) return ring_configure(p, gc);
     return shape_ok(p) && configure(p, c);
 }
 
@@ -414,6 +418,7 @@ bool streams(const Problem &p)
 {
     RingConfig gc;
     RowConfig rc;
+    if (p.dtype == GCONV_F32) return ring_configure(p, gc);
     return shape_ok(p) && (ring_configure(p, gc) || rows_configure(p, rc));
 }
 
@@ -470,10 +475,11 @@ hipError_t launch(const Problem &p, const Args &a, hipStream_t s)
     // stages halo boxes
     const Choice ch = choose(p);
     RingConfig gc;
-    if (ch.var == kRing && shape_ok(p) && ring_configure(p, gc)) {
+    if (ch.var == kRing && (shape_ok(p) || p.dtype == GCONV_F32) && ring_configure(p, gc)) {
         ring_set_rows(p, gc, ch.rows);
         return ring_launch(p, gc, a, s);
     }
+    if (p.dtype == GCONV_F32) return hipErrorInvalidValue;
     RowConfig rc;
     if (ch.var == kRows && shape_ok(p) && rows_configure(p, rc)) return rows_launch(p, rc, a, s);
     Config c;

@@ -9,6 +9,10 @@ namespace {
 template <typename T, int S, int R>
 hipError_t ring_go3(const Problem &p, const RingConfig &c, const Args &a, hipStream_t s)
 {
+    if constexpr (sizeof(T) == 4) {
+        // fp32 chunks hold 4 channels: tiles of 4 chunks (16 input channels) too
+        if (c.CH8 == 4) return ring_go4<T, S, R, 4, 1, 1, kRingPF2d>(p, c, a, s);
+    }
     return c.CH8 == 1 ? ring_go4<T, S, R, 1, 4, 1, kRingPF2d>(p, c, a, s)
                       : ring_go4<T, S, R, 2, 2, 1, kRingPF2d>(p, c, a, s);
 }
@@ -31,27 +35,30 @@ bool ring_configure(const Problem &p, RingConfig &c)
     } else if (p.ndim != 2 || p.sh != p.sw || (p.sh != 1 && p.sh != 2)) {
         return false;
     }
-    if (p.dtype != GCONV_F16 && p.dtype != GCONV_BF16) return false;
+    if (p.dtype != GCONV_F16 && p.dtype != GCONV_BF16 && p.dtype != GCONV_F32) return false;
+    const bool f32 = p.dtype == GCONV_F32;
+    const int epc = f32 ? 4 : 8;                           // channels per 16-byte chunk
     if (p.Kpg < 1 || p.Kpg > 16 || 16 % p.Kpg != 0) return false;
     c.GN = 16 / p.Kpg;
-    if (p.G % c.GN != 0 || (c.GN * p.Cpg) % 8 != 0) return false;
-    if (!(p.Cpg == 1 || p.Cpg == 2 || p.Cpg == 4 || p.Cpg % 8 == 0)) return false;
-    c.CH8 = c.GN * p.Cpg / 8;
-    if (c.CH8 != 1 && c.CH8 != 2) return false;
+    if (p.G % c.GN != 0 || (c.GN * p.Cpg) % epc != 0) return false;
+    // a chunk holds whole groups or lies inside one group
+    if (!(p.Cpg == 1 || p.Cpg == 2 || p.Cpg == 4 || p.Cpg % epc == 0)) return false;
+    c.CH8 = c.GN * p.Cpg / epc;
+    if (c.CH8 != 1 && c.CH8 != 2 && !(f32 && c.CH8 == 4)) return false;
     c.NT = p.G / c.GN;
     // ring pixels of 16 chunks (the 2D swizzle's period): NTW = 16 / (4 CH8)
     // tiles per wave; 3D falls back to pixels of 8 chunks when the tiles do
     // not fill 16
     c.NTW = 16 / (kWaves * c.CH8);
     if (c.NT % (kWaves * c.NTW) != 0) {
-        if (!is3) return false;
+        if (!is3 || c.NTW == 1) return false;
         c.NTW /= 2;
         if (c.NT % (kWaves * c.NTW) != 0) return false;
     }
     c.TPB = kWaves * c.NTW;
     c.ntb = c.NT / c.TPB;
     c.DZ = is3 ? 3 : 1;
-    const long long es = 2;
+    const long long es = f32 ? 4 : 2;
     if ((long long)p.D * p.H * p.W * p.C() * es >= (1LL << 31) ||
         (long long)p.Do * p.Ho * p.Wo * p.K() * es >= (1LL << 31))
         return false;
@@ -62,7 +69,7 @@ bool ring_configure(const Problem &p, RingConfig &c)
     if (c.NINS > 8 * kWaves) return false;
     // PF + 1 ring rows, the zero slot, two staging rows of 16 padded pixels
     const int nr = (is3 ? kRingPF3d : kRingPF2d) + 1;
-    c.lds = nr * c.RS * 16 + 16 + 2 * 16 * (c.TPB * 2 * 16 + 16);
+    c.lds = (int)(nr * c.RS * 16 + 16 + 2 * 16 * (c.TPB * es * 16 + 16));
     c.nmt = (p.Wo + 15) / 16;
     if (is3) {
         c.R = 7;                                           // short runs: 3D grids are small
@@ -93,6 +100,7 @@ void ring_set_rows(const Problem &p, RingConfig &c, int R)
 hipError_t ring_launch(const Problem &p, const RingConfig &c, const Args &a, hipStream_t s)
 {
     if (c.DZ == 3) return ring3d_launch(p, c, a, s);
+    if (p.dtype == GCONV_F32) return ring_launch_t<float>(p, c, a, s);
     return p.dtype == GCONV_F16 ? ring_launch_t<_Float16>(p, c, a, s) : ring_launch_t<__bf16>(p, c, a, s);
 }
 

@@ -11,6 +11,9 @@ template <typename T>
 hipError_t ring3d_launch_t(const Problem &p, const RingConfig &c, const Args &a, hipStream_t s)
 {
     constexpr int PF = kRingPF3d;
+    if constexpr (sizeof(T) == 4) {
+        if (c.CH8 == 4) return ring_go4<T, 1, 7, 4, 1, 3, PF>(p, c, a, s);
+    }
     if (c.CH8 == 1)
         return c.NTW == 4 ? ring_go4<T, 1, 7, 1, 4, 3, PF>(p, c, a, s) : ring_go4<T, 1, 7, 1, 2, 3, PF>(p, c, a, s);
     return c.NTW == 2 ? ring_go4<T, 1, 7, 2, 2, 3, PF>(p, c, a, s) : ring_go4<T, 1, 7, 2, 1, 3, PF>(p, c, a, s);
@@ -20,6 +23,7 @@ hipError_t ring3d_launch_t(const Problem &p, const RingConfig &c, const Args &a,
 
 hipError_t ring3d_launch(const Problem &p, const RingConfig &c, const Args &a, hipStream_t s)
 {
+    if (p.dtype == GCONV_F32) return ring3d_launch_t<float>(p, c, a, s);
     return p.dtype == GCONV_F16 ? ring3d_launch_t<_Float16>(p, c, a, s) : ring3d_launch_t<__bf16>(p, c, a, s);
 }
 

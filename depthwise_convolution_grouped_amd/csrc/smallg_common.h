@@ -57,6 +57,25 @@ template <> struct Mfma<__bf16> {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
 };
+// fp32: a 16-byte slice holds 4 channels, and a 16x16x4 MFMA takes one
+// value per lane (row or column lane % 16, k = lane / 16).  Element e of
+// both operands' slices goes to the e-th of four MFMAs, so the four MFMAs
+// together cover the 16 channels of the four lane groups' slices: the K
+// order inside one slice group is permuted the same way on both sides,
+// which leaves the sum unchanged.
+template <> struct Mfma<float> {
+    typedef f32x4 V;
+    static __device__ __forceinline__ f32x4 run(V a, V b, f32x4 c)
+    {
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
+    }
+};
+
+// elements of T in one 16-byte slice
+template <typename T> constexpr int kSliceElems = 16 / (int)sizeof(T);
 
 // The 8 weights of one K slice (8 input channels at one tap) for the output
 // channel of merged-tile row nn: the weight operand is block diagonal, so the
@@ -100,6 +119,43 @@ __device__ __forceinline__ uint4 wslice(const T *wk, int tap, int c8, int gout, 
         raw.w = dwi == 3 ? lo : (dwi == 2 ? hi : 0u);
     }
     return raw;
+}
+
+// fp32: the 4 weights of one K slice (4 input channels at one tap), zero
+// unless they belong to the group gout of the output channel (as above,
+// with 4-channel chunks c4).
+template <int CPGC>
+__device__ __forceinline__ uint4 wslice_f32(const float *wk, int tap, int c4, int gout, Div dCpg, bool live)
+{
+    uint4 raw = make_uint4(0, 0, 0, 0);
+    if constexpr (CPGC >= 4) {
+        // Cpg is a multiple of 4: all 4 channels belong to group (4 c4) / Cpg
+        const int Cpg = dCpg.d;
+        const int gs = fdiv(4 * c4, dCpg);
+        const bool hit = live && gs == gout;
+        const uint4 v = *reinterpret_cast<const uint4 *>(wk + tap * Cpg + (4 * c4 - gs * Cpg));
+        raw.x = hit ? v.x : 0u; raw.y = hit ? v.y : 0u;
+        raw.z = hit ? v.z : 0u; raw.w = hit ? v.w : 0u;
+    } else {
+        // group gout's CPGC (1 or 2) channels sit at e0 = gout * CPGC - 4 c4
+        const int e0 = gout * CPGC - 4 * c4;
+        const bool hit = live && e0 >= 0 && e0 < 4;
+        const unsigned *src = reinterpret_cast<const unsigned *>(wk + tap * CPGC);
+        const unsigned d0 = src[0], d1 = CPGC == 2 ? src[1] : 0u;
+        const unsigned v0 = hit ? d0 : 0u, v1 = hit ? d1 : 0u;
+        raw.x = e0 == 0 ? v0 : 0u;
+        raw.y = e0 == 1 ? v0 : (e0 == 0 ? v1 : 0u);
+        raw.z = e0 == 2 ? v0 : (e0 == 1 ? v1 : 0u);
+        raw.w = e0 == 3 ? v0 : (e0 == 2 ? v1 : 0u);
+    }
+    return raw;
+}
+
+template <typename T, int CPGC>
+__device__ __forceinline__ uint4 weight_slice(const T *wk, int tap, int c, int gout, Div dCpg, bool live)
+{
+    if constexpr (sizeof(T) == 4) return wslice_f32<CPGC>(wk, tap, c, gout, dCpg, live);
+    else return wslice<T, CPGC>(wk, tap, c, gout, dCpg, live);
 }
 
 template <int... Is, class F>

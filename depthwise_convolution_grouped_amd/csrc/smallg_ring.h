@@ -51,6 +51,8 @@ __global__ __launch_bounds__(kBlock) void ring_kernel(RingParams q, const T *__r
                                                       const T *__restrict__ bias, T *__restrict__ y)
 {
     typedef typename Mfma<T>::V V;
+    constexpr unsigned ES = sizeof(T);                 // bytes per element
+    constexpr unsigned EPC = 16 / ES;                  // channels per 16-byte chunk
     extern __shared__ uint4 ring[];
     constexpr int NSL = 3 * CH8;             // K slices of one input row
     constexpr int NSR = (NSL + 3) / 4;       // MFMAs per (input row, tile, window row)
@@ -95,7 +97,7 @@ __global__ __launch_bounds__(kBlock) void ring_kernel(RingParams q, const T *__r
         const int iw = iw0 + pp, id = od - q.pd + dz;
         const int c = cb + (j ^ swz(pp));
         const bool ok = m < nins && dz < DZ && id >= 0 && id < q.D && iw >= 0 && iw < q.W;
-        dcol[m] = ok ? (((unsigned)id * (unsigned)(q.H * q.W) + (unsigned)iw) * (unsigned)q.C + (unsigned)c * 8u) * 2u : kOob;
+        dcol[m] = ok ? (((unsigned)id * (unsigned)(q.H * q.W) + (unsigned)iw) * (unsigned)q.C + (unsigned)c * EPC) * ES : kOob;
     }
     const rsrc_t rs = make_rsrc(x + (size_t)n * q.D * q.H * q.W * q.C, q.img_bytes);
     auto issue_row = [&](int i) __attribute__((always_inline)) {
@@ -128,19 +130,15 @@ __global__ __launch_bounds__(kBlock) void ring_kernel(RingParams q, const T *__r
                     const int k8 = 4 * s2 + kq;
                     const bool live = k8 < NSL;
                     const int dx = live ? k8 / CH8 : 0, c = live ? k8 - (k8 / CH8) * CH8 : 0;
-                    const uint4 raw = wslice<T, CPGC>(wk, live ? (dz * 3 + dy) * 3 + dx : 0, c, gout, q.dCpg, live);
+                    const uint4 raw = weight_slice<T, CPGC>(wk, live ? (dz * 3 + dy) * 3 + dx : 0, c, gout, q.dCpg, live);
                     wfrag[j][dz][dy][s2] = *reinterpret_cast<const V *>(&raw);
                 }
     }
     float bias_v[NTW][4];
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-        uint2 braw = make_uint2(0u, 0u);
-        if (bias) braw = *reinterpret_cast<const uint2 *>(bias + (t0 + j) * 16 + 4 * kq);
-        const T *bel = reinterpret_cast<const T *>(&braw);
+    for (int j = 0; j < NTW; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) bias_v[j][e] = bias ? to_f32(bel[e]) : 0.f;
-    }
+        for (int e = 0; e < 4; ++e) bias_v[j][e] = bias ? to_f32(bias[(t0 + j) * 16 + 4 * kq + e]) : 0.f;
     // LDS byte offset (within a ring row) of the lane's fragment of tile j,
     // slice s2: ring pixel nn S + dx, ring chunk (lt0 + j) CH8 + c, swizzled;
     // a dead slice reads the zero slot
@@ -167,10 +165,10 @@ __global__ __launch_bounds__(kBlock) void ring_kernel(RingParams q, const T *__r
     // which the texture path handles far better.  y is written once and not
     // read back, so the stores are non-temporal (measured a few % faster).
     constexpr int kNonTemporal = 2;
-    constexpr int kStageChunks = kWaves * NTW * 2;           // 16-byte chunks per staged pixel
+    constexpr int kStageChunks = kWaves * NTW * (int)ES;     // 16-byte chunks per staged pixel
     constexpr int kStagePitch = kStageChunks * 16 + 16;      // bytes per staged pixel (padded)
     const unsigned stage_lds = zero_slot + 16u;
-    const unsigned stage_w = (unsigned)(nn * kStagePitch + lt0 * 32 + kq * 8);   // this lane's 8 bytes
+    const unsigned stage_w = (unsigned)(nn * kStagePitch) + (unsigned)lt0 * 16u * ES + (unsigned)kq * 4u * ES;   // this lane's 4 channels
     const auto ry = buf_rsrc(y + ((size_t)n * q.Do + od) * q.Ho * q.Wo * q.K, q.oimg_bytes);
     auto flush = [&](int o, int buf) __attribute__((always_inline)) {
         const unsigned sb = stage_lds + (unsigned)buf * 16u * kStagePitch;
@@ -180,7 +178,7 @@ __global__ __launch_bounds__(kBlock) void ring_kernel(RingParams q, const T *__r
             const uint4 v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(ring) +
                                                             (sb - ring_lds) + pix * kStagePitch + ck * 16);
             const bool ok = ow0 + pix < q.Wo && oh0 + o < q.Ho;
-            const unsigned go = ((unsigned)((oh0 + o) * q.Wo + ow0 + pix) * (unsigned)q.K + (unsigned)(tb * q.TPB * 16)) * 2u +
+            const unsigned go = ((unsigned)((oh0 + o) * q.Wo + ow0 + pix) * (unsigned)q.K + (unsigned)(tb * q.TPB * 16)) * ES +
                                 (unsigned)ck * 16u;
             __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, ry, ok ? go : kOob, 0, kNonTemporal);
         }
@@ -261,7 +259,10 @@ __global__ __launch_bounds__(kBlock) void ring_kernel(RingParams q, const T *__r
                 T ov[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) ov[e] = from_f32<T>(acc[o][j][e] + bias_v[j][e]);
-                *reinterpret_cast<uint2 *>(sb + j * 32) = *reinterpret_cast<const uint2 *>(ov);
+                if constexpr (ES == 4)
+                    *reinterpret_cast<uint4 *>(sb + j * 64) = *reinterpret_cast<const uint4 *>(ov);
+                else
+                    *reinterpret_cast<uint2 *>(sb + j * 32) = *reinterpret_cast<const uint2 *>(ov);
             }
         }
     });
@@ -283,9 +284,9 @@ hipError_t ring_go(const Problem &p, const RingConfig &c, const Args &a, hipStre
     q.IW = c.IW; q.RS = c.RS; q.NINS = c.NINS;
     q.TPB = c.TPB; q.ntb = c.ntb;
     q.nmt = c.nmt; q.nchunk = c.nchunk;
-    q.in_row = (unsigned)((long long)p.W * p.C() * 2);
-    q.img_bytes = (unsigned)((long long)p.D * p.H * p.W * p.C() * 2);
-    q.oimg_bytes = (unsigned)((long long)p.Ho * p.Wo * p.K() * 2);
+    q.in_row = (unsigned)((long long)p.W * p.C() * (long long)sizeof(T));
+    q.img_bytes = (unsigned)((long long)p.D * p.H * p.W * p.C() * (long long)sizeof(T));
+    q.oimg_bytes = (unsigned)((long long)p.Ho * p.Wo * p.K() * (long long)sizeof(T));
     const int blocks = c.blocks;
     auto k = ring_kernel<T, S, R, CH8, NTW, CPGC, DZ, PF>;
     static std::atomic<unsigned long long> lds_set{0};

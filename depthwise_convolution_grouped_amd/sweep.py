@@ -108,6 +108,7 @@ def main(argv=None):
     ap.add_argument("--random", type=int, default=26, help="seeded random shapes added to the fixed ones")
     ap.add_argument("--seed", type=int, default=2024, help="seed of the random shapes")
     ap.add_argument("--random-only", action="store_true", help="the random shapes alone (a held-out set)")
+    ap.add_argument("--dtype", default="", help="only the shapes of this element type (f16, bf16, f32)")
     ap.add_argument("--out", default="")
     a = ap.parse_args(argv)
     import torch
@@ -118,6 +119,8 @@ def main(argv=None):
     G.lib()
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
     shapes = ([] if a.random_only else SHAPES) + random_shapes(a.random, a.seed)
+    if a.dtype:
+        shapes = [(n, p) for n, p in shapes if p.dtype == a.dtype]
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     rows = []

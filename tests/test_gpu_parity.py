@@ -507,19 +507,73 @@ FP32_GROUPED = [
 
 @pytest.mark.parametrize("case", range(len(FP32_GROUPED)))
 def test_fp32_grouped_register_blocked_kernel(case):
-    """fp32 grouped problems on the register-blocked VALU kernel, element by
-    element (ResNeXt-style, large groups with dilation 2, 3D, and a ragged
-    one with 3 channels per group, 5 per output group, stride 2)."""
+    """fp32 grouped problems on the VALU direct path, element by element, on
+    every entry of its tile menu: the per-thread register-blocked kernel and
+    the wave-uniform-weight kernel, each with every channel block
+    (ResNeXt-style, large groups with dilation 2, 3D, and a ragged one with
+    3 channels per group, 5 per output group, stride 2)."""
     p = FP32_GROUPED[case]
     d = G.desc_from_problem(p)
     assert G.gconv_path_supported(d, G.GCONV_PATH_DIRECT) == 1
     t = inputs.make_tensors(p, 77000 + case)
-    y = run_and_fetch(p, t, G.GCONV_PATH_DIRECT)
     st, pd, dl = p.spatial_args()
     ref, scale = oracle.conv_fwd(*U.oracle_inputs(p, t), p.G, st, pd, dl)
+    y = run_and_fetch(p, t, G.GCONV_PATH_DIRECT)
     r = U.check(y, ref, scale, p.dtype, "direct_valu case %d" % case)
     print("direct_valu case %d (auto path %s) max err/tol %.3f"
           % (case, G.gconv_path_name(G.gconv_select_path(d)), r))
+    x, w, b = U.device_tensors(p, t)
+    n, _ = G.gconv_tile_count(d, G.GCONV_PATH_DIRECT)
+    assert n >= 2
+    for tile in range(n):
+        yt = poisoned_out(p)
+        rc = G.gconv_fwd_tile(d, G.GCONV_PATH_DIRECT, tile, x.data_ptr(), w.data_ptr(),
+                              b.data_ptr() if b is not None else None, yt.data_ptr(),
+                              torch.cuda.current_stream().cuda_stream)
+        assert rc == 0, G.gconv_status_str(rc)
+        torch.cuda.synchronize()
+        r = U.check(U.to_f64(yt), ref, scale, p.dtype, "direct_valu case %d tile %d" % (case, tile))
+        print("direct_valu case %d tile %d/%d max err/tol %.3f" % (case, tile, n, r))
+
+
+FP32_RING = [
+    # ndim, N, G, Cpg, Kpg, spatial (D,H,W), stride, bias: fp32 small groups on the LDS ring
+    (2, 2, 32, 8, 8, (1, 56, 56), 1, False),     # ResNeXt-style: 16-channel tiles of 4 fp32 chunks
+    (2, 1, 16, 4, 4, (1, 30, 29), 2, True),      # stride 2, four groups per tile
+    (2, 1, 64, 2, 2, (1, 17, 19), 1, True),      # 2-channel groups, eight per tile
+    (2, 1, 64, 1, 4, (1, 20, 21), 1, False),     # one input channel per group: 1 chunk per tile
+    (2, 2, 8, 8, 16, (1, 14, 14), 1, True),      # one group per tile, two chunks
+    (3, 8, 32, 2, 4, (8, 28, 28), 1, True),      # the 3D grouped shape at N=8, in fp32
+]
+
+
+@pytest.mark.parametrize("case", range(len(FP32_RING)))
+def test_fp32_small_groups_on_the_ring(case):
+    """fp32 small groups on the LDS-ring kernel with 16x16x4 fp32 MFMAs,
+    element by element against the oracle, on every entry of the small-group
+    path's menu."""
+    nd, N, Gr, Cpg, Kpg, sp, s, bias = FP32_RING[case]
+    st = (1, s, s) if nd == 2 else (s, s, s)
+    filt = (1, 3, 3) if nd == 2 else (3, 3, 3)
+    pad = (0, 1, 1) if nd == 2 else (1, 1, 1)
+    p = inputs.Problem(nd, "f32", N, Gr, Gr * Cpg, Gr * Kpg, sp, filt, st, pad, (1, 1, 1), bias)
+    d = G.desc_from_problem(p)
+    assert G.gconv_path_supported(d, G.GCONV_PATH_SMALLG) == 1, "the ring should take %r" % (p,)
+    assert G.gconv_path_name(G.gconv_select_path(d)) == "smallg_mfma"
+    t = inputs.make_tensors(p, 91000 + case)
+    sa, pa, da = p.spatial_args()
+    ref, scale = oracle.conv_fwd(*U.oracle_inputs(p, t), p.G, sa, pa, da)
+    x, w, b = U.device_tensors(p, t)
+    n, _ = G.gconv_tile_count(d, G.GCONV_PATH_SMALLG)
+    for tile in range(n):
+        y = poisoned_out(p)
+        rc = G.gconv_fwd_tile(d, G.GCONV_PATH_SMALLG, tile, x.data_ptr(), w.data_ptr(),
+                              b.data_ptr() if b is not None else None, y.data_ptr(),
+                              torch.cuda.current_stream().cuda_stream)
+        assert rc == 0, G.gconv_status_str(rc)
+        torch.cuda.synchronize()
+        r = U.check(U.to_f64(y), ref, scale, p.dtype, "fp32 ring case %d tile %d" % (case, tile))
+        print("fp32 ring case %d tile %d/%d max err/tol %.3f plan %s" % (case, tile, n, r, G.gconv_get_plan(d)))
 
 
 TILE_CASES = [("depthwise2d_f16", 2), ("depthwise2d_s2_f16", 2), ("grouped2d_resnext_bf16", 2),

@@ -402,13 +402,19 @@ def test_noalloc_entry_validates_before_any_hip_call():
 
 
 def test_fp32_grouped_problems_leave_the_generic_kernel():
-    # fp32 ResNeXt-shaped and large-group problems: the register-blocked VALU kernel
-    for C, G_ in ((256, 32), (1024, 8), (96, 32)):
+    # fp32 small groups whose 16-channel output tiles form 16-byte chunks
+    # (ResNeXt-shaped 8/8, 3-channel groups are not): the LDS ring with fp32
+    # MFMAs, in 2D and 3D
+    d = G.make_desc(2, "f32", 32, 32, 256, 256, (56, 56), (3, 3), (1, 1), (1, 1), (1, 1))
+    assert G.gconv_path_name(G.gconv_select_path(d)) == "smallg_mfma"
+    d = G.make_desc(3, "f32", 8, 32, 64, 128, (8, 28, 28), (3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1))
+    assert G.gconv_path_name(G.gconv_select_path(d)) == "smallg_mfma"
+    # large groups and odd group widths: the VALU direct kernels, the
+    # wave-uniform-weight one for wide groups over many workgroups
+    for C, G_, tile in ((1024, 8, 4), (96, 32, 0)):
         d = G.make_desc(2, "f32", 32, G_, C, C, (56, 56), (3, 3), (1, 1), (1, 1), (1, 1))
         assert G.gconv_path_name(G.gconv_select_path(d)) == "direct_valu"
-    # a 3D fp32 grouped problem as well
-    d = G.make_desc(3, "f32", 8, 32, 64, 128, (8, 28, 28), (3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1))
-    assert G.gconv_path_name(G.gconv_select_path(d)) == "direct_valu"
+        assert G.gconv_tile_count(d, G.GCONV_PATH_DIRECT)[1] == tile
     # too little work to fill the chip: the generic kernel's split reductions
     d = G.desc_from_problem(inputs.WORKLOADS["grouped2d_small_f32"].problem)
     assert G.gconv_path_name(G.gconv_select_path(d)) == "generic"
@@ -478,7 +484,9 @@ def test_selection_rules_from_the_held_out_sweep():
     # 4-channel blocks (8-channel blocks would leave too few threads)
     d = G.make_desc(3, "f32", 1, 1, 256, 256, (4, 28, 28), (3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1))
     assert G.gconv_path_name(G.gconv_select_path(d)) == "direct_valu"
-    assert G.gconv_tile_count(d, G.GCONV_PATH_DIRECT) == (4, 1)
+    # menu: the per-thread kernel with 8/4/2/1-channel blocks, then the
+    # wave-uniform-weight kernel with the same blocks
+    assert G.gconv_tile_count(d, G.GCONV_PATH_DIRECT) == (8, 1)
     # depthwise on 7-row images: runs of 7 rows (none past the image, none ragged)
     d = G.make_desc(2, "bf16", 256, 384, 384, 384, (7, 7), (3, 3), (1, 1), (1, 1), (1, 1))
     assert G.gconv_tile_count(d, G.GCONV_PATH_DEPTHWISE)[1] == 1
