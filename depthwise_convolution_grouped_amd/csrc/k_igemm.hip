@@ -93,17 +93,33 @@ template <> struct Mfma<__bf16> {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
 };
+// fp32: a 16-byte slot holds 4 channels; element e of both operands' slots
+// feeds the e-th of four 16x16x4 MFMAs (k = lane / 16 in each), so the four
+// cover the 16 channels of the lanes' four slots in a permuted order that
+// both operands share.
+template <> struct Mfma<float> {
+    typedef f32x4 V;
+    static __device__ __forceinline__ f32x4 run(V a, V b, f32x4 c)
+    {
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
+    }
+};
 
 // BN: output channels per tile (32, 64 or 128; each of the two waves along
-// N takes BN / 2); KT: K per stage (32 or 64); CHUNKED: K walked in 8-channel
-// chunks across taps (KT does not divide Cpg).
+// N takes BN / 2); KT: K per stage (32 or 64, fp32 16 or 32); CHUNKED: K
+// walked in 16-byte chunks (8 channels, fp32 4) across taps (KT does not
+// divide Cpg).
 template <typename T, int BN, int KT, bool CHUNKED>
 __global__ __launch_bounds__(kBlock) void kernel(Params q, const T *__restrict__ x,
                                                  const T *__restrict__ w,
                                                  const T *__restrict__ bias, T *__restrict__ y)
 {
     typedef typename Mfma<T>::V V;
-    constexpr int RS = KT / 8 + 1;              // 16-byte slots per staged row (one pad)
+    constexpr int EPC = 16 / (int)sizeof(T);    // channels per 16-byte slot
+    constexpr int RS = KT / EPC + 1;            // 16-byte slots per staged row (one pad)
     constexpr int A_SLOTS = BM * RS, B_SLOTS = BN * RS;
     constexpr int A_INSTR = (A_SLOTS + 63) / 64, B_INSTR = (B_SLOTS + 63) / 64;
     constexpr int INSTR = A_INSTR + B_INSTR;    // load instructions per stage (all waves)
@@ -111,7 +127,8 @@ __global__ __launch_bounds__(kBlock) void kernel(Params q, const T *__restrict__
     constexpr int STAGE_BYTES = (A_SLOTS + B_SLOTS) * 16;
     constexpr int WM = BM / 2, WN = BN / 2;     // wave tile
     constexpr int TM = WM / 16, TN = WN / 16;   // MFMA tiles per wave
-    constexpr int KS = KT / 32;                 // MFMA K steps per stage
+    constexpr int KS = KT / (4 * EPC);          // MFMA K steps per stage (four slots each)
+    static_assert(KS >= 1, "a stage holds at least one K step");
     extern __shared__ uint4 lds[];
 
     const int t = threadIdx.x;
@@ -170,7 +187,7 @@ __global__ __launch_bounds__(kBlock) void kernel(Params q, const T *__restrict__
         }
     }
     // issue stage st into buffer b: tap st / (Cpg/KT), channels c0 .. c0+KT-1,
-    // or, chunked, chunks st * KT/8 .. st * KT/8 + KT/8 - 1 of the K walk
+    // or, chunked, chunks st * KT/EPC .. st * KT/EPC + KT/EPC - 1 of the K walk
     const int cstages = CHUNKED ? 1 : q.Cpg / KT;
     auto issue = [&](int st, int b) {
         int tap = st / cstages;
@@ -183,11 +200,11 @@ __global__ __launch_bounds__(kBlock) void kernel(Params q, const T *__restrict__
                 unsigned vo = kOob;
                 bool live = true;
                 if constexpr (CHUNKED) {
-                    // this slot's chunk: its own tap and 8 channels
-                    const int q8 = st * (KT / 8) + ld_slot[i];
+                    // this slot's chunk: its own tap and EPC channels
+                    const int q8 = st * (KT / EPC) + ld_slot[i];
                     live = q8 < q.nq8;
                     tap = fdiv(q8, q.dCH8);
-                    c0 = (q8 - tap * q.dCH8.d) * 8 - ld_slot[i] * 8;
+                    c0 = (q8 - tap * q.dCH8.d) * EPC - ld_slot[i] * EPC;
                     const int t1 = fdiv(tap, q.dX);
                     xx = tap - t1 * q.X;
                     zz = fdiv(t1, q.dY);
@@ -198,10 +215,10 @@ __global__ __launch_bounds__(kBlock) void kernel(Params q, const T *__restrict__
                               iw = ld_pix_w[i] + xx * q.dw;
                     if (id >= 0 && id < q.D && ih >= 0 && ih < q.H && iw >= 0 && iw < q.W)
                         vo = ((unsigned)(((ld_pix_n[i] * q.D + id) * q.H + ih) * q.W + iw) * (unsigned)q.C +
-                              (unsigned)(g * q.Cpg + c0 + ld_slot[i] * 8)) * es;
+                              (unsigned)(g * q.Cpg + c0 + ld_slot[i] * EPC)) * es;
                 } else if (ld_kind[i] == 2 && ld_slot[i] < RS - 1 && ld_wrow[i] >= 0 && live) {
                     vo = ((unsigned)(ld_wrow[i] * taps + tap) * (unsigned)q.Cpg +
-                          (unsigned)(c0 + ld_slot[i] * 8)) * es;
+                          (unsigned)(c0 + ld_slot[i] * EPC)) * es;
                 }
                 if (ld_kind[i] != 0) {
                     // input instructions read through the x buffer, weight ones through w
@@ -259,10 +276,8 @@ __global__ __launch_bounds__(kBlock) void kernel(Params q, const T *__restrict__
         const int ch = n0 + wn + nt * 16 + 4 * kq;            // channel within the group
         float bv[4] = {0.f, 0.f, 0.f, 0.f};
         if (bias && ch < q.Kpg) {
-            const uint2 braw = *reinterpret_cast<const uint2 *>(bias + g * q.Kpg + ch);
-            const T *bel = reinterpret_cast<const T *>(&braw);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) bv[i] = to_f32(bel[i]);
+            for (int i = 0; i < 4; ++i) bv[i] = to_f32(bias[g * q.Kpg + ch + i]);
         }
 #pragma unroll
         for (int mt = 0; mt < TM; ++mt) {
@@ -271,7 +286,10 @@ __global__ __launch_bounds__(kBlock) void kernel(Params q, const T *__restrict__
                 T o[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) o[i] = from_f32<T>(acc[mt][nt][i] + bv[i]);
-                *reinterpret_cast<uint2 *>(y + (size_t)m * q.K + g * q.Kpg + ch) = *reinterpret_cast<const uint2 *>(o);
+                if constexpr (sizeof(T) == 4)
+                    *reinterpret_cast<uint4 *>(y + (size_t)m * q.K + g * q.Kpg + ch) = *reinterpret_cast<const uint4 *>(o);
+                else
+                    *reinterpret_cast<uint2 *>(y + (size_t)m * q.K + g * q.Kpg + ch) = *reinterpret_cast<const uint2 *>(o);
             }
         }
     }
@@ -294,9 +312,11 @@ bool wide(const Problem &p) { return p.Cpg % 32 == 0 && p.Kpg % 32 == 0; }
 int menu(const Problem &p, int (*m)[2])
 {
     const bool wd = wide(p);
+    const bool f32 = p.dtype == GCONV_F32;   // fp32 stages of 32 or 16 channels (twice the bytes)
     int n = 0;
     for (int bn : {128, 64, 32})
-        for (int kt : {64, 32}) {
+        for (int kt0 : {64, 32}) {
+            const int kt = f32 ? kt0 / 2 : kt0;
             const bool ok = wd ? (p.Kpg % bn == 0 && p.Cpg % kt == 0) : (bn == 32 || bn < 2 * p.Kpg);
             if (ok) {
                 m[n][0] = bn;
@@ -312,7 +332,7 @@ int menu(const Problem &p, int (*m)[2])
 // resident); with fewer 128-channel tiles than CUs, 64-channel tiles with
 // 64-channel steps; with fewer than two tiles per CU, 64-channel steps.  Other widths: the widest tile that pads Kpg no more
 // than 32-channel tiles do, with 32-channel steps.
-void own_pick(const Problem &p, long long mt, Config &c)
+void own_pick_half(const Problem &p, long long mt, Config &c)
 {
     c.KT = 32;
     if (wide(p)) {
@@ -339,17 +359,30 @@ void own_pick(const Problem &p, long long mt, Config &c)
         }
 }
 
+void own_pick(const Problem &p, long long mt, Config &c)
+{
+    own_pick_half(p, mt, c);
+    if (p.dtype != GCONV_F32) return;
+    // fp32: stages of half the channels, the same bytes per staged row; with
+    // fewer than 128 tiles, 32-channel tiles for more workgroups (fp32 tile
+    // sweep: 1.3-1.8x on 3D images of one batch)
+    c.KT /= 2;
+    if (mt * ((p.Kpg + c.BN - 1) / c.BN) * p.G < 128) c.BN = 32;
+}
+
 bool configure(const Problem &p, Config &c)
 {
-    if (p.dtype != GCONV_F16 && p.dtype != GCONV_BF16) return false;
-    if (p.Cpg % 8 != 0 || p.Kpg % 4 != 0) return false;
-    const long long xb = (long long)p.N * p.D * p.H * p.W * p.C() * 2;
-    const long long wb = (long long)p.K() * p.taps() * p.Cpg * 2;
+    if (p.dtype != GCONV_F16 && p.dtype != GCONV_BF16 && p.dtype != GCONV_F32) return false;
+    const int epc = p.dtype == GCONV_F32 ? 4 : 8;     // channels per 16-byte slot
+    const long long es = p.dtype == GCONV_F32 ? 4 : 2;
+    if (p.Cpg % epc != 0 || p.Kpg % 4 != 0) return false;
+    const long long xb = (long long)p.N * p.D * p.H * p.W * p.C() * es;
+    const long long wb = (long long)p.K() * p.taps() * p.Cpg * es;
     if (xb >= (1LL << 31) || wb >= (1LL << 31)) return false;
     const long long M = (long long)p.N * p.Do * p.Ho * p.Wo;
     if (M >= (1LL << 31)) return false;
     // the chunk decode divides exactly below 2^16
-    const long long nq8 = (long long)p.taps() * (p.Cpg / 8);
+    const long long nq8 = (long long)p.taps() * (p.Cpg / epc);
     if (nq8 + 8 >= (1LL << 16)) return false;
     const long long mt = (M + BM - 1) / BM;
     own_pick(p, mt, c);
@@ -363,8 +396,8 @@ bool configure(const Problem &p, Config &c)
     c.nq8 = (int)nq8;
     c.mtiles = (int)mt;
     c.ntiles = (p.Kpg + c.BN - 1) / c.BN;
-    c.stages = (int)((nq8 + c.KT / 8 - 1) / (c.KT / 8));
-    const int RS = c.KT / 8 + 1;
+    c.stages = (int)((nq8 + c.KT / epc - 1) / (c.KT / epc));
+    const int RS = c.KT / epc + 1;
     c.lds = 2 * (BM + c.BN) * RS * 16;
     return c.mtiles < (1 << 30) && c.ntiles < 65536 && p.G < 65536;
 }
@@ -380,9 +413,10 @@ hipError_t go4(const Problem &p, const Config &c, const Args &a, hipStream_t s)
     q.dd = p.dd; q.dh = p.dh; q.dw = p.dw;
     q.M = p.N * p.Do * p.Ho * p.Wo;
     q.mtiles = c.mtiles; q.ntiles = c.ntiles; q.stages = c.stages; q.nq8 = c.nq8;
-    q.dCH8 = make_div(p.Cpg / 8); q.dX = make_div(p.X); q.dY = make_div(p.Y);
-    q.x_bytes = (unsigned)((long long)p.N * p.D * p.H * p.W * p.C() * 2);
-    q.w_bytes = (unsigned)((long long)p.K() * p.taps() * p.Cpg * 2);
+    const long long es = (long long)sizeof(T);
+    q.dCH8 = make_div(p.Cpg / (16 / (int)sizeof(T))); q.dX = make_div(p.X); q.dY = make_div(p.Y);
+    q.x_bytes = (unsigned)((long long)p.N * p.D * p.H * p.W * p.C() * es);
+    q.w_bytes = (unsigned)((long long)p.K() * p.taps() * p.Cpg * es);
     auto k = kernel<T, BN, KT, CHUNKED>;
     static std::atomic<unsigned long long> lds_set{0};
     if (c.lds > 64 * 1024) {
@@ -402,9 +436,16 @@ hipError_t go3(const Problem &p, const Config &c, const Args &a, hipStream_t s)
 template <typename T>
 hipError_t go(const Problem &p, const Config &c, const Args &a, hipStream_t s)
 {
-    if (c.BN == 128) return c.KT == 64 ? go3<T, 128, 64>(p, c, a, s) : go3<T, 128, 32>(p, c, a, s);
-    if (c.BN == 64) return c.KT == 64 ? go3<T, 64, 64>(p, c, a, s) : go3<T, 64, 32>(p, c, a, s);
-    return c.KT == 64 ? go3<T, 32, 64>(p, c, a, s) : go3<T, 32, 32>(p, c, a, s);
+    if constexpr (sizeof(T) == 4) {
+        // fp32: stages of 32 or 16 channels
+        if (c.BN == 128) return c.KT == 32 ? go3<T, 128, 32>(p, c, a, s) : go3<T, 128, 16>(p, c, a, s);
+        if (c.BN == 64) return c.KT == 32 ? go3<T, 64, 32>(p, c, a, s) : go3<T, 64, 16>(p, c, a, s);
+        return c.KT == 32 ? go3<T, 32, 32>(p, c, a, s) : go3<T, 32, 16>(p, c, a, s);
+    } else {
+        if (c.BN == 128) return c.KT == 64 ? go3<T, 128, 64>(p, c, a, s) : go3<T, 128, 32>(p, c, a, s);
+        if (c.BN == 64) return c.KT == 64 ? go3<T, 64, 64>(p, c, a, s) : go3<T, 64, 32>(p, c, a, s);
+        return c.KT == 64 ? go3<T, 32, 64>(p, c, a, s) : go3<T, 32, 32>(p, c, a, s);
+    }
 }
 
 }  // namespace
@@ -449,6 +490,7 @@ hipError_t launch(const Problem &p, const Args &a, hipStream_t s)
 {
     Config c;
     if (!configure(p, c)) return hipErrorInvalidValue;
+    if (p.dtype == GCONV_F32) return go<float>(p, c, a, s);
     if (p.dtype == GCONV_F16) return go<_Float16>(p, c, a, s);
     return go<__bf16>(p, c, a, s);
 }

@@ -576,6 +576,45 @@ def test_fp32_small_groups_on_the_ring(case):
         print("fp32 ring case %d tile %d/%d max err/tol %.3f plan %s" % (case, tile, n, r, G.gconv_get_plan(d)))
 
 
+FP32_IGEMM = [
+    # ndim, N, G, Cpg, Kpg, spatial (D,H,W), filt (Z,Y,X), stride, pad, dil, bias
+    (2, 2, 8, 128, 128, (1, 14, 14), (1, 3, 3), 1, 1, 1, True),    # large groups: one tap per stage
+    (2, 3, 4, 64, 64, (1, 28, 27), (1, 3, 3), 2, 1, 1, False),     # stride 2, ragged M
+    (2, 2, 2, 24, 20, (1, 13, 11), (1, 5, 3), 1, (0, 2, 1), 1, True),  # 4-channel chunks across taps, partial N tile
+    (3, 1, 2, 32, 32, (4, 6, 7), (3, 3, 3), 1, 1, 1, True),        # 3D
+    (2, 2, 4, 64, 64, (1, 14, 14), (1, 3, 3), 1, 2, 2, True),      # dilation 2
+    (2, 1, 3, 36, 44, (1, 9, 10), (1, 1, 1), 1, 0, 1, False),      # 1x1, odd widths
+]
+
+
+@pytest.mark.parametrize("case", range(len(FP32_IGEMM)))
+def test_fp32_implicit_gemm_every_tile(case):
+    """fp32 groups of 4k input and output channels on the M-tiled implicit
+    GEMM with 16x16x4 fp32 MFMAs, element by element, on every tile."""
+    nd, N, Gr, Cpg, Kpg, sp, fl, s, pd, dl, bias = FP32_IGEMM[case]
+    tr = lambda v: (v if isinstance(v, tuple) else (v, v, v))
+    st, pad, dil = tr(s), tr(pd), tr(dl)
+    if nd == 2:
+        st, pad, dil = (1, st[1], st[2]), (0, pad[1], pad[2]), (1, dil[1], dil[2])
+    p = inputs.Problem(nd, "f32", N, Gr, Gr * Cpg, Gr * Kpg, sp, fl, st, pad, dil, bias)
+    d = G.desc_from_problem(p)
+    assert G.gconv_path_supported(d, G.GCONV_PATH_IGEMM) == 1, "the implicit GEMM should take %r" % (p,)
+    t = inputs.make_tensors(p, 93000 + case)
+    sa, pa, da = p.spatial_args()
+    ref, scale = oracle.conv_fwd(*U.oracle_inputs(p, t), p.G, sa, pa, da)
+    x, w, b = U.device_tensors(p, t)
+    n, _ = G.gconv_tile_count(d, G.GCONV_PATH_IGEMM)
+    for tile in range(n):
+        y = poisoned_out(p)
+        rc = G.gconv_fwd_tile(d, G.GCONV_PATH_IGEMM, tile, x.data_ptr(), w.data_ptr(),
+                              b.data_ptr() if b is not None else None, y.data_ptr(),
+                              torch.cuda.current_stream().cuda_stream)
+        assert rc == 0, G.gconv_status_str(rc)
+        torch.cuda.synchronize()
+        r = U.check(U.to_f64(y), ref, scale, p.dtype, "fp32 igemm case %d tile %d" % (case, tile))
+        print("fp32 igemm case %d tile %d/%d max err/tol %.3f" % (case, tile, n, r))
+
+
 TILE_CASES = [("depthwise2d_f16", 2), ("depthwise2d_s2_f16", 2), ("grouped2d_resnext_bf16", 2),
               ("grouped3d_f16_n8", 1), ("grouped2d_large_bf16", 2), ("grouped2d_large_dil2_bf16", 1)]
 

@@ -409,12 +409,20 @@ def test_fp32_grouped_problems_leave_the_generic_kernel():
     assert G.gconv_path_name(G.gconv_select_path(d)) == "smallg_mfma"
     d = G.make_desc(3, "f32", 8, 32, 64, 128, (8, 28, 28), (3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1))
     assert G.gconv_path_name(G.gconv_select_path(d)) == "smallg_mfma"
-    # large groups and odd group widths: the VALU direct kernels, the
-    # wave-uniform-weight one for wide groups over many workgroups
-    for C, G_, tile in ((1024, 8, 4), (96, 32, 0)):
-        d = G.make_desc(2, "f32", 32, G_, C, C, (56, 56), (3, 3), (1, 1), (1, 1), (1, 1))
-        assert G.gconv_path_name(G.gconv_select_path(d)) == "direct_valu"
-        assert G.gconv_tile_count(d, G.GCONV_PATH_DIRECT)[1] == tile
+    # groups of 4k channels: the implicit GEMM with fp32 MFMAs; 32-channel
+    # tiles when 128-channel ones would leave fewer than 128 workgroups
+    d = G.make_desc(2, "f32", 32, 8, 1024, 1024, (56, 56), (3, 3), (1, 1), (1, 1), (1, 1))
+    assert G.gconv_path_name(G.gconv_select_path(d)) == "igemm_mfma"
+    d = G.make_desc(3, "f32", 1, 1, 256, 256, (4, 28, 28), (3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1))
+    assert G.gconv_path_name(G.gconv_select_path(d)) == "igemm_mfma"
+    assert G.gconv_get_plan(d)["grid"][1] == 8
+    # odd group widths: the VALU direct kernel; on it, the wave-uniform-weight
+    # variant for wide groups over many workgroups
+    d = G.make_desc(2, "f32", 32, 32, 96, 96, (56, 56), (3, 3), (1, 1), (1, 1), (1, 1))
+    assert G.gconv_path_name(G.gconv_select_path(d)) == "direct_valu"
+    assert G.gconv_tile_count(d, G.GCONV_PATH_DIRECT)[1] == 0
+    d = G.make_desc(2, "f32", 32, 8, 1024, 1024, (56, 56), (3, 3), (1, 1), (1, 1), (1, 1))
+    assert G.gconv_tile_count(d, G.GCONV_PATH_DIRECT)[1] == 4
     # too little work to fill the chip: the generic kernel's split reductions
     d = G.desc_from_problem(inputs.WORKLOADS["grouped2d_small_f32"].problem)
     assert G.gconv_path_name(G.gconv_select_path(d)) == "generic"
@@ -464,8 +472,9 @@ def test_half_type_groups_off_the_32_channel_grid_take_the_implicit_gemm():
 def test_generic_kernel_splits_long_reductions_of_small_outputs():
     # 200k outputs of 1728-long reductions: 8 threads per output (the 4th tile)
     d = G.make_desc(3, "f32", 1, 8, 512, 512, (4, 28, 28), (3, 3, 3), (2, 2, 2), (1, 1, 1), (1, 1, 1))
-    assert G.gconv_path_name(G.gconv_select_path(d)) == "generic"
     assert G.gconv_tile_count(d, G.GCONV_PATH_GENERIC) == (5, 3)
+    # the fp32 implicit GEMM takes it (92 against 128 us in the fp32 sweep)
+    assert G.gconv_path_name(G.gconv_select_path(d)) == "igemm_mfma"
 
 
 def test_dilated_small_groups_without_a_row_variant_take_the_implicit_gemm():
@@ -480,13 +489,14 @@ def test_dilated_small_groups_without_a_row_variant_take_the_implicit_gemm():
 
 
 def test_selection_rules_from_the_held_out_sweep():
-    # fp32 large groups with few pixels: the register-blocked kernel on
-    # 4-channel blocks (8-channel blocks would leave too few threads)
+    # fp32 large groups with few pixels: on the VALU direct path, the
+    # register-blocked kernel on 4-channel blocks (8-channel blocks would
+    # leave too few threads); the menu is the per-thread kernel with
+    # 8/4/2/1-channel blocks, then the wave-uniform-weight kernel with the
+    # same blocks.  The dispatcher sends it to the fp32 implicit GEMM.
     d = G.make_desc(3, "f32", 1, 1, 256, 256, (4, 28, 28), (3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1))
-    assert G.gconv_path_name(G.gconv_select_path(d)) == "direct_valu"
-    # menu: the per-thread kernel with 8/4/2/1-channel blocks, then the
-    # wave-uniform-weight kernel with the same blocks
     assert G.gconv_tile_count(d, G.GCONV_PATH_DIRECT) == (8, 1)
+    assert G.gconv_path_name(G.gconv_select_path(d)) == "igemm_mfma"
     # depthwise on 7-row images: runs of 7 rows (none past the image, none ragged)
     d = G.make_desc(2, "bf16", 256, 384, 384, 384, (7, 7), (3, 3), (1, 1), (1, 1), (1, 1))
     assert G.gconv_tile_count(d, G.GCONV_PATH_DEPTHWISE)[1] == 1
