@@ -368,6 +368,10 @@ void own_pick(const Problem &p, long long mt, Config &c)
     // sweep: 1.3-1.8x on 3D images of one batch)
     c.KT /= 2;
     if (mt * ((p.Kpg + c.BN - 1) / c.BN) * p.G < 128) c.BN = 32;
+    // groups of 32k channels with fewer than 512 tiles: 32-channel stages
+    // (as the half types' 64-channel steps under two tiles per CU; 1.2x on
+    // a 2-group 32/32 problem of 356 tiles)
+    if (wide(p) && c.KT == 16 && p.Cpg % 32 == 0 && mt * ((p.Kpg + c.BN - 1) / c.BN) * p.G < 512) c.KT = 32;
 }
 
 bool configure(const Problem &p, Config &c)
