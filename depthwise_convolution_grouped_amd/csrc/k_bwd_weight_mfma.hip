@@ -60,7 +60,12 @@ constexpr unsigned kOob = 0x80000000u;   // a buffer offset past any tensor: loa
 constexpr int kMaxBoxIns = 16;           // box DMA instructions per wave and step
 constexpr int kMaxDyIns = 8;             // dy-tile DMA instructions per wave and step
 constexpr int kMaxLds = 80 * 1024;       // both buffers: two workgroups per CU
-constexpr int kTargetWaves = 8192;       // about eight waves per CU, two rounds
+// Chunks for one round of 8 waves per CU (two 4-wave workgroups, or one of
+// 8 waves): measured against 512 .. 8192 waves on the ResNeXt-style, 3D
+// 2-in/4-out and large-group shapes, 2048 was fastest on all of them (1.2-1.6x
+// over two rounds: fewer chunks of partial sums for stage 2 and no second,
+// partly filled round)
+constexpr int kTargetWaves = 2048;
 // chunks are also capped so that stage 2 (which reads every chunk's partial
 // sums) moves at most kStage2Share x the bytes of x and dy
 constexpr double kStage2Share = 1.0;
