@@ -9,10 +9,8 @@ namespace {
 template <typename T, int S, int R>
 hipError_t ring_go3(const Problem &p, const RingConfig &c, const Args &a, hipStream_t s)
 {
-    if constexpr (sizeof(T) == 4) {
-        // fp32 chunks hold 4 channels: tiles of 4 chunks (16 input channels) too
-        if (c.CH8 == 4) return ring_go4<T, S, R, 4, 1, 1, kRingPF2d>(p, c, a, s);
-    }
+    // tiles of 4 chunks (fp32 16/16, or 32 input channels per 16 outputs)
+    if (c.CH8 == 4) return ring_go4<T, S, R, 4, 1, 1, kRingPF2d>(p, c, a, s);
     return c.CH8 == 1 ? ring_go4<T, S, R, 1, 4, 1, kRingPF2d>(p, c, a, s)
                       : ring_go4<T, S, R, 2, 2, 1, kRingPF2d>(p, c, a, s);
 }
@@ -44,7 +42,7 @@ bool ring_configure(const Problem &p, RingConfig &c)
     // a chunk holds whole groups or lies inside one group
     if (!(p.Cpg == 1 || p.Cpg == 2 || p.Cpg == 4 || p.Cpg % epc == 0)) return false;
     c.CH8 = c.GN * p.Cpg / epc;
-    if (c.CH8 != 1 && c.CH8 != 2 && !(f32 && c.CH8 == 4)) return false;
+    if (c.CH8 != 1 && c.CH8 != 2 && c.CH8 != 4) return false;
     c.NT = p.G / c.GN;
     // ring pixels of 16 chunks (the 2D swizzle's period): NTW = 16 / (4 CH8)
     // tiles per wave; 3D falls back to pixels of 8 chunks when the tiles do

@@ -11,9 +11,7 @@ template <typename T>
 hipError_t ring3d_launch_t(const Problem &p, const RingConfig &c, const Args &a, hipStream_t s)
 {
     constexpr int PF = kRingPF3d;
-    if constexpr (sizeof(T) == 4) {
-        if (c.CH8 == 4) return ring_go4<T, 1, 7, 4, 1, 3, PF>(p, c, a, s);
-    }
+    if (c.CH8 == 4) return ring_go4<T, 1, 7, 4, 1, 3, PF>(p, c, a, s);
     if (c.CH8 == 1)
         return c.NTW == 4 ? ring_go4<T, 1, 7, 1, 4, 3, PF>(p, c, a, s) : ring_go4<T, 1, 7, 1, 2, 3, PF>(p, c, a, s);
     return c.NTW == 2 ? ring_go4<T, 1, 7, 2, 2, 3, PF>(p, c, a, s) : ring_go4<T, 1, 7, 2, 1, 3, PF>(p, c, a, s);

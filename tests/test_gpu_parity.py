@@ -268,6 +268,8 @@ SMALLG_CASES = [
     (3, "f16", 1, 32, 2, 4, (8, 28, 28), (3, 3, 3), 1, 1, 1, True),     # the 3D workload at N=1
     (3, "bf16", 2, 8, 2, 4, (5, 7, 9), (3, 3, 3), 1, 1, 1, True),
     (3, "f16", 1, 16, 4, 4, (6, 5, 7), (3, 3, 3), 2, 1, 1, True),       # 14 MFMAs per tile
+    (2, "bf16", 2, 32, 4, 2, (1, 20, 21), (1, 3, 3), 1, 1, 1, True),    # ring tiles of 4 chunks (32 in / 16 out)
+    (3, "f16", 16, 32, 4, 2, (8, 14, 14), (3, 3, 3), 1, 1, 1, False),   # the same in 3D (the 3D N=8 shape transposed)
     (3, "bf16", 1, 8, 8, 8, (4, 6, 6), (3, 1, 3), 1, (1, 0, 1), 1, False),
     (3, "f16", 1, 4, 4, 4, (7, 7, 7), (3, 3, 3), 1, 2, 2, True),
 ]
