@@ -352,8 +352,8 @@ hipError_t go(const Problem &p, const Config &c, const Args &a, hipStream_t s)
 
 namespace {
 
-// Tile menu: the LDS ring (rows per workgroup 14 and 28 for 2D stride 1,
-// its own value otherwise), then the row-streaming variant, then the halo
+// Tile menu: the LDS ring (rows per workgroup 14 and 28 for 2D stride 1, 7 and
+// 2 in 3D, its own value otherwise), then the row-streaming variant, then the halo
 // box, each where it takes the problem.  The own pick is the first variant
 // that applies, with the ring's own row count, except at stride 2, where the
 // row-streaming variant measured faster than the ring (tile sweep: 1.2-1.3x
@@ -375,6 +375,10 @@ int menu(const Problem &p, Choice *m, int *own)
             m[n++] = {kRing, 14};
             m[n++] = {kRing, 28};
             *own = gc.R == 28 ? 1 : 0;
+        } else if (p.ndim == 3) {
+            m[n++] = {kRing, 7};
+            m[n++] = {kRing, 2};
+            *own = gc.R == 2 ? 1 : 0;
         } else {
             m[n++] = {kRing, gc.R};
             *own = 0;

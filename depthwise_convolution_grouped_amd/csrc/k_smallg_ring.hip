@@ -70,7 +70,10 @@ bool ring_configure(const Problem &p, RingConfig &c)
     c.lds = (int)(nr * c.RS * 16 + 16 + 2 * 16 * (c.TPB * es * 16 + 16));
     c.nmt = (p.Wo + 15) / 16;
     if (is3) {
-        c.R = 7;                                           // short runs: 3D grids are small
+        // short runs: 3D grids are small; 2-row runs when 7-row ones would
+        // leave fewer workgroups than CUs
+        c.R = 7;
+        if ((long long)c.nmt * ((p.Ho + 6) / 7) * c.ntb * p.Do * p.N < 256) c.R = 2;
     } else {
         // rows per workgroup from {14, 28}: the longer run while the grid still
         // gives every CU two workgroups (long runs amortise the two halo rows);
@@ -81,15 +84,15 @@ bool ring_configure(const Problem &p, RingConfig &c)
     c.nchunk = (p.Ho + c.R - 1) / c.R;
     const long long blocks = (long long)c.nmt * c.nchunk * c.ntb * p.Do * p.N;
     c.blocks = (int)blocks;
-    // a 3D grid of fewer workgroups than CUs is faster as halo boxes (more,
-    // smaller workgroups; measured on the N=1 8x28x28 case)
-    if (is3 && blocks < 256) return false;
+    // a 3D grid of fewer than 128 workgroups is left to the halo boxes
+    if (is3 && blocks < 128) return false;
     return blocks < (1LL << 31);
 }
 
 void ring_set_rows(const Problem &p, RingConfig &c, int R)
 {
-    if (p.ndim != 2 || p.sh != 1 || (R != 14 && R != 28)) return;
+    const bool ok = p.ndim == 2 ? p.sh == 1 && (R == 14 || R == 28) : (R == 2 || R == 7);
+    if (!ok) return;
     c.R = R;
     c.nchunk = (p.Ho + c.R - 1) / c.R;
     c.blocks = (int)((long long)c.nmt * c.nchunk * c.ntb * p.Do * p.N);
