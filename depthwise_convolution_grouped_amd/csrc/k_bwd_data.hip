@@ -178,6 +178,24 @@ __global__ __launch_bounds__(kBlock) void flip_kernel(Problem p, const U *__rest
     }
 }
 
+// The same transform for narrow groups (Cpg or Kpg under 32, where the
+// 32 x 32 tiles would be mostly empty): one thread per element of wt, in wt's
+// order (k fastest), each reading its source element
+template <typename U>
+__global__ __launch_bounds__(kBlock) void flip_small_kernel(Problem p, const U *__restrict__ w, U *__restrict__ wt,
+                                                            int total)
+{
+    const int e = blockIdx.x * kBlock + threadIdx.x;
+    if (e >= total) return;
+    const int T = p.Z * p.Y * p.X;
+    int r = e;
+    const int k = r % p.Kpg;  r /= p.Kpg;
+    const int t = r % T;      r /= T;
+    const int c = r % p.Cpg;
+    const int g = r / p.Cpg;
+    wt[e] = w[(((size_t)g * p.Kpg + k) * T + (T - 1 - t)) * p.Cpg + c];
+}
+
 int lanes_for(const Problem &p, long long elems)
 {
     int L = 1;
@@ -337,6 +355,16 @@ hipError_t launch_phase_scatter(PhaseScatter q, int elem, const void *src, void 
 
 hipError_t launch_flip(const Problem &p, const void *w, void *wt, hipStream_t s)
 {
+    const long long total = (long long)p.G * p.Cpg * p.taps() * p.Kpg;
+    if ((p.Cpg < 32 || p.Kpg < 32) && total < (1LL << 31)) {
+        const dim3 g1((unsigned)((total + kBlock - 1) / kBlock));
+        Args a{};
+        if (elem_size(p.dtype) == 4)
+            return enqueue(flip_small_kernel<uint32_t>, g1, dim3(kBlock), 0, s, a, p, (const uint32_t *)w,
+                           (uint32_t *)wt, (int)total);
+        return enqueue(flip_small_kernel<uint16_t>, g1, dim3(kBlock), 0, s, a, p, (const uint16_t *)w,
+                       (uint16_t *)wt, (int)total);
+    }
     // x: (group, tap, 32-channel tile of c), y: 32-channel tile of k
     const dim3 grid((unsigned)((long long)p.G * p.taps() * ((p.Cpg + 31) / 32)), (p.Kpg + 31) / 32, 1);
     Args a{};
