@@ -508,3 +508,29 @@ def test_selection_rules_from_the_held_out_sweep():
     # the dilation-2 large-group workload keeps the halo kernel (18x18 box for 14x14)
     d = G.desc_from_problem(inputs.WORKLOADS["grouped2d_large_dil2_bf16"].problem)
     assert G.gconv_path_name(G.gconv_select_path(d)) == "ighalo_mfma"
+
+
+def test_ring_tiles_of_four_chunks_and_3d_run_lengths():
+    # half-type groups of 32 input channels per 16-channel output tile
+    # (4-in/2-out; the 3D workload's backward-data problem) stream on the
+    # ring; the menu is 7-row runs, 2-row runs, then the halo box
+    d = G.make_desc(3, "f16", 8, 32, 128, 64, (8, 28, 28), (3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1))
+    assert G.gconv_path_name(G.gconv_select_path(d)) == "smallg_mfma"
+    assert G.gconv_tile_count(d, G.GCONV_PATH_SMALLG) == (3, 0)
+    assert G.gconv_get_plan(d)["grid"][0] == 512
+    # the 3D workload: 7-row runs at N=8 (512 workgroups); at N=1 those
+    # would leave fewer workgroups than CUs, so 2-row runs (224)
+    d8 = G.desc_from_problem(inputs.WORKLOADS["grouped3d_f16_n8"].problem)
+    assert G.gconv_tile_count(d8, G.GCONV_PATH_SMALLG) == (3, 0)
+    assert G.gconv_get_plan(d8)["grid"][0] == 512
+    d1 = G.desc_from_problem(inputs.WORKLOADS["grouped3d_f16_n1"].problem)
+    assert G.gconv_tile_count(d1, G.GCONV_PATH_SMALLG) == (3, 1)
+    assert G.gconv_get_plan(d1)["grid"][0] == 224
+
+
+def test_bwd_weight_chunks_fill_one_round():
+    # ResNeXt-style: 4 tiles of 4-wave workgroups per chunk, 128 chunks =
+    # 512 workgroups, one round at two per CU; the workspace holds 128
+    # chunks of fp32 partial sums of the 32 x 8 x 9 x 8 weights
+    d = G.desc_from_problem(inputs.WORKLOADS["grouped2d_resnext_bf16"].problem)
+    assert G.gconv_bwd_weight_workspace(d) == 128 * (32 * 8 * 9 * 8) * 4
