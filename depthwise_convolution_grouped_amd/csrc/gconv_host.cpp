@@ -669,15 +669,23 @@ int run_bwd_data(const gconv_desc *d, const void *dy, const void *w, void *dx, v
             return run_bwd_polyphase(whole, ph, nph, wb, dy, w, dx, ws, s);
     }
     const bool route = !direct && bwd_as_forward(d) && ws && ws_bytes >= weight_bytes(d) && aligned(ws, 16);
+    // depthwise: the forward kernel reads the windows reversed itself, so no
+    // transformed weight copy is made
+    bool dw_reversed = false;
     if (route) {
-        Problem whole = to_problem(d, out);
-        if (bwd::launch_flip(whole, w, ws, s) != hipSuccess) return GCONV_ERR_LAUNCH;
+        Problem whole = to_problem(d, out), tw;
+        dw_reversed = bwd_forward_problem(whole, tw) && depthwise::supported(tw);
+        if (!dw_reversed && bwd::launch_flip(whole, w, ws, s) != hipSuccess) return GCONV_ERR_LAUNCH;
     }
     return for_bwd_pieces(d, out, [&](const Piece &pc, bool, bool) {
         const void *dyp = (const char *)dy + pc.in_off;
         void *dxp = (char *)dx + pc.out_off;
         Problem t;
-        if (route && bwd_forward_problem(pc.p, t)) {
+        if (route && dw_reversed && bwd_forward_problem(pc.p, t) && depthwise::supported(t)) {
+            Args a{dyp, w, nullptr, dxp};
+            return depthwise::launch_flipped(t, a, s) == hipSuccess ? (int)GCONV_OK : (int)GCONV_ERR_LAUNCH;
+        }
+        if (route && !dw_reversed && bwd_forward_problem(pc.p, t)) {
             const int pth = launch_path(t, GCONV_PATH_AUTO, dyp, ws, nullptr, dxp);
             Args a{dyp, ws, nullptr, dxp};
             return launch_problem(t, pth, a, s);

@@ -87,6 +87,10 @@ int tiles(const Problem &p, int *picked);
 bool supported(const Problem &p);
 gconv_plan plan(const Problem &p);
 hipError_t launch(const Problem &p, const Args &a, hipStream_t s);
+// The same convolution with each channel's window reversed (weight tap t
+// read as tap taps-1-t): backward data at stride 1 without a transformed
+// weight copy.
+hipError_t launch_flipped(const Problem &p, const Args &a, hipStream_t s);
 }
 namespace smallg {
 int tiles(const Problem &p, int *picked);

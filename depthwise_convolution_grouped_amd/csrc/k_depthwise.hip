@@ -67,6 +67,7 @@ struct Params {
     unsigned in_row, out_row;       // bytes of one row of x / of y
     unsigned img_bytes, oimg_bytes; // bytes of one image of x / of y
     unsigned w_bytes, b_bytes;      // bytes of w and of bias (0: no bias)
+    int flip;              // read each channel's window reversed (w[t] as w[8 - t])
 };
 
 template <typename T> struct VecOf { static constexpr int n = 16 / (int)sizeof(T); };
@@ -79,6 +80,38 @@ __device__ __forceinline__ void static_for(std::integer_sequence<int, Is...>, F 
 }
 
 typedef unsigned u4 __attribute__((ext_vector_type(4)));
+
+// The lane's 9 * VEC weights (channel e, tap t at element 9 e + t, VEC
+// channels in nine 16-byte vectors) with every channel's taps reversed:
+// element 9 e + t takes element 9 e + 8 - t.  Indices are compile-time, so
+// this is register moves (and half-word merges for 2-byte types).
+template <typename T>
+__device__ __forceinline__ void reverse_taps(u4 (&w)[9])
+{
+    constexpr int ES = (int)sizeof(T);
+    constexpr int VEC = 16 / ES;
+    auto src_of = [](int k) { return (k / 9) * 9 + 8 - k % 9; };
+    u4 o[9];
+    if constexpr (ES == 4) {
+#pragma unroll
+        for (int k = 0; k < 9 * VEC; ++k) {
+            const int sidx = src_of(k);
+            o[k >> 2][k & 3] = w[sidx >> 2][sidx & 3];
+        }
+    } else {
+        auto half_at = [&](int k) -> unsigned {
+            const unsigned d = w[k >> 3][(k & 7) >> 1];
+            return (k & 1) ? (d >> 16) : (d & 0xffffu);
+        };
+#pragma unroll
+        for (int d = 0; d < 9 * VEC / 2; ++d) {
+            const unsigned lo = half_at(src_of(2 * d)), hi = half_at(src_of(2 * d + 1));
+            o[d >> 2][d & 3] = lo | (hi << 16);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 9; ++i) w[i] = o[i];
+}
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 // acc += a.lo * b.lo + a.hi * b.hi (fp16 pairs, fp32 accumulation)
@@ -163,6 +196,7 @@ __global__ __launch_bounds__(kBlock) void kernel(Params q, const T *__restrict__
     u4 wraw[9];
 #pragma unroll
     for (int i = 0; i < 9; ++i) wraw[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, (unsigned)(cv * 9 + i) * 16u, 0, 0);
+    if (q.flip) reverse_taps<T>(wraw);
     const auto rb = rsrc(bias, q.b_bytes);
     const u4 braw = __builtin_amdgcn_raw_buffer_load_b128(rb, q.b_bytes ? (unsigned)cv * 16u : kOob, 0, 0);
     // weight (e, dy, dx) is element e * 9 + dy * 3 + dx of the lane's 9 * VEC.
@@ -338,9 +372,10 @@ bool configure(const Problem &p, Config &c)
 }
 
 template <typename T, int SH, int DH, int R, int PF>
-hipError_t go4(const Problem &p, const Config &c, const Args &a, hipStream_t s)
+hipError_t go4(const Problem &p, const Config &c, const Args &a, hipStream_t s, bool flip)
 {
     Params q;
+    q.flip = flip ? 1 : 0;
     q.C = p.G; q.Cv = p.G / VecOf<T>::n;
     q.H = p.H; q.W = p.W; q.Ho = p.Ho; q.Wo = p.Wo;
     q.sw = p.sw; q.dw = p.dw; q.ph = p.ph; q.pw = p.pw;
@@ -357,22 +392,34 @@ hipError_t go4(const Problem &p, const Config &c, const Args &a, hipStream_t s)
 }
 
 template <typename T, int R>
-hipError_t go3(const Problem &p, const Config &c, const Args &a, hipStream_t s)
+hipError_t go3(const Problem &p, const Config &c, const Args &a, hipStream_t s, bool flip)
 {
-    if (p.sh == 1) return p.dh == 1 ? go4<T, 1, 1, R, 3>(p, c, a, s) : go4<T, 1, 2, R, 3>(p, c, a, s);
+    if (p.sh == 1)
+        return p.dh == 1 ? go4<T, 1, 1, R, 3>(p, c, a, s, flip) : go4<T, 1, 2, R, 3>(p, c, a, s, flip);
     if constexpr (R <= 14)
-        return p.dh == 1 ? go4<T, 2, 1, R, 3>(p, c, a, s) : go4<T, 2, 2, R, 3>(p, c, a, s);
+        return p.dh == 1 ? go4<T, 2, 1, R, 3>(p, c, a, s, flip) : go4<T, 2, 2, R, 3>(p, c, a, s, flip);
     return hipErrorInvalidValue;   // configure() never picks R > 14 for stride 2
 }
 
 template <typename T>
-hipError_t go(const Problem &p, const Config &c, const Args &a, hipStream_t s)
+hipError_t go(const Problem &p, const Config &c, const Args &a, hipStream_t s, bool flip)
 {
     switch (c.R) {
-    case 4: return go3<T, 4>(p, c, a, s);
-    case 7: return go3<T, 7>(p, c, a, s);
-    case 14: return go3<T, 14>(p, c, a, s);
-    default: return go3<T, 28>(p, c, a, s);
+    case 4: return go3<T, 4>(p, c, a, s, flip);
+    case 7: return go3<T, 7>(p, c, a, s, flip);
+    case 14: return go3<T, 14>(p, c, a, s, flip);
+    default: return go3<T, 28>(p, c, a, s, flip);
+    }
+}
+
+hipError_t launch_as(const Problem &p, const Args &a, hipStream_t s, bool flip)
+{
+    Config c;
+    if (!configure(p, c)) return hipErrorInvalidValue;
+    switch (p.dtype) {
+    case GCONV_F32: return go<float>(p, c, a, s, flip);
+    case GCONV_F16: return go<_Float16>(p, c, a, s, flip);
+    default: return go<__bf16>(p, c, a, s, flip);
     }
 }
 
@@ -409,16 +456,9 @@ gconv_plan plan(const Problem &p)
     return pl;
 }
 
-hipError_t launch(const Problem &p, const Args &a, hipStream_t s)
-{
-    Config c;
-    if (!configure(p, c)) return hipErrorInvalidValue;
-    switch (p.dtype) {
-    case GCONV_F32: return go<float>(p, c, a, s);
-    case GCONV_F16: return go<_Float16>(p, c, a, s);
-    default: return go<__bf16>(p, c, a, s);
-    }
-}
+hipError_t launch(const Problem &p, const Args &a, hipStream_t s) { return launch_as(p, a, s, false); }
+
+hipError_t launch_flipped(const Problem &p, const Args &a, hipStream_t s) { return launch_as(p, a, s, true); }
 
 }  // namespace depthwise
 }  // namespace gconv
