@@ -1,7 +1,9 @@
-// Register-blocked direct kernel on the vector ALUs: the path for grouped
-// problems the matrix-core kernels do not take, above all fp32 (the TileOPs
-// PR 1568 review's grouped kernels and the CK tile engine's datatypes
-// include fp32; CK grouped_conv tile-engine README, Hardware).
+// Register-blocked direct kernels on the vector ALUs: the path for grouped
+// problems the matrix-core kernels do not take (group widths off the
+// 4-channel grid, and what fp32 leaves to it; the TileOPs PR 1568 review's
+// grouped kernels and the CK tile engine's datatypes include fp32; CK
+// grouped_conv tile-engine README, Hardware).  Two kernels: the per-thread
+// one below, and a wave-uniform-weight one further down.
 //
 // A thread owns KB output channels of one group x PW consecutive output
 // pixels of one output row.  For each tap of the window and each vector of

@@ -1,6 +1,7 @@
-// Implicit-GEMM grouped convolution on the matrix cores (fp16 / bf16, 2D and
-// 3D), for groups of 8k input and 4k output channels that the small-group
-// kernels do not take (wider groups, or more output than input channels).
+// Implicit-GEMM grouped convolution on the matrix cores (fp16 / bf16 on
+// 16x16x32 MFMAs, fp32 on four chained 16x16x4 ones; 2D and 3D), for groups
+// of 8k (fp32: 4k) input and 4k output channels that the small-group kernels
+// do not take (wider groups, or more output than input channels).
 //
 // Per group g the convolution is a GEMM: M = output pixels (N * Do * Ho *
 // Wo), N = Kpg output channels, K = taps * Cpg.  The group is the grid's z
@@ -16,6 +17,8 @@
 // slot decodes its own (tap, chunk), and chunks past taps * Cpg/8 are zero.
 // Either way the weight operand of a stage is KT contiguous values of each
 // output channel's GKZYXC row (the B descriptor's channel extent is Cpg).
+// For fp32 a 16-byte slot holds 4 channels, so the chunks above are 4
+// channels and a stage of KT channels has KT / 16 MFMA K steps.
 // Output-channel tiles past Kpg (Kpg not a multiple of BN) read zero weights
 // and store nothing.
 //

@@ -1,7 +1,8 @@
 // Pieces shared by the small-group MFMA kernels (halo box, row streaming,
 // LDS ring): launch shape, buffer descriptors, the direct-to-LDS load, the
-// 16x16x32 MFMA per element type and the block-diagonal weight slice, plus
-// the host entry points of the two row-walking variants.
+// MFMA per element type (16x16x32 for fp16/bf16, four chained 16x16x4 for
+// fp32) and the block-diagonal weight slice, plus the host entry points of
+// the two row-walking variants.
 #pragma once
 
 #include <utility>

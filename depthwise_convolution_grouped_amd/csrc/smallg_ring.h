@@ -12,7 +12,11 @@
 // loads, PF rows ahead, and each wave reads its operand fragments from LDS (a
 // window column is just an address offset).  The accumulators of each output
 // row leave as soon as the row is complete, the workgroup's four waves
-// together writing TPB x 32 contiguous bytes of each pixel.
+// together writing TPB x 16 contiguous output channels of each pixel.
+//
+// fp16/bf16 tiles take 16-byte chunks of 8 channels and 16x16x32 MFMAs; fp32
+// tiles take chunks of 4 channels, each fragment read feeding four chained
+// 16x16x4 fp32 MFMAs (smallg_common.h); byte offsets follow the element size.
 //
 // LDS: slot j (16 bytes) of ring pixel p holds channel chunk j ^ f(p),
 // f(p) = (p / S) mod 16, so the 16 pixels one fragment read touches (p =
@@ -160,8 +164,8 @@ __global__ __launch_bounds__(kBlock) void ring_kernel(RingParams q, const T *__r
     // ---- output.  A completed output row goes through an LDS staging
     // buffer (two, alternating): each lane drops its four channels of pixel
     // nn there, and after the next barrier the workgroup writes the row's 16
-    // pixels x TPB * 32 bytes with one 16-byte store per thread and chunk --
-    // whole TPB * 32-byte pixel runs instead of 8-byte pieces of 16 pixels,
+    // pixels x TPB * 16 channels with one 16-byte store per thread and chunk
+    // -- whole pixel runs instead of 8-byte (fp32: 16-byte) pieces of 16 pixels,
     // which the texture path handles far better.  y is written once and not
     // read back, so the stores are non-temporal (measured a few % faster).
     constexpr int kNonTemporal = 2;

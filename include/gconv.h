@@ -97,13 +97,16 @@ typedef enum gconv_status {
 typedef enum gconv_path {
     GCONV_PATH_AUTO = -1,
     GCONV_PATH_GENERIC = 0,     /* one thread per output, any shape */
-    GCONV_PATH_DEPTHWISE = 1,   /* Cpg = Kpg = 1: LDS halo tile, channel vectors, VALU */
-    GCONV_PATH_SMALLG = 2,      /* small groups: LDS halo tile, block-diagonal MFMA */
-    GCONV_PATH_IGEMM = 3,       /* large groups: M-tiled implicit GEMM, group on grid z, MFMA */
+    GCONV_PATH_DEPTHWISE = 1,   /* Cpg = Kpg = 1: input rows streamed through registers,
+                                   channel vectors, VALU */
+    GCONV_PATH_SMALLG = 2,      /* small groups: LDS row ring or halo box, block-diagonal
+                                   MFMA (fp16/bf16; the ring also fp32) */
+    GCONV_PATH_IGEMM = 3,       /* larger groups: M-tiled implicit GEMM, group on grid z,
+                                   MFMA (fp16/bf16/fp32) */
     GCONV_PATH_IGHALO = 4,      /* large groups: implicit GEMM over an LDS input box per
-                                   output block, persistent, MFMA */
-    GCONV_PATH_DIRECT = 5,      /* register-blocked direct kernel on the vector ALUs
-                                   (fp32 grouped; any shape) */
+                                   output block, persistent, MFMA (fp16/bf16) */
+    GCONV_PATH_DIRECT = 5,      /* register-blocked direct kernels on the vector ALUs
+                                   (group widths no matrix-core path takes; any shape) */
     GCONV_NUM_PATHS = 6
 } gconv_path;
 
