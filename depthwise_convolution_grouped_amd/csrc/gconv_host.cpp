@@ -650,6 +650,14 @@ int run_bwd_polyphase(const Problem &p, const BwdPhase *ph, int nph, size_t w_by
     return GCONV_OK;
 }
 
+// Stride-1 backward data whose transposed problem is depthwise: the forward
+// depthwise kernel reverses the windows itself.
+bool bwd_dw_reversed(const gconv_desc *d, const int64_t *out)
+{
+    Problem t;
+    return bwd_as_forward(d) && bwd_forward_problem(to_problem(d, out), t) && depthwise::supported(t);
+}
+
 int run_bwd_data(const gconv_desc *d, const void *dy, const void *w, void *dx, void *ws,
                  size_t ws_bytes, bool direct, void *stream)
 {
@@ -668,20 +676,20 @@ int run_bwd_data(const gconv_desc *d, const void *dy, const void *w, void *dx, v
         if (bwd_phases(whole, ph, &nph, &wb, &tb) && ws_bytes >= wb + tb)
             return run_bwd_polyphase(whole, ph, nph, wb, dy, w, dx, ws, s);
     }
-    const bool route = !direct && bwd_as_forward(d) && ws && ws_bytes >= weight_bytes(d) && aligned(ws, 16);
     // depthwise: the forward kernel reads the windows reversed itself, so no
-    // transformed weight copy is made
-    bool dw_reversed = false;
-    if (route) {
-        Problem whole = to_problem(d, out), tw;
-        dw_reversed = bwd_forward_problem(whole, tw) && depthwise::supported(tw);
-        if (!dw_reversed && bwd::launch_flip(whole, w, ws, s) != hipSuccess) return GCONV_ERR_LAUNCH;
-    }
+    // transformed weight copy (and no workspace) is needed
+    const bool dw_reversed = !direct && bwd_dw_reversed(d, out);
+    const bool route = !direct && bwd_as_forward(d) &&
+                       (dw_reversed || (ws && ws_bytes >= weight_bytes(d) && aligned(ws, 16)));
+    if (route && !dw_reversed && bwd::launch_flip(to_problem(d, out), w, ws, s) != hipSuccess) return GCONV_ERR_LAUNCH;
     return for_bwd_pieces(d, out, [&](const Piece &pc, bool, bool) {
         const void *dyp = (const char *)dy + pc.in_off;
         void *dxp = (char *)dx + pc.out_off;
         Problem t;
-        if (route && dw_reversed && bwd_forward_problem(pc.p, t) && depthwise::supported(t)) {
+        // the depthwise kernel's vector accesses need what launch_path checks
+        // for the forward call; otherwise the direct kernel runs
+        if (route && dw_reversed && aligned(dyp, 16) && aligned(dxp, 16) && aligned(w, 16) &&
+            bwd_forward_problem(pc.p, t) && depthwise::supported(t)) {
             Args a{dyp, w, nullptr, dxp};
             return depthwise::launch_flipped(t, a, s) == hipSuccess ? (int)GCONV_OK : (int)GCONV_ERR_LAUNCH;
         }
@@ -912,7 +920,7 @@ GCONV_API int gconv_bwd_data_workspace(const gconv_desc *d, size_t *bytes)
     int nph = 0;
     size_t wb = 0, tb = 0;
     if (bwd_phases(to_problem(d, out), ph, &nph, &wb, &tb)) *bytes = wb + tb;
-    else *bytes = bwd_as_forward(d) ? weight_bytes(d) : 0;
+    else *bytes = bwd_as_forward(d) && !bwd_dw_reversed(d, out) ? weight_bytes(d) : 0;
     return GCONV_OK;
 }
 

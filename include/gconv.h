@@ -243,7 +243,8 @@ int gconv_fwd_timed(const gconv_desc *d, int path, const void *x, const void *w,
  * use for any):
  *  - at stride 1 with dil*(k-1) >= pad on every axis, the size of w: the call
  *    becomes a weight transform plus one forward launch on the fastest
- *    forward path;
+ *    forward path (depthwise needs none: the forward depthwise kernel reads
+ *    each window reversed, so 0 is returned and no workspace is used);
  *  - at a stride above 1, for groups other than depthwise, whose tensors fit
  *    one launch: the weights of every residue class of dx (per axis the dx
  *    positions i = r + stride*m receive only the taps t with (t*dil - r - pad)
@@ -256,7 +257,8 @@ int gconv_bwd_data_workspace(const gconv_desc *d, size_t *bytes);
 /* Backward data, asynchronous on `stream`.  `workspace` (device memory the
  * caller owns, 16-byte aligned, may be NULL) of `workspace_bytes`: when it
  * holds gconv_bwd_data_workspace bytes, the workspace route runs (at stride
- * 1 the weight transform and the forward kernel; at larger strides three
+ * 1 the weight transform and the forward kernel, or for depthwise the
+ * forward kernel alone, with or without a workspace; at larger strides three
  * kernels per residue class); otherwise one direct kernel runs.  Tensors too large for one launch are split as in
  * gconv_fwd: whole images, else slices of dx along the outermost spatial
  * axis, each with the dy slices that reach it.  The workspace may be reused

@@ -225,9 +225,12 @@ def test_bwd_data_workspace_sizes():
     # bytes) and a dense buffer for the largest class (5 x 5 pixels of 8)
     d = G.make_desc(2, "f16", 1, 1, 8, 8, (9, 9), (3, 3), (2, 2), (1, 1), (1, 1))
     assert G.gconv_bwd_data_workspace(d) == 256 + 256 + 256 + 512 + 512
-    # depthwise at stride 2 runs its channel-vector direct kernel, and a pad
-    # beyond the dilated filter has no use for one
+    # depthwise at stride 2 runs its channel-vector direct kernel, at stride 1
+    # the forward depthwise kernel with each window reversed (no weight
+    # copy), and a pad beyond the dilated filter has no use for one
     d = G.make_desc(2, "f16", 1, 16, 16, 16, (9, 9), (3, 3), (2, 2), (1, 1), (1, 1))
+    assert G.gconv_bwd_data_workspace(d) == 0
+    d = G.make_desc(2, "f16", 1, 16, 16, 16, (9, 9), (3, 3), (1, 1), (1, 1), (1, 1))
     assert G.gconv_bwd_data_workspace(d) == 0
     d = G.make_desc(2, "f16", 1, 1, 8, 8, (9, 9), (3, 3), (1, 1), (3, 3), (1, 1))
     assert G.gconv_bwd_data_workspace(d) == 0
