@@ -702,43 +702,47 @@ int run_bwd_data(const gconv_desc *d, const void *dy, const void *w, void *dx, v
     });
 }
 
-size_t bwd_weight_partials_bytes(const Problem &p, int nch)
-{
-    return nch > 1 ? (size_t)nch * (size_t)p.G * p.Kpg * p.taps() * p.Cpg * sizeof(float) : 0;
-}
-
-// Backward weight reduces over the whole batch.  A batch too large for one
-// launch runs stage 1 as launches of whole images, each writing its own
-// chunks of partial sums into the workspace (consecutive ranges, in batch
-// order), and one stage 2 adds them all in chunk order.  The launches'
-// chunk counts, and so the summation order, depend only on the descriptor
-// and the workspace size.
+// Backward weight reduces over every output pixel of the batch.  Stage 1
+// runs as the forward call's launches (the whole batch, else whole images,
+// else, image by image, output slices with the input windows they read),
+// each writing its own chunks of partial sums into the workspace
+// (consecutive ranges, in launch order), and one stage 2 adds them all in
+// chunk order.  The launches' chunk counts, and so the summation order,
+// depend only on the descriptor and the workspace size.
 struct BwdwPlan {
-    int64_t nl;        // images per launch
     int64_t launches;
-    int per;           // chunks per launch (the last may use fewer)
+    int want;          // chunks a launch would take to fill the GPU
+    int per;           // chunks per launch (a launch may use fewer)
     int total;         // chunks in all (1: stage 1 writes dw itself)
+    size_t per_chunk;  // bytes of one chunk of partial sums
 };
+
+// Launches and the ideal chunk count (from the first launch, the largest:
+// later ones are shorter runs of images or slices), before any workspace.
+void bwdw_launches(const gconv_desc *d, const int64_t out[3], BwdwPlan &pl)
+{
+    Problem first{};
+    pl.launches = 0;
+    for_fwd_pieces(d, out, [&](const Piece &pc, bool, bool) {
+        if (pl.launches++ == 0) first = pc.p;
+        return (int)GCONV_OK;
+    });
+    pl.want = bwdw::ideal_chunks(first);
+    pl.per_chunk = (size_t)first.G * first.Kpg * first.taps() * first.Cpg * sizeof(float);
+}
 
 int bwdw_plan(const gconv_desc *d, const int64_t out[3], size_t ws_bytes, bool have_ws, BwdwPlan &pl)
 {
-    pl.nl = images_per_launch(d, out);
-    if (pl.nl < 1) return GCONV_ERR_TOO_LARGE;           // one image beyond a launch: not split for this reduction
-    pl.launches = (d->N + pl.nl - 1) / pl.nl;
-    gconv_desc t = *d;
-    t.N = pl.nl;
-    const Problem p = to_problem(&t, out);
-    const size_t per_chunk = (size_t)p.G * p.Kpg * p.taps() * p.Cpg * sizeof(float);
-    const int64_t room = have_ws ? (int64_t)(ws_bytes / per_chunk) : 0;
-    int64_t want = bwdw::ideal_chunks(p);
+    bwdw_launches(d, out, pl);
+    const int64_t room = have_ws ? (int64_t)(ws_bytes / pl.per_chunk) : 0;
     if (pl.launches == 1) {
-        pl.per = (int)(room >= 2 ? min64(want, room) : 1);
+        pl.per = (int)(room >= 2 ? min64(pl.want, room) : 1);
         pl.total = pl.per;
         return GCONV_OK;
     }
     // every launch needs at least one chunk of its own in the workspace
     if (room < pl.launches) return GCONV_ERR_TOO_LARGE;
-    pl.per = (int)max64(1, min64(want, room / pl.launches));
+    pl.per = (int)max64(1, min64(pl.want, room / pl.launches));
     pl.total = (int)(pl.per * pl.launches);
     return GCONV_OK;
 }
@@ -757,23 +761,22 @@ int run_bwd_weight(const gconv_desc *d, const void *x, const void *dy, void *dw,
     rc = bwdw_plan(d, out, ws_bytes, have_ws, pl);
     if (rc != GCONV_OK) return rc;
     hipStream_t s = (hipStream_t)stream;
-    const size_t x_img = (size_t)(d->in[0] * d->in[1] * d->in[2] * d->C) * es;
-    const size_t y_img = (size_t)(out[0] * out[1] * out[2] * d->K) * es;
-    Problem whole = to_problem(d, out);
+    const Problem whole = to_problem(d, out);
     const size_t welems = (size_t)whole.G * whole.Kpg * whole.taps() * whole.Cpg;
+    const bool final_ = pl.total == 1;
     int base = 0;
-    for (int64_t n0 = 0; n0 < d->N; n0 += pl.nl) {
-        gconv_desc t = *d;
-        t.N = d->N - n0 < pl.nl ? d->N - n0 : pl.nl;
-        const Problem p = to_problem(&t, out);
+    // a slice whose window lies wholly in the padding (negative leading pad)
+    // reads no input: the kernels' bounds checks leave its chunks zero
+    rc = for_fwd_pieces(d, out, [&](const Piece &pc, bool, bool) {
         int used = 0;
-        const bool final_ = pl.total == 1;
-        if (bwdw::stage1(p, (const char *)x + (size_t)n0 * x_img, (const char *)dy + (size_t)n0 * y_img,
+        if (bwdw::stage1(pc.p, (const char *)x + pc.in_off, (const char *)dy + pc.out_off,
                          final_ ? nullptr : (float *)ws + (size_t)base * welems, final_ ? dw : nullptr, pl.per,
                          &used, s) != hipSuccess)
-            return GCONV_ERR_LAUNCH;
+            return (int)GCONV_ERR_LAUNCH;
         base += used;
-    }
+        return (int)GCONV_OK;
+    });
+    if (rc != GCONV_OK) return rc;
     if (pl.total > 1 && bwdw::stage2(whole, (const float *)ws, dw, base, s) != hipSuccess) return GCONV_ERR_LAUNCH;
     return GCONV_OK;
 }
@@ -942,17 +945,12 @@ GCONV_API int gconv_bwd_weight_workspace(const gconv_desc *d, size_t *bytes)
     int64_t out[3];
     int rc = check_desc(d, out);
     if (rc != GCONV_OK) return rc;
-    const int64_t nl = images_per_launch(d, out);
-    if (nl < 1) return GCONV_ERR_TOO_LARGE;
-    gconv_desc t = *d;
-    t.N = nl;
-    const Problem p = to_problem(&t, out);
-    const int64_t launches = (d->N + nl - 1) / nl;
-    const int per = bwdw::ideal_chunks(p);
+    BwdwPlan pl;
+    bwdw_launches(d, out, pl);
     // one launch: the ideal chunks (none when one chunk fills the chip); a
-    // split batch: the ideal chunks of every launch
-    *bytes = launches == 1 ? bwd_weight_partials_bytes(p, per)
-                           : (size_t)launches * (size_t)per * (size_t)p.G * p.Kpg * p.taps() * p.Cpg * sizeof(float);
+    // call split into launches: the ideal chunks of every launch
+    *bytes = pl.launches == 1 ? (pl.want > 1 ? (size_t)pl.want * pl.per_chunk : 0)
+                              : (size_t)pl.launches * (size_t)pl.want * pl.per_chunk;
     return GCONV_OK;
 }
 
@@ -972,7 +970,7 @@ GCONV_API int gconv_bwd_weight_noalloc(const gconv_desc *d, const void *x, const
     // the sizes are checked against the fixed scratch before any HIP call
     BwdwPlan pl;
     rc = bwdw_plan(d, out, kScratchBytes, true, pl);
-    if (rc == GCONV_ERR_TOO_LARGE && images_per_launch(d, out) >= 1) return GCONV_ERR_SCRATCH;
+    if (rc == GCONV_ERR_TOO_LARGE) return GCONV_ERR_SCRATCH;   // the only refusal left after check_desc
     if (rc != GCONV_OK) return rc;
     void *ws = scratch_ptr();
     if (!ws) return GCONV_ERR_LAUNCH;

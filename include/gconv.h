@@ -83,8 +83,9 @@ typedef enum gconv_status {
     GCONV_ERR_TOO_LARGE = -4,       /* w has >= 2^31 elements, N or an extent >= 2^31, or
                                        one slice along the outermost spatial axis (a row
                                        in 2D, a plane in 3D) of x or y, with the window it
-                                       needs, spans >= 2^31 bytes; backward weight: x or y
-                                       has >= 2^31 elements */
+                                       needs, spans >= 2^31 bytes; backward weight split
+                                       into launches: a workspace holding fewer chunks of
+                                       partial sums than the call has launches */
     GCONV_ERR_MISALIGNED = -5,      /* a pointer is not aligned as the path needs */
     GCONV_ERR_BAD_PATH = -6,        /* unknown path id */
     GCONV_ERR_PATH_UNSUPPORTED = -7,/* forced path cannot run this problem */
@@ -284,6 +285,11 @@ int gconv_bwd_data_direct(const gconv_desc *d, const void *dy, const void *w, vo
  *
  *   dw[g,k,t,c] = sum over output pixels o whose tap t reads an in-bounds
  *                 input i = o*stride - pad + t*dil of dy[n,o,g,k] * x[n,i,g,c]
+ *
+ * Tensors too large for one launch are split as in gconv_fwd (whole images,
+ * else output slices along the outermost spatial axis with the input slices
+ * their windows read); each launch then adds its own chunks of partial sums,
+ * so the workspace must hold at least one chunk per launch.
  */
 
 /* Bytes of fp32 partial-sum workspace that lets gconv_bwd_weight split the
@@ -315,9 +321,9 @@ int gconv_bwd_weight(const gconv_desc *d, const void *x, const void *dy, void *d
  * holds (at most the gconv_bwd_weight_workspace amount), so the result is
  * bitwise that of gconv_bwd_weight with a workspace of
  * min(GCONV_NOALLOC_SCRATCH_BYTES, gconv_bwd_weight_workspace) bytes.
- * Returns GCONV_ERR_SCRATCH, before any HIP call, when a batch that must be
- * split into launches needs more than the scratch holds (one chunk of
- * partial sums per launch).  Every call on one GPU uses that GPU's one
+ * Returns GCONV_ERR_SCRATCH, before any HIP call, when a call that must be
+ * split into launches (a batch or an image too large for one) needs more
+ * than the scratch holds (one chunk of partial sums per launch).  Every call on one GPU uses that GPU's one
  * scratch array: calls that overlap on the same GPU (other streams or host
  * threads) race and must be serialised by the caller.  Status codes
  * otherwise as gconv_bwd_weight. */

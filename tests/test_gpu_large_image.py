@@ -1,7 +1,7 @@
 """One image too large for a single launch (>= 2^31 elements) is split into
 launches of output slices along its outermost spatial axis (rows in 2D,
 planes in 3D), each with the halo its window needs (gconv_fwd,
-gconv_bwd_data).  Checked against the oracle on bands of slices around
+gconv_bwd_data, gconv_bwd_weight).  Checked against the oracle on bands of slices around
 every launch boundary and at both ends of the image: the oracle runs on the
 band of input slices the band's outputs read (its outputs depend on nothing
 else), so the comparison is exact in its extent.  Inputs are seeded N(0, 1)
@@ -115,3 +115,68 @@ def test_forward_3d_image_split_into_plane_slices():
         r = U.check(got, ref, scale, "bf16", "forward planes %d..%d" % (p0, p1))
         print("3D forward planes %d..%d (boundary every %d planes) max err/tol %.3f" % (p0, p1, per, r))
     del x, y
+
+
+def _bwd_weight_bands(x, dy, groups, filt, per, extent, dtype, what):
+    """dw of the whole image against the sum of the bands' contributions:
+    dy is zero outside the bands (which are apart), so each band's share is
+    the oracle's dw on the band's dy slices and the input slices they read
+    (one slice of halo each side; the slices next to a band hold zero dy,
+    so the halo's own padding in the band's problem adds nothing).  Inputs
+    are uniform in [0, 0.5): the products share one sign, so the tolerance,
+    which scales with the sum of |products|, stays small against every
+    band's share."""
+    nd = len(filt)
+    dw = G.conv_bwd_weight(x, dy, groups, filt, (1,) * nd, (1,) * nd, (1,) * nd)
+    torch.cuda.synchronize()
+    got = dw.to("cpu", torch.float64).numpy()
+    ref, scale, shares = 0.0, 0.0, []
+    for a0, a1 in bands(extent, per):
+        lo, hi = max(a0 - 1, 0), min(a1 + 1, extent)
+        r, s = oracle.conv_bwd_weight(x[:, lo:hi].to("cpu", torch.float64).numpy(),
+                                      dy[:, lo:hi].to("cpu", torch.float64).numpy(),
+                                      groups, filt, (1,) * nd, (1,) * nd, (1,) * nd)
+        ref, scale = ref + r, scale + s
+        shares.append(r)
+    r = U.check(got, ref, scale, dtype, what)
+    print("%s (boundary every %d slices) max err/tol %.3f" % (what, per, r))
+    # every band's share is far above the tolerance, so a launch dropped or
+    # counted twice (or a halo slice lost) cannot pass
+    tol = U.tolerance(scale, dtype)
+    for sh in shares:
+        assert (np.abs(sh) > 4 * tol).any()
+
+
+@pytest.mark.parametrize("groups", [64, 8])
+def test_bwd_weight_2d_image_split_into_row_slices(groups):
+    """Depthwise (channel-vector kernel) and 8-channel groups (matrix-core
+    kernel) over one 4.6 GB image: three launches of row slices."""
+    H = W = 6000
+    C = 64
+    gen = torch.Generator(device="cuda").manual_seed(24)
+    x = (torch.rand((1, H, W, C), device="cuda", generator=gen, dtype=torch.float32) / 2).to(torch.float16)
+    assert x.numel() >= 1 << 31
+    per = fwd_slices(W * C * 2, W * C * 2, 3, 1)
+    assert per < H
+    dy = torch.zeros((1, H, W, C), device="cuda", dtype=torch.float16)
+    for r0, r1 in bands(H, per):
+        dy[:, r0:r1] = (torch.rand((1, r1 - r0, W, C), device="cuda", generator=gen) / 2).to(torch.float16)
+    _bwd_weight_bands(x, dy, groups, (3, 3), per, H, "f16", "bwd_weight G=%d rows" % groups)
+    del x, dy
+
+
+def test_bwd_weight_3d_image_split_into_plane_slices():
+    """2-channel groups over one 4.4 GB 3D image: three launches of plane
+    slices (16 channels keep the oracle's bands to seconds)."""
+    D, H, W = 600, 480, 480
+    G8, C = 8, 16
+    gen = torch.Generator(device="cuda").manual_seed(25)
+    x = (torch.rand((1, D, H, W, C), device="cuda", generator=gen, dtype=torch.float32) / 2).to(torch.bfloat16)
+    assert x.numel() >= 1 << 31
+    per = fwd_slices(H * W * C * 2, H * W * C * 2, 3, 1)
+    assert per < D
+    dy = torch.zeros((1, D, H, W, C), device="cuda", dtype=torch.bfloat16)
+    for p0, p1 in bands(D, per):
+        dy[:, p0:p1] = (torch.rand((1, p1 - p0, H, W, C), device="cuda", generator=gen) / 2).to(torch.bfloat16)
+    _bwd_weight_bands(x, dy, G8, (3, 3, 3), per, D, "bf16", "3D bwd_weight planes")
+    del x, dy

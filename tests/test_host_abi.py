@@ -392,6 +392,18 @@ def test_image_beyond_one_launch_is_split_into_slices():
     assert G.gconv_select_path(big3) >= 0
     # backward data accepts it as well (dx slices with the dy slices reaching them)
     assert G.gconv_bwd_data_workspace(big) == 64 * 9 * 2
+    # backward weight runs the forward call's launches (three row slices of
+    # up to 2794 rows here), each adding its own chunks of partial sums: the
+    # workspace holds the same number of chunks for each, and fewer chunks
+    # than launches is refused before any launch
+    chunk = 64 * 9 * 4
+    need = G.gconv_bwd_weight_workspace(big)
+    assert need > 0 and need % (3 * chunk) == 0
+    assert G.gconv_bwd_weight(big, 16, 16, 16, None, 0) == G.GCONV_ERR_TOO_LARGE
+    assert G.gconv_bwd_weight(big, 16, 16, 16, 32, 2 * chunk) == G.GCONV_ERR_TOO_LARGE
+    big3w = G.make_desc(3, "bf16", 1, 8, 16, 16, (600, 480, 480), (3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1))
+    need3 = G.gconv_bwd_weight_workspace(big3w)
+    assert need3 > 0 and need3 % (3 * 16 * 27 * 2 * 4) == 0
 
 
 def test_noalloc_entry_validates_before_any_hip_call():
