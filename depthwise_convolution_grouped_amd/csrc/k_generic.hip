@@ -9,7 +9,10 @@
 // thread ends in the shared bias/convert epilogue.  L = 1 for large outputs;
 // small problems (few outputs, long reductions) spread each reduction over
 // up to 16 threads, so the whole chip works and each thread's loads are few
-// and independent instead of one long dependent chain per output.
+// and independent instead of one long dependent chain per output.  Windows
+// of at most 9 taps with at most 4 channels per thread take a flat form that
+// issues all of a thread's loads before its first product, so the thread
+// waits for one memory latency instead of one per tap.
 #include "device_common.h"
 #include "gconv_internal.h"
 
@@ -60,6 +63,70 @@ __global__ __launch_bounds__(kBlock) void kernel(Problem p, const T *__restrict_
     if (e < total && part == 0) y[e] = finish<T>(acc, bias, g * p.Kpg + k);
 }
 
+// The flat form: taps and channel slots unrolled to fixed bounds.  A slot
+// outside the window, the input or the group loads from a valid address and
+// its product is dropped by a select (never multiplied by zero, so a
+// non-finite weight next to the padding stays out of the sum); the products
+// are added in the loop form's order (taps outer, channels c = part + j L
+// inner), so both forms give the same bits.
+constexpr int kFlatTaps = 9, kFlatCh = 4;
+
+template <typename T, int L>
+__global__ __launch_bounds__(kBlock) void flat_kernel(Problem p, const T *__restrict__ x,
+                                                      const T *__restrict__ w,
+                                                      const T *__restrict__ bias, T *__restrict__ y,
+                                                      int total)
+{
+    const int tid = blockIdx.x * kBlock + threadIdx.x;
+    const int e = tid / L, part = tid - (tid / L) * L;
+    const bool live = e < total;
+    int r = live ? e : 0;
+    const int k = r % p.Kpg;  r /= p.Kpg;
+    const int g = r % p.G;    r /= p.G;
+    const int ow = r % p.Wo;  r /= p.Wo;
+    const int oh = r % p.Ho;  r /= p.Ho;
+    const int od = r % p.Do;  r /= p.Do;
+    const int n = r;
+    const int C = p.G * p.Cpg, taps = p.Z * p.Y * p.X;
+    const T *wk = w + (size_t)(g * p.Kpg + k) * taps * p.Cpg;
+    float xv[kFlatTaps][kFlatCh], wv[kFlatTaps][kFlatCh];
+    bool use[kFlatTaps][kFlatCh];
+    int z = 0, yy = 0, xx = 0;   // tap t = (z Y + yy) X + xx
+#pragma unroll
+    for (int t = 0; t < kFlatTaps; ++t) {
+        const int id = od * p.sd - p.pd + z * p.dd;
+        const int ih = oh * p.sh - p.ph + yy * p.dh;
+        const int iw = ow * p.sw - p.pw + xx * p.dw;
+        const bool in = live && t < taps && (unsigned)id < (unsigned)p.D && (unsigned)ih < (unsigned)p.H &&
+                        (unsigned)iw < (unsigned)p.W;
+        const size_t xo = (size_t)(((n * p.D + id) * p.H + ih) * p.W + iw) * C + g * p.Cpg;
+#pragma unroll
+        for (int j = 0; j < kFlatCh; ++j) {
+            const int c = part + j * L;
+            use[t][j] = in && c < p.Cpg;
+            xv[t][j] = to_f32(x[use[t][j] ? xo + c : 0]);
+            wv[t][j] = to_f32(wk[use[t][j] ? (size_t)t * p.Cpg + c : 0]);
+        }
+        if (++xx == p.X) {
+            xx = 0;
+            if (++yy == p.Y) {
+                yy = 0;
+                ++z;
+            }
+        }
+    }
+    float acc = 0.f;
+#pragma unroll
+    for (int t = 0; t < kFlatTaps; ++t)
+#pragma unroll
+        for (int j = 0; j < kFlatCh; ++j) acc = use[t][j] ? fmaf(xv[t][j], wv[t][j], acc) : acc;
+#pragma unroll
+    for (int m = L / 2; m >= 1; m /= 2) acc += __shfl_xor(acc, m);
+    if (live && part == 0) y[e] = finish<T>(acc, bias, g * p.Kpg + k);
+}
+
+bool flat_ok(const Problem &p, int L) { return p.taps() <= kFlatTaps && (p.Cpg + L - 1) / L <= kFlatCh; }
+
 // threads per output: doubled while the launch stays under 2^21 threads
 // (eight waves per SIMD on 256 CUs), at most the channels a thread would
 // otherwise walk alone (tile sweep: a 1728-long reduction over 200k outputs
@@ -85,6 +152,9 @@ hipError_t go2(const Problem &p, const Args &a, hipStream_t s)
     using T = typename Elem<DT>::T;
     const int total = (int)p.y_elems();
     const int blocks = (int)(((long long)total * L + kBlock - 1) / kBlock);
+    if (flat_ok(p, L))
+        return enqueue(flat_kernel<T, L>, dim3(blocks), dim3(kBlock), 0, s, a, p,
+                       (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y, total);
     return enqueue(kernel<T, L>, dim3(blocks), dim3(kBlock), 0, s, a, p,
                    (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y, total);
 }

@@ -647,3 +647,63 @@ def test_every_tile_of_every_path(name, N):
             ran += 1
     assert ran >= 2
     print("%s N=%d: %d tile variants checked" % (name, N, ran))
+
+
+GENERIC_CASES = [
+    # problem, then what it exercises
+    (inputs.conv2d("f32", 1, 2, 64, 64, 8, 8, 3, 3, 1, 1), "the small fp32 config: flat at 8 and 16 threads"),
+    (inputs.conv2d("f16", 2, 3, 15, 6, 9, 11, 3, 1, 2, 1), "5 channels per group, 3 taps, stride 2"),
+    (inputs.conv2d("bf16", 1, 4, 16, 8, 13, 10, 3, 3, 1, 2, 2), "dilation 2"),
+    (inputs.conv2d("f32", 3, 1, 3, 7, 7, 5, 1, 1, 2, 1), "1x1 window, stride 2, padding"),
+    (inputs.Problem(3, "f16", 1, 2, 8, 4, (5, 6, 7), (3, 3, 3), (1, 1, 1), (1, 1, 1)), "27 taps: loop form"),
+    (inputs.conv2d("f32", 1, 2, 80, 4, 6, 6, 3, 3, 1, 1), "40 channels: loop form below 16 threads"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(GENERIC_CASES)), ids=[c[1] for c in GENERIC_CASES])
+def test_generic_every_tile(case):
+    """Every generic tile (1, 2, 4, 8, 16 threads per output), in its flat
+    form (windows of <= 9 taps, <= 4 channels per thread) and its loop form."""
+    p, what = GENERIC_CASES[case]
+    t = inputs.make_tensors(p, 5100 + case)
+    st, pd, dl = p.spatial_args()
+    ref, scale = oracle.conv_fwd(*U.oracle_inputs(p, t), p.G, st, pd, dl)
+    d = G.desc_from_problem(p)
+    x, w, b = U.device_tensors(p, t)
+    taps = p.filt[0] * p.filt[1] * p.filt[2]
+    forms = []
+    for tile in range(5):
+        y = poisoned_out(p)
+        rc = G.gconv_fwd_tile(d, G.GCONV_PATH_GENERIC, tile, x.data_ptr(), w.data_ptr(),
+                              b.data_ptr() if b is not None else None, y.data_ptr(),
+                              torch.cuda.current_stream().cuda_stream)
+        assert rc == 0, G.gconv_status_str(rc)
+        torch.cuda.synchronize()
+        U.check(U.to_f64(y), ref, scale, p.dtype, "%s generic tile=%d" % (what, tile))
+        forms.append("flat" if taps <= 9 and -(-p.Cpg // (1 << tile)) <= 4 else "loop")
+    print("%s: generic tiles %s" % (what, forms))
+
+
+def test_generic_inf_weight_beside_the_padding():
+    """An Inf weight at tap (0, 0) of one output channel: outputs whose
+    window puts that tap in the padding have no such product in the sum and
+    stay finite (the flat form drops a product, it never multiplies the
+    weight by zero); the others are infinite, as in the oracle."""
+    p = inputs.conv2d("f32", 1, 2, 64, 64, 8, 8, 3, 3, 1, 1)
+    t = inputs.make_tensors(p, 5200)
+    t.w[5, 0, 0, 3] = np.inf
+    st, pd, dl = p.spatial_args()
+    ref, scale = oracle.conv_fwd(*U.oracle_inputs(p, t), p.G, st, pd, dl)
+    fin = np.isfinite(ref)
+    assert fin[0, 0, :, 5].all() and fin[0, :, 0, 5].all() and not fin[0, 1:, 1:, 5].any()
+    d = G.desc_from_problem(p)
+    x, w, b = U.device_tensors(p, t)
+    for tile in range(5):
+        y = poisoned_out(p)
+        rc = G.gconv_fwd_tile(d, G.GCONV_PATH_GENERIC, tile, x.data_ptr(), w.data_ptr(), b.data_ptr(),
+                              y.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        assert rc == 0, G.gconv_status_str(rc)
+        torch.cuda.synchronize()
+        got = U.to_f64(y)
+        U.check(got[fin], ref[fin], scale[fin], p.dtype, "Inf weight, finite outputs, tile=%d" % tile)
+        assert np.isinf(got[~fin]).all(), "tile=%d" % tile
