@@ -740,9 +740,10 @@ int bwdw_plan(const gconv_desc *d, const int64_t out[3], size_t ws_bytes, bool h
         pl.total = pl.per;
         return GCONV_OK;
     }
-    // every launch needs at least one chunk of its own in the workspace
-    if (room < pl.launches) return GCONV_ERR_TOO_LARGE;
-    pl.per = (int)max64(1, min64(pl.want, room / pl.launches));
+    // every launch needs at least one chunk of its own in the workspace (and
+    // the chunk count in all stays an int)
+    if (room < pl.launches || pl.launches > INT32_MAX) return GCONV_ERR_TOO_LARGE;
+    pl.per = (int)max64(1, min64(min64(pl.want, room / pl.launches), INT32_MAX / pl.launches));
     pl.total = (int)(pl.per * pl.launches);
     return GCONV_OK;
 }
