@@ -14,7 +14,8 @@
 //     range, and split the Kpg output channels of the group between them
 //     (partial sums joined by lane exchanges), fp32 accumulation; for
 //     depthwise problems with 16-byte aligned dy and dx, a channel-vector
-//     form of it;
+//     form of it (and, for 3x3 windows at stride 2, one over 2 x 2 blocks of
+//     dx pixels);
 //   - the weight transform of the stride-1 route: at stride 1, dx is the
 //     forward convolution of dy with the weights flipped in space and with
 //     C and K exchanged (wt[g][c][Z-1-z][Y-1-y][X-1-x][k] = w[g][k][z][y][x][c]:
@@ -149,6 +150,87 @@ __global__ __launch_bounds__(kBlock) void depthwise_kernel(Problem p, const T *_
     }
 }
 
+// Depthwise 2D, 3x3 window, stride 2, dilation 1 (the strided depthwise
+// layer of MobileNet-style blocks): one thread owns a 2 x 2 block of dx
+// pixels (rows 2a, 2a + 1, columns 2b, 2b + 1) and one 16-byte channel
+// vector.  Row i = 2a + ry receives the taps ty with (i + pad - ty) even, at
+// dy row (i + pad - ty) / 2; for both rows of the block these are the two dy
+// rows a + f and a + f + 1, f = floor((pad - 1) / 2) (likewise for columns).
+// So the thread loads the 2 x 2 dy vectors its block reads once (zero
+// outside dy) instead of once per dx pixel that reads them, and adds each
+// dx pixel's products in the tap order of the plain kernel.  PH and PW are
+// the pads' parities: with them every tap's dy slot is a constant (odd pad:
+// (ry - ty + 1) / 2, even pad: (ry - ty) / 2 + 1).
+template <typename T, int PH, int PW>
+__global__ __launch_bounds__(kBlock) void depthwise_s2_kernel(Problem p, const T *__restrict__ dy,
+                                                              const T *__restrict__ w, T *__restrict__ dx,
+                                                              int total)
+{
+    constexpr int VEC = 16 / (int)sizeof(T);
+    extern __shared__ uint4 wl4[];
+    T *wl = reinterpret_cast<T *>(wl4);
+    for (int i = threadIdx.x; i < p.G * 9; i += kBlock) {   // w[g][t] -> wl[t][g]
+        const int g = i / 9, t = i - g * 9;
+        wl[t * p.G + g] = w[i];
+    }
+    __syncthreads();
+    const int Cv = p.G / VEC;
+    const int Hb = (p.H + 1) / 2, Wb = (p.W + 1) / 2;
+    const int fh = p.ph == 0 ? -1 : (p.ph - 1) / 2, fw = p.pw == 0 ? -1 : (p.pw - 1) / 2;
+    for (int e = blockIdx.x * kBlock + threadIdx.x; e < total; e += gridDim.x * kBlock) {
+        int r = e;
+        const int cv = r % Cv;  r /= Cv;
+        const int b = r % Wb;   r /= Wb;
+        const int a = r % Hb;   r /= Hb;
+        const int n = r;
+        const int g0 = cv * VEC;
+        // the 2 x 2 dy vectors of the block (rows a + fh + u, columns b + fw + v)
+        float d[2][2][VEC];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int v = 0; v < 2; ++v) {
+                const int oh = a + fh + u, ow = b + fw + v;
+                const bool in = (unsigned)oh < (unsigned)p.Ho && (unsigned)ow < (unsigned)p.Wo;
+                uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+                if (in) raw = *reinterpret_cast<const uint4 *>(dy + (((size_t)n * p.Ho + oh) * p.Wo + ow) * p.G + g0);
+                const T *dv = reinterpret_cast<const T *>(&raw);
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) d[u][v][j] = to_f32(dv[j]);
+            }
+#pragma unroll
+        for (int ry = 0; ry < 2; ++ry)
+#pragma unroll
+            for (int rx = 0; rx < 2; ++rx) {
+                const int ih = 2 * a + ry, iw = 2 * b + rx;
+                float acc[VEC];
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) acc[j] = 0.f;
+#pragma unroll
+                for (int ty = 0; ty < 3; ++ty) {
+                    if ((ry + PH - ty) & 1) continue;         // the tap misses row ih
+                    const int u = PH ? (ry - ty + 1) / 2 : (ry - ty) / 2 + 1;   // dy row a + fh + u
+#pragma unroll
+                    for (int tx = 0; tx < 3; ++tx) {
+                        if ((rx + PW - tx) & 1) continue;
+                        const int v = PW ? (rx - tx + 1) / 2 : (rx - tx) / 2 + 1;
+                        const uint4 wraw = *reinterpret_cast<const uint4 *>(wl + (ty * 3 + tx) * p.G + g0);
+                        const T *wv = reinterpret_cast<const T *>(&wraw);
+#pragma unroll
+                        for (int j = 0; j < VEC; ++j) acc[j] = fmaf(d[u][v][j], to_f32(wv[j]), acc[j]);
+                    }
+                }
+                if (ih < p.H && iw < p.W) {
+                    T o[VEC];
+#pragma unroll
+                    for (int j = 0; j < VEC; ++j) o[j] = from_f32<T>(acc[j]);
+                    *reinterpret_cast<uint4 *>(dx + (((size_t)n * p.H + ih) * p.W + iw) * p.G + g0) =
+                        *reinterpret_cast<const uint4 *>(o);
+                }
+            }
+    }
+}
+
 // wt[g][c][t][k] = w[g][k][T-1-t][c] (t the flat tap (z, y, x), so T-1-t
 // flips all three axes at once): for each (group, tap) a Kpg x Cpg matrix
 // transposed through LDS in 32 x 32 tiles, read along c and written along
@@ -228,6 +310,13 @@ hipError_t go(const Problem &p, const void *dy, const void *w, void *dx, hipStre
 
 }  // namespace
 
+// the 2 x 2 block form: 2D, 3x3, stride 2, dilation 1 on both axes
+static bool s2_ok(const Problem &p)
+{
+    return p.ndim == 2 && p.Y == 3 && p.X == 3 && p.sh == 2 && p.sw == 2 && p.dh == 1 && p.dw == 1 &&
+           p.ph >= 0 && p.pw >= 0;
+}
+
 template <typename T>
 hipError_t go_dw(const Problem &p, const void *dy, const void *w, void *dx, hipStream_t s)
 {
@@ -237,9 +326,17 @@ hipError_t go_dw(const Problem &p, const void *dy, const void *w, void *dx, hipS
     const long long blocks = (total + kBlock - 1) / kBlock;
     const dim3 grid((unsigned)(blocks < 2048 ? blocks : 2048));   // 8 per CU, grid-stride beyond
     const bool same = p.sh == p.sw && (p.ndim == 2 || p.sd == p.sh);   // 2D: sd is 1 and unused
+    const unsigned lds = (unsigned)(p.G * p.taps() * (int)sizeof(T));
+    if (s2_ok(p)) {
+        const long long tq = (long long)p.N * ((p.H + 1) / 2) * ((p.W + 1) / 2) * (p.G / VEC);
+        const long long bq = (tq + kBlock - 1) / kBlock;
+        auto k2 = (p.ph & 1) ? ((p.pw & 1) ? depthwise_s2_kernel<T, 1, 1> : depthwise_s2_kernel<T, 1, 0>)
+                             : ((p.pw & 1) ? depthwise_s2_kernel<T, 0, 1> : depthwise_s2_kernel<T, 0, 0>);
+        return enqueue(k2, dim3((unsigned)(bq < 2048 ? bq : 2048)), dim3(kBlock), lds, s, a, p,
+                       (const T *)dy, (const T *)w, (T *)dx, (int)tq);
+    }
     auto k = same && p.sh == 1 ? depthwise_kernel<T, 1> : same && p.sh == 2 ? depthwise_kernel<T, 2>
                                                                              : depthwise_kernel<T, 0>;
-    const unsigned lds = (unsigned)(p.G * p.taps() * (int)sizeof(T));
     return enqueue(k, grid, dim3(kBlock), lds, s, a, p, (const T *)dy, (const T *)w, (T *)dx, (int)total);
 }
 

@@ -73,6 +73,11 @@ CASES = [
     (2, "f32", 2, 12, 12, 12, (11, 10), (3, 3), 2, 1, 2),       # depthwise fp32, channel vectors of 4
     (3, "bf16", 1, 24, 24, 24, (5, 9, 8), (3, 3, 3), 2, 1, 1),  # depthwise 3D stride 2, vectors of 8
     (2, "f16", 1, 20, 20, 20, (9, 9), (3, 3), 2, 1, 1),         # depthwise, C not a multiple of 8: scalar
+    # depthwise 3x3 stride 2 on 2 x 2 dx blocks: both pad parities per axis, odd extents
+    (2, "f16", 2, 24, 24, 24, (12, 16), (3, 3), 2, 0, 1),       # pad 0, even extents
+    (2, "bf16", 1, 16, 16, 16, (15, 9), (3, 3), 2, 2, 1),       # pad 2, odd extents (half blocks)
+    (2, "f32", 2, 8, 8, 8, (10, 7), (3, 3), 2, (3, 0), 1),      # pad 3 rows (past the window), 0 columns
+    (2, "bf16", 3, 40, 40, 40, (5, 6), (3, 3), 2, (0, 1), 1),   # mixed parities, tiny image
     # strided, grouped: residue classes of dx on the forward kernels
     (2, "bf16", 2, 4, 512, 512, (14, 13), (3, 3), 2, 1, 1),     # large groups: the classes on the halo / M-tiled GEMMs
     (2, "bf16", 2, 32, 256, 256, (15, 14), (3, 3), 2, 1, 1),    # ResNeXt-like 8/8 groups, stride 2
@@ -109,7 +114,7 @@ def test_bwd_data_random_small(case):
     run_case(p, 8600 + 10 * case, "bwd_data random %s" % (p,))
 
 
-@pytest.mark.parametrize("name,N", [("depthwise2d_f16", 2), ("grouped2d_resnext_bf16", 1),
+@pytest.mark.parametrize("name,N", [("depthwise2d_f16", 2), ("depthwise2d_s2_f16", 2), ("grouped2d_resnext_bf16", 1),
                                     ("grouped3d_f16_n1", 1), ("grouped2d_large_bf16", 1)])
 def test_bwd_data_reduced_workloads(name, N):
     wl = inputs.WORKLOADS[name].problem
