@@ -74,7 +74,7 @@ def test_bwd_weight_random_small(case):
     run_case(p, 9600 + 10 * case, "bwd_weight random %s" % (p,))
 
 
-@pytest.mark.parametrize("name,N", [("depthwise2d_f16", 2), ("grouped2d_resnext_bf16", 1),
+@pytest.mark.parametrize("name,N", [("depthwise2d_f16", 2), ("depthwise2d_s2_f16", 2), ("grouped2d_resnext_bf16", 1),
                                     ("grouped3d_f16_n1", 1)])
 def test_bwd_weight_reduced_workloads(name, N):
     wl = inputs.WORKLOADS[name].problem
